@@ -1,0 +1,227 @@
+"""CPU oracle of the MoE routing / dispatch / combine path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product path
+(``combine_moe_route_03_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain single-threaded C, double
+precision); this module only marshals numpy arrays through ctypes. bf16 tensors
+travel as their raw 16-bit patterns in ``numpy.uint16`` arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("expert_max_over_mean", ctypes.c_double),
+        ("expert_gini", ctypes.c_double),
+        ("rank_max_over_mean", ctypes.c_double),
+        ("rank_gini", ctypes.c_double),
+        ("total", ctypes.c_int64),
+        ("expert_max", ctypes.c_int32),
+        ("expert_min", ctypes.c_int32),
+        ("rank_max", ctypes.c_int32),
+        ("rank_min", ctypes.c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C11, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+             _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        L.oracle_route.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i32p, _f64p]
+        L.oracle_counts.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]
+        L.oracle_offsets.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     _i32p, _i32p, _i32p]
+        L.oracle_positions.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                       _i32p, _i32p, _i32p]
+        L.oracle_dispatch_copy.argtypes = [_vp, ctypes.c_int64, _i32p, ctypes.c_int64, _vp]
+        L.oracle_expert_scale.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                          _i32p, _i32p, _vp]
+        L.oracle_combine_f64.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int32, _f64p, _i32p, ctypes.c_int64, _f64p]
+        L.oracle_combine_f32fma.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, _f32p, _i32p, ctypes.c_int64, _vp]
+        L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
+        L.oracle_gini_i64.argtypes = [_i64p, ctypes.c_int32]
+        L.oracle_gini_i64.restype = ctypes.c_double
+        L.oracle_round_bf16.argtypes = [ctypes.c_double]
+        L.oracle_round_bf16.restype = ctypes.c_uint16
+        _lib_handle = L
+    return _lib_handle
+
+
+def _p(a: np.ndarray, ptype):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ptype)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"hidden-state arrays must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+# --------------------------------------------------------------------- steps
+
+def route(logits: np.ndarray, k: int):
+    """Top-k indices (int32 [T,k]) and softmax-over-k weights (float64 [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib().oracle_route(_p(logits, _f32p), T, E, k, _p(idx, _i32p), _p(w, _f64p))
+    return idx, w
+
+
+def counts(idx: np.ndarray, E: int, R: int, W: int):
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    ec = np.empty(E, np.int32)
+    rc = np.empty(W * R, np.int32)
+    lib().oracle_counts(_p(idx, _i32p), T, k, E, R, W, _p(ec, _i32p), _p(rc, _i32p))
+    return ec, rc
+
+
+def offsets(expert_counts: np.ndarray, R: int, W: int):
+    ec = np.ascontiguousarray(expert_counts, dtype=np.int32)
+    E = ec.shape[0]
+    eo = np.empty(E, np.int32)
+    ro = np.empty(W * R, np.int32)
+    wo = np.empty(W + 1, np.int32)
+    lib().oracle_offsets(_p(ec, _i32p), E, R, W, _p(eo, _i32p), _p(ro, _i32p), _p(wo, _i32p))
+    return eo, ro, wo
+
+
+def positions(idx: np.ndarray, E: int, expert_offsets: np.ndarray, nrows: int):
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    eo = np.ascontiguousarray(expert_offsets, dtype=np.int32)
+    pos = np.empty((T, k), np.int32)
+    row_token = np.full(max(nrows, 0), -1, np.int32)
+    lib().oracle_positions(_p(idx, _i32p), T, k, E, _p(eo, _i32p), _p(pos, _i32p),
+                           _p(row_token, _i32p) if nrows > 0 else None)
+    return pos, row_token
+
+
+def dispatch_copy(x: np.ndarray, row_token: np.ndarray, nrows: int):
+    x = np.ascontiguousarray(x)
+    H = x.shape[1]
+    out = np.zeros((max(nrows, 0), H), x.dtype)
+    if nrows > 0:
+        rt = np.ascontiguousarray(row_token, dtype=np.int32)
+        lib().oracle_dispatch_copy(x.ctypes.data, H * x.itemsize, _p(rt, _i32p), nrows,
+                                   out.ctypes.data)
+    return out
+
+
+def dispatch(x: np.ndarray, idx: np.ndarray, E: int, R: int, W: int):
+    """All dispatch outputs of one call, as a dict keyed like the C-ABI arguments."""
+    T, k = idx.shape
+    ec, rc = counts(idx, E, R, W)
+    eo, ro, wo = offsets(ec, R, W)
+    nrows = int(ec.sum())
+    pos, row_token = positions(idx, E, eo, nrows)
+    send = dispatch_copy(x, row_token, nrows)
+    return dict(expert_counts=ec, rank_counts=rc, expert_offsets=eo, rank_offsets=ro,
+                wave_offsets=wo, pos=pos, row_token=row_token, send_buf=send, nrows=nrows)
+
+
+def expert_scale(send_buf: np.ndarray, expert_offsets: np.ndarray, expert_counts: np.ndarray):
+    send_buf = np.ascontiguousarray(send_buf)
+    n, H = send_buf.shape
+    out = np.zeros_like(send_buf)
+    eo = np.ascontiguousarray(expert_offsets, dtype=np.int32)
+    ec = np.ascontiguousarray(expert_counts, dtype=np.int32)
+    lib().oracle_expert_scale(send_buf.ctypes.data, _dtype_code(send_buf), H, eo.shape[0],
+                              _p(eo, _i32p), _p(ec, _i32p), out.ctypes.data)
+    return out
+
+
+def combine_f64(expert_out: np.ndarray, w: np.ndarray, pos: np.ndarray, T: int):
+    expert_out = np.ascontiguousarray(expert_out)
+    nrows, H = expert_out.shape
+    k = pos.shape[1]
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    y = np.empty((T, H), np.float64)
+    lib().oracle_combine_f64(expert_out.ctypes.data, _dtype_code(expert_out), T, H, k,
+                             _p(w, _f64p), _p(pos, _i32p), nrows, _p(y, _f64p))
+    return y
+
+
+def combine_f32fma(expert_out: np.ndarray, w32: np.ndarray, pos: np.ndarray, T: int):
+    expert_out = np.ascontiguousarray(expert_out)
+    nrows, H = expert_out.shape
+    k = pos.shape[1]
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    y = np.empty((T, H), expert_out.dtype)
+    lib().oracle_combine_f32fma(expert_out.ctypes.data, _dtype_code(expert_out), T, H, k,
+                                _p(w32, _f32p), _p(pos, _i32p), nrows, y.ctypes.data)
+    return y
+
+
+def stats(expert_counts: np.ndarray, R: int) -> dict:
+    ec = np.ascontiguousarray(expert_counts, dtype=np.int32)
+    s = Stats()
+    lib().oracle_stats(_p(ec, _i32p), ec.shape[0], R, ctypes.byref(s))
+    return s.as_dict()
+
+
+def gini(values) -> float:
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.int64))
+    return float(lib().oracle_gini_i64(_p(v, _i64p), v.shape[0]))
+
+
+def round_bf16(v: float) -> int:
+    return int(lib().oracle_round_bf16(float(v)))
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (a bit shift, no arithmetic)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)

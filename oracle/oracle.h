@@ -1,0 +1,113 @@
+/*
+ * oracle.h -- plain single-threaded CPU reference of the MoE routing,
+ * dispatch, expert, combine and skew-statistics path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark do. It shares no header, helper, table or constant with
+ * the HIP library under combine_moe_route_03_amd/csrc.
+ *
+ * Conventions
+ *   - Floating point is IEEE double unless a function says otherwise.
+ *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *   - Token-major row layouts: logits[T][E], x[T][H], idx/w/pos[T][k].
+ *   - Expert e lives on rank e / L (L = E / R local experts per rank) in local
+ *     slot e % L; its wave is floor(slot * W / L).
+ *   - Buckets are ordered by (wave, rank, local slot); inside a bucket, rows
+ *     follow ascending token index.
+ *   - A pick whose expert id lies outside [0, E) is dropped: it is not counted,
+ *     gets pos = -1, and contributes nothing to the combine.
+ *
+ * Parity status per function is stated in each comment ("pinned by").
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Top-k gating, MoE systems survey (crad.ict.ac.cn) section 1.1, eq. (2):
+ * G(x) = softmax(TopK(x W_gate, k)); the logits x W_gate are the input.
+ * idx[t][i]: the i-th largest logit of row t (ties -> lower expert id).
+ * w[t][i]  : exp(l_i - l_0) / sum_j exp(l_j - l_0) in double. */
+void oracle_route(const float* logits, int64_t T, int32_t E, int32_t k,
+                  int32_t* idx, double* w);
+
+/* Send-count matrix S (DODOCO summary, "metrics"; irregular AllToAll page,
+ * "EP irregular a2a" and "link to other primitives"): expert_counts[e] is the
+ * number of picks of expert e; viewed as R x L it is S. rank_counts[w*R+r] is
+ * the number of rows wave w sends to rank r (Alltoallv send counts). */
+void oracle_counts(const int32_t* idx, int64_t T, int32_t k, int32_t E,
+                   int32_t R, int32_t W, int32_t* expert_counts,
+                   int32_t* rank_counts);
+
+/* Exclusive prefix sums in bucket order: expert_offsets[E], rank_offsets[W*R]
+ * (absolute first row), wave_offsets[W+1]. */
+void oracle_offsets(const int32_t* expert_counts, int32_t E, int32_t R,
+                    int32_t W, int32_t* expert_offsets, int32_t* rank_offsets,
+                    int32_t* wave_offsets);
+
+/* Stable positions (MoE systems survey section 1.1, EP flow step 2: invert
+ * token->expert into expert->token and place same-expert tokens contiguously).
+ * pos[t][i] = expert_offsets[e] + #{t' < t : e in idx[t']}; row_token[pos] = t.
+ * row_token entries past the last placed row are left untouched. */
+void oracle_positions(const int32_t* idx, int64_t T, int32_t k, int32_t E,
+                      const int32_t* expert_offsets, int32_t* pos,
+                      int32_t* row_token);
+
+/* send_buf[n][:] = x[row_token[n]][:] for n < nrows (raw byte copy). */
+void oracle_dispatch_copy(const void* x, int64_t row_bytes,
+                          const int32_t* row_token, int64_t nrows,
+                          void* send_buf);
+
+/* Identity-scaled experts: out[n] = round_dtype((e(n) + 1) * in[n]) where
+ * e(n) is the expert whose bucket holds row n. */
+void oracle_expert_scale(const void* in, int32_t dtype, int64_t H, int32_t E,
+                         const int32_t* expert_offsets,
+                         const int32_t* expert_counts, void* out);
+
+/* Combine, MoE systems survey section 1.1 eq. (1) and EP flow step 4:
+ * y[t][h] = sum_i w[t][i] * out[pos[t][i]][h], all in double, unrounded. */
+void oracle_combine_f64(const void* expert_out, int32_t dtype, int64_t T,
+                        int64_t H, int32_t k, const double* w,
+                        const int32_t* pos, int64_t nrows, double* y);
+
+/* The same sum with the output quantised in the precision a single-precision
+ * kernel decides it in: acc = 0f; acc = fmaf(w_i, out_i, acc) for i = 0..k-1
+ * (pick order); y = round_to_nearest_even_dtype(acc). w is fp32 here. */
+void oracle_combine_f32fma(const void* expert_out, int32_t dtype, int64_t T,
+                           int64_t H, int32_t k, const float* w,
+                           const int32_t* pos, int64_t nrows, void* y);
+
+/* Skew statistics of S, DODOCO summary ("metrics"): per-expert max/mean and
+ * Gini coefficient of per-rank loads (per-expert Gini alongside). */
+typedef struct {
+  double expert_max_over_mean;
+  double expert_gini;
+  double rank_max_over_mean;
+  double rank_gini;
+  int64_t total;
+  int32_t expert_max;
+  int32_t expert_min;
+  int32_t rank_max;
+  int32_t rank_min;
+} oracle_stats_t;
+
+void oracle_stats(const int32_t* expert_counts, int32_t E, int32_t R,
+                  oracle_stats_t* out);
+
+/* Gini of n non-negative integers: sum_a sum_b |v_a - v_b| / (2 n sum v). */
+double oracle_gini_i64(const int64_t* v, int32_t n);
+
+/* Round a double to the nearest bf16 (ties to even); returns the bit pattern. */
+uint16_t oracle_round_bf16(double v);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
