@@ -1,0 +1,238 @@
+"""Python binding of libmoe_route.so, the gfx950 MoE routing / dispatch / combine library.
+
+Argument marshalling only: every step runs in the library's HIP kernels on the
+caller's current torch stream. torch provides device memory and the stream;
+outputs are allocated with torch when the caller does not pass them. The
+library must be built (``__graft_entry__.build()``); importing the functions
+without it raises, there is no fallback.
+
+Entry points mirror include/moe_route.h: ``route``, ``dispatch_index``,
+``dispatch_copy``, ``dispatch``, ``expert_scale``, ``combine``, ``stats``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+_CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("R", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MoeStats(ctypes.Structure):
+    _fields_ = [("expert_max_over_mean", ctypes.c_double), ("expert_gini", ctypes.c_double),
+                ("rank_max_over_mean", ctypes.c_double), ("rank_gini", ctypes.c_double),
+                ("total", ctypes.c_int64), ("expert_max", ctypes.c_int32),
+                ("expert_min", ctypes.c_int32), ("rank_max", ctypes.c_int32),
+                ("rank_min", ctypes.c_int32)]
+
+
+STATS_BYTES = ctypes.sizeof(MoeStats)
+
+# Every extern "C" function of include/moe_route.h with its ctypes signature.
+_vp, _i32, _i32p, _f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+_shp = ctypes.POINTER(MoeShape)
+SIGNATURES = {
+    "moe_route": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "moe_dispatch_workspace_bytes": ([_shp], ctypes.c_size_t),
+    "moe_dispatch_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                            _vp], ctypes.c_int),
+    "moe_dispatch_copy": ([_shp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                      ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_route.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe_route must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    H: int
+    E: int
+    k: int
+    R: int
+    W: int
+    dtype: torch.dtype
+
+    def c(self) -> MoeShape:
+        return MoeShape(self.T, self.H, self.E, self.k, self.R, self.W, _DTYPE_CODE[self.dtype])
+
+    @property
+    def L(self) -> int:
+        return self.E // self.R
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+# ----------------------------------------------------------------------- route
+
+def route(logits: torch.Tensor, k: int, topk_idx: torch.Tensor | None = None,
+          topk_w: torch.Tensor | None = None):
+    """Top-k gating: (topk_idx int32 [T,k], topk_w float32 [T,k])."""
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    dev = logits.device
+    topk_idx = _empty((T, k), torch.int32, dev) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, dev) if topk_w is None else topk_w
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream()),
+           "moe_route")
+    return topk_idx, topk_w
+
+
+# -------------------------------------------------------------------- dispatch
+
+def dispatch_workspace_bytes(shape: Shape) -> int:
+    sh = shape.c()
+    return int(lib().moe_dispatch_workspace_bytes(ctypes.byref(sh)))
+
+
+def alloc_dispatch(shape: Shape, device) -> dict:
+    """Output and workspace buffers of one dispatch call for this shape."""
+    T, k, E, R, W, H = shape.T, shape.k, shape.E, shape.R, shape.W, shape.H
+    i32 = torch.int32
+    return dict(
+        send_buf=_empty((T * k, H), shape.dtype, device),
+        expert_counts=_empty((E,), i32, device), expert_offsets=_empty((E,), i32, device),
+        rank_counts=_empty((W * R,), i32, device), rank_offsets=_empty((W * R,), i32, device),
+        wave_offsets=_empty((W + 1,), i32, device), pos=_empty((T, k), i32, device),
+        row_token=_empty((T * k,), i32, device),
+        workspace=_empty((max(dispatch_workspace_bytes(shape), 1),), torch.uint8, device))
+
+
+def dispatch_index(topk_idx: torch.Tensor, shape: Shape, out: dict):
+    sh = shape.c()
+    _check(lib().moe_dispatch_index(
+        ctypes.byref(sh), _ptr(topk_idx), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]),
+        _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream()), "moe_dispatch_index")
+    return out
+
+
+def dispatch_copy(x: torch.Tensor, pos: torch.Tensor, shape: Shape, send_buf: torch.Tensor):
+    sh = shape.c()
+    _check(lib().moe_dispatch_copy(ctypes.byref(sh), _ptr(x), _ptr(pos), _ptr(send_buf),
+                                   _stream()), "moe_dispatch_copy")
+    return send_buf
+
+
+def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
+             out: dict | None = None) -> dict:
+    """Counts, offsets, positions and the permuted send buffer (one call)."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    shape = Shape(T, H, E, k, R, W, x.dtype)
+    out = alloc_dispatch(shape, x.device) if out is None else out
+    sh = shape.c()
+    _check(lib().moe_dispatch(
+        ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]),
+        _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
+        _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]), _ptr(out["pos"]),
+        _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
+        "moe_dispatch")
+    return out
+
+
+# ----------------------------------------------------------- expert / combine
+
+def expert_scale(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
+                 expert_counts: torch.Tensor, shape: Shape,
+                 expert_out: torch.Tensor | None = None) -> torch.Tensor:
+    expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
+    sh = shape.c()
+    _check(lib().moe_expert_scale(ctypes.byref(sh), _ptr(send_buf), _ptr(expert_offsets),
+                                  _ptr(expert_counts), _ptr(expert_out), _stream()),
+           "moe_expert_scale")
+    return expert_out
+
+
+def combine(expert_out: torch.Tensor, topk_w: torch.Tensor, pos: torch.Tensor, shape: Shape,
+            y: torch.Tensor | None = None) -> torch.Tensor:
+    y = _empty((shape.T, shape.H), shape.dtype, expert_out.device) if y is None else y
+    sh = shape.c()
+    _check(lib().moe_combine(ctypes.byref(sh), _ptr(expert_out), _ptr(topk_w), _ptr(pos), _ptr(y),
+                             _stream()), "moe_combine")
+    return y
+
+
+# ---------------------------------------------------------------------- stats
+
+def stats_device(expert_counts: torch.Tensor, R: int, out: torch.Tensor | None = None):
+    """Enqueue the statistics kernel; returns the raw device struct (uint8 tensor)."""
+    E = expert_counts.numel()
+    out = _empty((STATS_BYTES,), torch.uint8, expert_counts.device) if out is None else out
+    _check(lib().moe_stats(_ptr(expert_counts), E, R, _ptr(out), _stream()), "moe_stats")
+    return out
+
+
+def stats_to_dict(raw: torch.Tensor) -> dict:
+    s = MoeStats.from_buffer_copy(raw.cpu().numpy().tobytes())
+    return {name: getattr(s, name) for name, _ in MoeStats._fields_}
+
+
+def stats(expert_counts: torch.Tensor, R: int) -> dict:
+    """Statistics as a host dict (synchronises with the stream)."""
+    return stats_to_dict(stats_device(expert_counts, R))

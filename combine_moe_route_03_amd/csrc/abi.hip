@@ -1,0 +1,179 @@
+// abi.hip -- the extern "C" entry points declared in include/moe_route.h.
+// Every call validates its arguments on the host before touching the HIP
+// runtime; on error it returns a negative moe_status and launches nothing.
+#include "../../include/moe_route.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kIndexLimit = int64_t(1) << 31;  // flat 32-bit index spaces of the row kernels
+
+int elem_bytes(int32_t dtype) {
+  return dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 0);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const moe_shape* sh) {
+  if (!sh) return MOE_ERR_ARG;
+  if (sh->dtype != MOE_F32 && sh->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (sh->T < 0 || sh->H < 1 || sh->E < 1 || sh->E > 1024 || sh->k < 1 || sh->k > 32 ||
+      sh->k > sh->E || sh->R < 1 || sh->W < 1)
+    return MOE_ERR_ARG;
+  if (sh->E % sh->R != 0) return MOE_ERR_ARG;
+  if ((sh->E / sh->R) % sh->W != 0) return MOE_ERR_ARG;
+  const int64_t row_bytes = int64_t(sh->H) * elem_bytes(sh->dtype);
+  if (row_bytes % 16 != 0) return MOE_ERR_ALIGN;
+  const int64_t picks = int64_t(sh->T) * sh->k;
+  if (picks >= kIndexLimit) return MOE_ERR_ARG;
+  if (picks * (row_bytes / 16) >= kIndexLimit) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t workspace_bytes(const moe_shape* sh) {
+  const int64_t nb = moe::num_chunks(int64_t(sh->T) * sh->k);
+  const int64_t bytes = (nb < 1 ? 1 : nb) * int64_t(sh->E) * 4;
+  return size_t((bytes + 255) / 256 * 256);
+}
+
+int check_index_args(const moe_shape* sh, const int32_t* topk_idx, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                     int32_t* wave_offsets, int32_t* pos, int32_t* row_token, void* workspace,
+                     size_t workspace_bytes_given) {
+  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets || !wave_offsets ||
+      !workspace)
+    return MOE_ERR_ARG;
+  if (sh->T > 0 && (!topk_idx || !pos || !row_token)) return MOE_ERR_ARG;
+  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        wave_offsets, pos, row_token, workspace};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+  if (workspace_bytes_given < workspace_bytes(sh)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int check_copy_args(const moe_shape* sh, const void* x, const int32_t* pos, void* send_buf) {
+  if (sh->T > 0 && (!x || !pos || !send_buf)) return MOE_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(pos, 4)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG: null pointer or size/shape outside the limits";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: pointer or row size breaks the alignment rules";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unknown dtype";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: the HIP runtime rejected a launch";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+              float* topk_w, moe_stream_t stream) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E) return MOE_ERR_ARG;
+  if (int64_t(T) * k >= kIndexLimit || int64_t(T) * E >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+  if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_route(logits, T, E, k, topk_idx, topk_w, as_stream(stream)));
+}
+
+size_t moe_dispatch_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return workspace_bytes(shape);
+}
+
+int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token, void* workspace,
+                       size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                        rank_offsets, wave_offsets, pos, row_token, workspace,
+                        workspace_bytes_given);
+  if (st != MOE_OK) return st;
+  const int64_t npicks = int64_t(shape->T) * shape->k;
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  hipStream_t s = as_stream(stream);
+  st = status_of(moe::launch_count(topk_idx, npicks, shape->E, hist, s));
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_place(topk_idx, npicks, shape->k, shape->E, shape->R, shape->W,
+                                     hist, expert_counts, expert_offsets, rank_counts,
+                                     rank_offsets, wave_offsets, pos, row_token, s));
+}
+
+int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos, void* send_buf,
+                      moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_copy_args(shape, x, pos, send_buf);
+  if (st != MOE_OK) return st;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(
+      moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, send_buf, as_stream(stream)));
+}
+
+int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx, void* send_buf,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* rank_counts,
+                 int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
+                 void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                        rank_offsets, wave_offsets, pos, row_token, workspace,
+                        workspace_bytes_given);
+  if (st != MOE_OK) return st;
+  st = check_copy_args(shape, x, pos, send_buf);
+  if (st != MOE_OK) return st;
+  st = moe_dispatch_index(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                          rank_offsets, wave_offsets, pos, row_token, workspace,
+                          workspace_bytes_given, stream);
+  if (st != MOE_OK) return st;
+  return moe_dispatch_copy(shape, x, pos, send_buf, stream);
+}
+
+int moe_expert_scale(const moe_shape* shape, const void* send_buf, const int32_t* expert_offsets,
+                     const int32_t* expert_counts, void* expert_out, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !expert_counts) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!send_buf || !expert_out)) return MOE_ERR_ARG;
+  if (!aligned(send_buf, 16) || !aligned(expert_out, 16) || !aligned(expert_offsets, 4) ||
+      !aligned(expert_counts, 4))
+    return MOE_ERR_ALIGN;
+  const int64_t rows = int64_t(shape->T) * shape->k;
+  return status_of(moe::launch_expert_scale(send_buf, shape->dtype, rows, shape->H, shape->E,
+                                            shape->R, shape->W, expert_offsets, expert_counts,
+                                            expert_out, as_stream(stream)));
+}
+
+int moe_combine(const moe_shape* shape, const void* expert_out, const float* topk_w,
+                const int32_t* pos, void* y, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->T > 0 && (!expert_out || !topk_w || !pos || !y)) return MOE_ERR_ARG;
+  if (!aligned(expert_out, 16) || !aligned(y, 16) || !aligned(topk_w, 4) || !aligned(pos, 4))
+    return MOE_ERR_ALIGN;
+  return status_of(moe::launch_combine(expert_out, shape->dtype, topk_w, pos, shape->T, shape->k,
+                                       shape->H, y, as_stream(stream)));
+}
+
+int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R, moe_stats_t* out,
+              moe_stream_t stream) {
+  if (!expert_counts || !out) return MOE_ERR_ARG;
+  if (E < 1 || E > 1024 || R < 1 || E % R != 0) return MOE_ERR_ARG;
+  if (!aligned(expert_counts, 4) || !aligned(out, 8)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_stats(expert_counts, E, R, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// device.h -- small device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN stays NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger uint).
+// -0 is folded onto +0 first so that the two compare equal, as IEEE says.
+__device__ __forceinline__ uint32_t float_order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_key_float(uint32_t key) {
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const uint32_t lane = __lane_id();
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Streaming store that does not need to stay in cache.
+template <typename V>
+__device__ __forceinline__ void store_stream(V* p, const V& v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+}  // namespace moe

@@ -1,0 +1,179 @@
+/*
+ * moe_route.h -- C ABI of the gfx950 (MI355X) library for the one-GPU share of
+ * the Mixture-of-Experts expert-parallel exchange: top-k gating, send-count
+ * matrix S with Alltoallv-style counts and offsets, stable permutation of token
+ * rows into expert/rank/wave-contiguous send buffers, gate-weighted combine,
+ * and S's skew statistics.
+ *
+ * The steps follow the MoE-layer flow of the cross-card communication
+ * explainer (cloud.baidu.com, section 4: gating -> permute by device ->
+ * all-to-all -> local experts -> all-to-all -> combine) and the EP flow of the
+ * MoE systems survey (crad.ict.ac.cn, section 1.1, steps 1-4). The all-to-all
+ * itself is not performed: the rank-bucketed send buffer is what one GPU would
+ * hand to it.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise. The
+ *     caller owns every buffer; the library never allocates, frees or keeps
+ *     pointers past the call, and holds no mutable global state.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream). Results are ready when the stream reaches that point.
+ *   - Arguments are validated on the host before anything is launched. On any
+ *     error nothing is launched and nothing is written; the return value is a
+ *     negative moe_status. A failed launch returns MOE_ERR_DEVICE; a fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - Layouts are row-major: logits[T][E] fp32, x and y [T][H], topk_idx,
+ *     topk_w and pos [T][k]; send buffers and expert outputs [T*k][H].
+ *   - Expert e lives on virtual rank r = e / L (L = E / R local experts per
+ *     rank, contiguous blocks; experts are split evenly over devices,
+ *     explainer section 3 item 1) in local slot s = e % L. Its wave is
+ *     floor(s * W / L): W waves of E / W experts each (irregular AllToAll
+ *     page, "Wave-Scheduled"), each wave reaching every rank.
+ *   - Send-buffer rows are grouped in buckets ordered by (wave, rank, slot);
+ *     inside a bucket rows follow ascending token index (stable). With W = 1
+ *     this is plain expert-id order. Counts and offsets are in ROWS; the byte
+ *     displacement of a row is rows * H * element size.
+ *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), E % R == 0, L % W == 0,
+ *     T >= 0, T * k < 2^31, H * element size a multiple of 16 bytes, hidden-
+ *     state pointers 16-byte aligned, index/weight pointers 4-byte aligned.
+ *   - T == 0 is valid: counts and offsets are written as zeros, nothing else.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,         /* null pointer, or a size/shape outside the limits */
+  MOE_ERR_ALIGN = -2,       /* a pointer or the row size breaks the alignment rules */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_dispatch_workspace_bytes() */
+  MOE_ERR_UNSUPPORTED = -4, /* unknown dtype */
+  MOE_ERR_DEVICE = -5       /* the HIP runtime rejected a launch */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem shape shared by the dispatch, expert and combine calls. */
+typedef struct {
+  int32_t T;     /* tokens held by this GPU */
+  int32_t H;     /* hidden size (elements per token row) */
+  int32_t E;     /* experts */
+  int32_t k;     /* experts per token */
+  int32_t R;     /* virtual destination ranks (E % R == 0) */
+  int32_t W;     /* expert waves (L % W == 0) */
+  int32_t dtype; /* moe_dtype of x, send buffers, expert outputs and y */
+} moe_shape;
+
+/* Skew statistics of the send-count matrix (DODOCO summary, "metrics"). */
+typedef struct {
+  double expert_max_over_mean; /* max_e c[e] / (total / E) */
+  double expert_gini;          /* Gini of the E per-expert loads */
+  double rank_max_over_mean;   /* max_r l[r] / (total / R), l = row sums of S */
+  double rank_gini;            /* Gini of the R per-rank loads */
+  int64_t total;               /* sum of S */
+  int32_t expert_max, expert_min, rank_max, rank_min;
+} moe_stats_t;
+
+/* Top-k gating, MoE systems survey section 1.1 eq. (2):
+ *   G(x) = softmax(TopK(x W_gate, k)), the non-kept logits acting as -inf.
+ * logits   [T][E] fp32 (the router GEMM output x W_gate; finite values).
+ * topk_idx [T][k] int32 out: experts by descending logit; equal logits (and
+ *          +0 / -0) are ordered by ascending expert id.
+ * topk_w   [T][k] fp32 out: exp(l_i - l_0) / sum_j exp(l_j - l_0), evaluated
+ *          in double and rounded once to fp32.
+ * Errors: MOE_ERR_ARG (null pointer with T > 0, E or k outside the limits),
+ *         MOE_ERR_ALIGN (a pointer not 4-byte aligned), MOE_ERR_DEVICE. */
+int moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+              int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/* Bytes of device workspace moe_dispatch / moe_dispatch_index need for this
+ * shape (host-only, pure; 0 for an invalid shape). */
+size_t moe_dispatch_workspace_bytes(const moe_shape* shape);
+
+/* Counts, offsets and positions: everything the Alltoallv needs before the
+ * payload moves (irregular AllToAll page: the top-k index set is the a2a
+ * send-count matrix, passed in full as Alltoallv counts; survey section 4.1:
+ * sort/count/index dispatch instead of one-hot matrix products).
+ * topk_idx       [T][k] int32 in: entries outside [0, E) are dropped picks
+ *                (not counted, pos = -1, no row).
+ * expert_counts  [E]   out: c[e]; viewed as R x L (row = destination rank,
+ *                column = local slot) it is S.
+ * expert_offsets [E]   out: first row of expert e's bucket.
+ * rank_counts    [W*R] out: rows wave w sends to rank r (Alltoallv sendcounts).
+ * rank_offsets   [W*R] out: absolute first row of (w, r); the wave-local
+ *                sdispls are rank_offsets[w*R + r] - wave_offsets[w].
+ * wave_offsets   [W+1] out: first row of each wave; wave_offsets[W] = rows.
+ * pos            [T][k] out: send-buffer row of pick (t, i).
+ * row_token      [T*k] out: token of each row (rows >= sum c are untouched).
+ * workspace      device scratch of moe_dispatch_workspace_bytes(shape) bytes
+ *                (contents need not be initialised; clobbered by the call).
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
+ *         MOE_ERR_DEVICE. */
+int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx,
+                       int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* rank_counts, int32_t* rank_offsets,
+                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
+                       void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream);
+
+/* The permute copy (explainer section 3 item 5: rows are reordered by
+ * destination and packed before sending): send_buf[pos[t][i]][:] = x[t][:],
+ * a bit copy. Each x row is read once and written k times; picks with
+ * pos outside [0, T*k) are skipped.
+ * x [T][H], send_buf [T*k][H] (dtype of shape). */
+int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos,
+                      void* send_buf, moe_stream_t stream);
+
+/* moe_dispatch_index followed by moe_dispatch_copy on the same stream. */
+int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                 void* send_buf, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* rank_counts,
+                 int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                 int32_t* row_token, void* workspace, size_t workspace_bytes,
+                 moe_stream_t stream);
+
+/* Identity-scaled experts (the experts of the synthetic workloads):
+ * expert_out[n][:] = round_dtype((e(n) + 1) * send_buf[n][:]) for every row n
+ * inside some expert's bucket [expert_offsets[e], + expert_counts[e]); other
+ * rows are untouched. Rounding is to nearest, ties to even. */
+int moe_expert_scale(const moe_shape* shape, const void* send_buf,
+                     const int32_t* expert_offsets,
+                     const int32_t* expert_counts, void* expert_out,
+                     moe_stream_t stream);
+
+/* Combine, MoE systems survey section 1.1 eq. (1) and EP flow step 4 (restore
+ * the original token order, weight each expert output by its gate value):
+ *   y[t][:] = round_dtype( fma-chain over i = 0..k-1 of
+ *             topk_w[t][i] * expert_out[pos[t][i]][:] )
+ * accumulated in fp32 in pick order with fused multiply-adds, rounded once to
+ * nearest-even. Picks with pos outside [0, T*k) contribute nothing.
+ * expert_out [T*k][H], topk_w [T][k] fp32, pos [T][k], y [T][H]. */
+int moe_combine(const moe_shape* shape, const void* expert_out,
+                const float* topk_w, const int32_t* pos, void* y,
+                moe_stream_t stream);
+
+/* Skew statistics of S from expert_counts [E] (DODOCO summary, "metrics"):
+ * per-expert max/mean and the Gini coefficient
+ *   G(v) = sum_a sum_b |v_a - v_b| / (2 n sum v)
+ * of the per-rank loads (and of the per-expert loads), with exact 64-bit
+ * integer numerators and one double division each; 0 when sum v = 0.
+ * out: DEVICE pointer to one moe_stats_t.
+ * Errors: MOE_ERR_ARG (null pointer, E outside the limits, E % R != 0). */
+int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
+              moe_stats_t* out, moe_stream_t stream);
+
+/* Human-readable name of a moe_status value (static string, never NULL). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_ROUTE_H */

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int32, _f64p, _i32p, ctypes.c_int64, _f64p]
         L.oracle_combine_f32fma.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int32, _f32p, _i32p, ctypes.c_int64, _vp]
+        L.oracle_scaled_tokens.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, _i32p, _f64p, _f32p, _i64p,
+                                           ctypes.c_int64, _f64p, _vp]
         L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
         L.oracle_gini_i64.argtypes = [_i64p, ctypes.c_int32]
         L.oracle_gini_i64.restype = ctypes.c_double
@@ -200,6 +203,29 @@ def combine_f32fma(expert_out: np.ndarray, w32: np.ndarray, pos: np.ndarray, T: 
     lib().oracle_combine_f32fma(expert_out.ctypes.data, _dtype_code(expert_out), T, H, k,
                                 _p(w32, _f32p), _p(pos, _i32p), nrows, y.ctypes.data)
     return y
+
+
+def scaled_tokens(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, tokens,
+                  w32: np.ndarray | None = None):
+    """End-to-end result for identity-scaled experts on the listed tokens:
+    (y_f64 [n,H] double, y_q [n,H] in x's dtype from the fp32 fma chain or None)."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    k = idx.shape[1]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    n = tok.shape[0]
+    y64 = np.empty((n, H), np.float64)
+    yq = None
+    if w32 is not None:
+        w32 = np.ascontiguousarray(w32, dtype=np.float32)
+        yq = np.empty((n, H), x.dtype)
+    lib().oracle_scaled_tokens(x.ctypes.data, _dtype_code(x), H, E, k, _p(idx, _i32p),
+                               _p(w, _f64p), _p(w32, _f32p) if w32 is not None else None,
+                               _p(tok, _i64p), n, _p(y64, _f64p),
+                               yq.ctypes.data if yq is not None else None)
+    return y64, yq
 
 
 def stats(expert_counts: np.ndarray, R: int) -> dict:

@@ -60,6 +60,13 @@ static double load_elem(const void* base, int32_t dtype, int64_t i) {
   return (double)f;
 }
 
+static double load_elem_bits_bf16(uint16_t b) {
+  uint32_t bits = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
 static void store_elem(void* base, int32_t dtype, int64_t i, double v) {
   if (dtype == ORACLE_F32)
     ((float*)base)[i] = (float)v; /* C conversion: round to nearest even */
@@ -207,6 +214,31 @@ void oracle_combine_f32fma(const void* expert_out, int32_t dtype, int64_t T,
       }
       store_elem(y, dtype, t * H + h, (double)acc);
     }
+}
+
+void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
+                          int32_t k, const int32_t* idx, const double* w,
+                          const float* w32, const int64_t* tokens, int64_t n,
+                          double* y_f64, void* y_q) {
+  for (int64_t j = 0; j < n; ++j) {
+    int64_t t = tokens[j];
+    for (int64_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      float acc32 = 0.0f;
+      for (int32_t i = 0; i < k; ++i) {
+        int32_t e = idx[t * k + i];
+        if (e < 0 || e >= E) continue; /* dropped pick */
+        /* the expert output element, rounded to dtype as the expert stores it */
+        double prod = (double)(e + 1) * load_elem(x, dtype, t * H + h);
+        double o = (dtype == ORACLE_F32) ? (double)(float)prod
+                                         : load_elem_bits_bf16(oracle_round_bf16(prod));
+        if (w) acc += w[t * k + i] * o;
+        if (w32) acc32 = fmaf(w32[t * k + i], (float)o, acc32);
+      }
+      if (y_f64) y_f64[j * H + h] = acc;
+      if (y_q) store_elem(y_q, dtype, j * H + h, (double)acc32);
+    }
+  }
 }
 
 /* ------------------------------------------------------------------- stats */

@@ -84,6 +84,17 @@ void oracle_combine_f32fma(const void* expert_out, int32_t dtype, int64_t T,
                            int64_t H, int32_t k, const float* w,
                            const int32_t* pos, int64_t nrows, void* y);
 
+/* The whole path for identity-scaled experts, on selected tokens only: for each
+ * listed token t, y[j][h] = sum_i w[t][i] * round_dtype((idx[t][i] + 1) * x[t][h])
+ * (combine of the scaled copies of x[t]; survey section 1.1 eq. (1)).
+ * y_f64 [n][H] is the double sum; y_q [n][H] is the same sum taken as the
+ * single-precision fma chain in pick order with fp32 weights w32, rounded to
+ * dtype (the kernel-precision quantisation). Either output may be NULL. */
+void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
+                          int32_t k, const int32_t* idx, const double* w,
+                          const float* w32, const int64_t* tokens, int64_t n,
+                          double* y_f64, void* y_q);
+
 /* Skew statistics of S, DODOCO summary ("metrics"): per-expert max/mean and
  * Gini coefficient of per-rank loads (per-expert Gini alongside). */
 typedef struct {

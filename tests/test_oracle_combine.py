@@ -140,3 +140,18 @@ def test_golden_tiny_combine_factor():
     out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
     y = oracle.combine_f64(out, w, d["pos"], 4)
     np.testing.assert_allclose(y[:, 0], g["combine_factor"], rtol=1e-15)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scaled_tokens_equals_composed_path(dtype):
+    # the sampled-token shortcut must reproduce dispatch -> expert -> combine exactly
+    T, E, k, R, W, H = 70, 32, 4, 4, 2, 40
+    idx, w, x, d = _route_dispatch(T, E, k, R, W, H, dtype, seed=9)
+    out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
+    w32 = w.astype(np.float32)
+    y64 = oracle.combine_f64(out, w, d["pos"], T)
+    yq = oracle.combine_f32fma(out, w32, d["pos"], T)
+    toks = np.array([0, 5, 69, 33, 33, 12])
+    s64, sq = oracle.scaled_tokens(x, idx, w, E, toks, w32=w32)
+    np.testing.assert_array_equal(s64, y64[toks])
+    np.testing.assert_array_equal(sq, yq[toks])
