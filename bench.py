@@ -37,6 +37,30 @@ SINGLE_KERNEL = {"route": "route_kernel", "dispatch_copy": "copy_kernel",
                  "stats": "stats_kernel"}
 
 
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        st = self.hip.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return out.value
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -46,6 +70,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-evicted loop")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K steps replayed from one captured HIP graph")
     return ap.parse_args()
 
 
@@ -140,48 +166,113 @@ def main() -> int:
         "stats": (L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream)),
     }
 
-    def step(evs=None):
-        for s_i, name in enumerate(STAGES):
-            if evs is not None:
-                evs[s_i].record()
+    hipev = HipEvents()
+    set_events = L.moe_set_timing_events
+
+    def step(kev=None, iev=None):
+        """One pass of the path. kev[name] = (start, stop) raw events filled by the
+        library's extended launches (kernel execution time); iev = torch events
+        around the two-kernel index stage."""
+        for name in STAGES:
             fn, a = calls[name]
+            if name == "dispatch_index" and iev is not None:
+                iev[0].record()
+            if kev is not None and name in kev:
+                set_events(*kev[name])
             st = fn(*a)
+            if kev is not None and name in kev:
+                set_events(None, None)
+            if name == "dispatch_index" and iev is not None:
+                iev[1].record()
             if st != 0:
                 raise RuntimeError(f"{name}: {moe.status_string(st)}")
-        if evs is not None:
-            evs[len(STAGES)].record()
+
+    def timed_events(n):
+        kev = [{nm: (hipev.create(), hipev.create()) for nm in SINGLE_KERNEL} for _ in range(n)]
+        iev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        return kev, iev
+
+    def stage_means(kev, iev):
+        out = {nm: float(np.mean([hipev.ms(*kv[nm]) for kv in kev])) for nm in SINGLE_KERNEL}
+        out["dispatch_index"] = float(np.mean([a.elapsed_time(b) for a, b in iev]))
+        return out
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
+    kev, iev = timed_events(K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(evs[i])
+        step(kev[i], iev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {K} timed steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
-
-    stage_ms = {name: float(np.mean([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)]))
-                for s, name in enumerate(STAGES)}
+    stage_ms = stage_means(kev, iev)
     nbytes = algorithmic_bytes(wl)
+
+    # Same steps without any timing events (host launch cost only).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t0
+
+    graph_wall = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stream_c = ctypes.c_void_p(side.cuda_stream)
+            for nm in calls:  # rebind the stream argument to the capture stream
+                fn, a = calls[nm]
+                calls[nm] = (fn, tuple(stream_c if x is stream else x for x in a))
+            step()
+            torch.cuda.current_stream().synchronize()
+            with torch.cuda.graph(g, stream=side):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        for nm in calls:
+            fn, a = calls[nm]
+            calls[nm] = (fn, tuple(stream if x is stream_c else x for x in a))
+
+    # Plain device copy of 1 GiB (beyond the Infinity Cache): the bandwidth a
+    # trivial streaming kernel reaches on this box.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(5):
+        dst.copy_(src)
+    cb.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    del src, dst
 
     cold_ms = None
     if not args.no_cold:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         Kc = max(5, min(K, 50))
-        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
-                for _ in range(Kc)]
+        ckev, ciev = timed_events(Kc)
         for i in range(Kc):
             flush.fill_(i & 0xFF)
-            step(cevs[i])
+            step(ckev[i], ciev[i])
         torch.cuda.synchronize()
-        cold_ms = {name: float(np.mean([cevs[i][s].elapsed_time(cevs[i][s + 1])
-                                        for i in range(Kc)]))
-                   for s, name in enumerate(STAGES)}
+        cold_ms = stage_means(ckev, ciev)
         del flush
 
     dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
@@ -223,7 +314,14 @@ def main() -> int:
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": nbytes[dom], "avg_us": round(stage_ms[dom] * 1e3, 2)},
         "stages": stage_report(stage_ms),
+        "wall_ms_per_step_without_timing_events": round(wall_plain * 1e3 / K, 4),
+        "plain_copy_GBs": round(copy_gbs, 1),
+        "stage_timing": "kernel start/stop events from the library's extended launches; "
+                        "dispatch_index = torch events around its two kernels",
     }
+    if graph_wall is not None:
+        result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
+                                  "tokens_per_s": round(T * K / graph_wall, 1)}
     if cold_ms is not None:
         cdc = cold_ms["dispatch_index"] + cold_ms["dispatch_copy"] + cold_ms["combine"]
         result["cold_cache"] = {

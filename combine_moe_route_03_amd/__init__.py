@@ -55,6 +55,7 @@ SIGNATURES = {
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "moe_set_timing_events": ([_vp, _vp], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 

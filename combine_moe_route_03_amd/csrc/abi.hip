@@ -35,7 +35,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; 
 hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 size_t workspace_bytes(const moe_shape* sh) {
-  const int64_t nb = moe::num_chunks(int64_t(sh->T) * sh->k);
+  const int64_t nb = moe::num_chunks(int64_t(sh->T) * sh->k, sh->E);
   const int64_t bytes = (nb < 1 ? 1 : nb) * int64_t(sh->E) * 4;
   return size_t((bytes + 255) / 256 * 256);
 }
@@ -64,7 +64,21 @@ int check_copy_args(const moe_shape* sh, const void* x, const int32_t* pos, void
 
 }  // namespace
 
+namespace moe {
+LaunchTiming& launch_timing() {
+  thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace moe
+
 extern "C" {
+
+int moe_set_timing_events(void* start_event, void* stop_event) {
+  moe::LaunchTiming& t = moe::launch_timing();
+  t.start = reinterpret_cast<hipEvent_t>(start_event);
+  t.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
 
 const char* moe_status_string(int status) {
   switch (status) {

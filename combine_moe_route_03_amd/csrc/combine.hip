@@ -4,7 +4,8 @@
 //
 // Flat over (token, 16-byte column): each thread gathers its column from the k
 // expert rows of its token (all k loads issued before any arithmetic), runs the
-// fp32 fused multiply-add chain in pick order, rounds once to the output dtype
+// fp32 fused multiply-add chain in pick order (seeded with -0, the additive
+// identity, so an all -0 sum stays -0), rounds once to the output dtype
 // and writes one 16-byte vector. Lanes of a wave cover consecutive columns of
 // one row, so every gather and the store are contiguous 1 KiB segments.
 #include "device.h"
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint4* __restrict
 
   uint4 out;
   if constexpr (kBF16) {
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float a[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};  // -0: additive identity
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k && ok[i]) {
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint4* __restrict
     out.z = pack_bf16x2(a[4], a[5]);
     out.w = pack_bf16x2(a[6], a[7]);
   } else {
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    float a[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k && ok[i]) {
@@ -82,15 +83,13 @@ template <int KMAX>
 hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int k,
               uint32_t nvec, uint32_t total, uint32_t nrows, void* y, hipStream_t s) {
   const unsigned grid = (total + kBlock - 1) / kBlock;
+  const uint4* in = static_cast<const uint4*>(eo);
+  uint4* out = static_cast<uint4*>(y);
   if (bf16)
-    hipLaunchKernelGGL((combine_kernel<KMAX, true>), dim3(grid), dim3(kBlock), 0, s,
-                       static_cast<const uint4*>(eo), w, pos, k, nvec, total, nrows,
-                       static_cast<uint4*>(y));
-  else
-    hipLaunchKernelGGL((combine_kernel<KMAX, false>), dim3(grid), dim3(kBlock), 0, s,
-                       static_cast<const uint4*>(eo), w, pos, k, nvec, total, nrows,
-                       static_cast<uint4*>(y));
-  return hipGetLastError();
+    return launch(combine_kernel<KMAX, true>, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec,
+                  total, nrows, out);
+  return launch(combine_kernel<KMAX, false>, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec,
+                total, nrows, out);
 }
 
 }  // namespace

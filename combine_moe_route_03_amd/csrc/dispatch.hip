@@ -6,13 +6,18 @@
 // same-expert rows contiguously (survey section 1.1, EP flow step 2).
 //
 // Three kernels, all on the caller's stream:
-//   count_kernel  one block per chunk of picks: LDS histogram -> hist[chunk][E]
-//   place_kernel  one block per chunk: prefix of earlier chunks + bucket-order
-//                 exclusive scan (every block redoes the E-long scan in LDS, so
-//                 no separate scan launch is needed); block 0 publishes counts
-//                 and offsets; then stable in-chunk ranks from wave64 ballots
-//                 (bit-sliced match on the expert id, popcount of lower lanes)
-//                 and an LDS prefix across the block's four waves.
+//   count_kernel  one 1024-thread block per chunk of picks: LDS histogram ->
+//                 hist[chunk][E] (LDS integer atomics: order-free, exact).
+//   place_kernel  one 1024-thread block per chunk. Each block re-derives what it
+//                 needs from the small hist matrix instead of waiting for a
+//                 separate scan launch: the prefix of earlier chunks and the
+//                 totals (threads laid out as (row slice, expert) so all loads
+//                 are independent), then the bucket-order exclusive scan (one
+//                 bucket per thread). Block 0 publishes counts and offsets.
+//                 Stable in-chunk ranks come from wave64 ballots (bit-sliced
+//                 match on the expert id, popcount of lower lanes) and an LDS
+//                 prefix across the block's 16 waves; the next batch of ids is
+//                 prefetched while the current one is placed.
 //   copy_kernel   flat over (token, 16-byte column): one load of x, k stores.
 #include "device.h"
 #include "launch.h"
@@ -20,114 +25,139 @@
 namespace moe {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kB = kIndexBlock;  // 1024 threads, 16 waves
+constexpr int kWaves = kB / kWave;
 constexpr int kMaxE = 1024;
 
-__global__ __launch_bounds__(kBlock) void count_kernel(const int32_t* __restrict__ idx,
-                                                       int64_t npicks, int64_t chunk, int E,
-                                                       int32_t* __restrict__ hist) {
+__global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ idx,
+                                                   int64_t npicks, int64_t chunk, int E,
+                                                   int32_t* __restrict__ hist) {
   __shared__ int32_t h[kMaxE];
-  for (int e = threadIdx.x; e < E; e += kBlock) h[e] = 0;
+  const int tid = threadIdx.x;
+  if (tid < E) h[tid] = 0;
   __syncthreads();
   const int64_t p0 = (int64_t)blockIdx.x * chunk;
   const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
-  for (int64_t p = p0 + threadIdx.x; p < p1; p += kBlock) {
-    const int e = idx[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  for (int64_t base = p0; base < p1; base += 4 * kB) {
+    int ev[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t p = base + u * kB + tid;
+      ev[u] = (p < p1) ? idx[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&h[ev[u]], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kBlock) hist[(int64_t)blockIdx.x * E + e] = h[e];
+  if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = h[tid];
 }
 
-__global__ __launch_bounds__(kBlock) void place_kernel(
-    const int32_t* __restrict__ idx, int64_t npicks, int64_t chunk, int nb, int k, int E, int R,
-    int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
+__global__ __launch_bounds__(kB) void place_kernel(
+    const int32_t* __restrict__ idx, int64_t npicks, int64_t chunk, int nb, int k, int E,
+    int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
     int32_t* __restrict__ pos, int32_t* __restrict__ row_token) {
-  __shared__ int32_t run[kMaxE];      // next free row per expert for this block
-  __shared__ int32_t cnt[kMaxE];      // total picks per expert
-  __shared__ int32_t off[kMaxE];      // first row of each expert's bucket
-  __shared__ int32_t wcnt[4][kMaxE];  // per-wave counts inside one 256-pick batch
-  __shared__ int32_t part[4];
+  __shared__ int32_t run[kMaxE];           // next free row per expert for this block
+  __shared__ int32_t cnt[kMaxE];           // total picks per expert
+  __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
+  __shared__ int32_t ppre[kB];             // (slice, expert) partial prefix
+  __shared__ int32_t pall[kB];             // (slice, expert) partial total
+  __shared__ int32_t wcnt[kWaves][kMaxE];  // per-wave counts of one 1024-pick batch
+  __shared__ int32_t part[kWaves];
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = blockIdx.x;
   const int L = E / R, LW = L / W;
+  const int ep = 1 << elog;        // E rounded up to a power of two
+  const int nslice = kB >> elog;   // row slices of the hist matrix
 
-  for (int e = tid; e < E; e += kBlock) {
-    wcnt[0][e] = 0;
-    wcnt[1][e] = 0;
-    wcnt[2][e] = 0;
-    wcnt[3][e] = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) wcnt[q][tid] = 0;
   }
-  // 1. Picks of expert e in earlier chunks (run) and in all chunks (cnt).
-  for (int e = tid; e < E; e += kBlock) {
+
+  // 1. Picks of each expert in earlier chunks and in all chunks. Thread
+  //    (s, e) = (tid >> elog, tid & (ep-1)) sums rows s, s+nslice, ...
+  {
+    const int e = tid & (ep - 1), s = tid >> elog;
     int pre = 0, all = 0;
-    for (int bb = 0; bb < nb; ++bb) {
-      const int v = hist[(int64_t)bb * E + e];
-      all += v;
-      pre += (bb < b) ? v : 0;
+    if (e < E) {
+      for (int r0 = s; r0 < nb; r0 += 4 * nslice) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u * nslice;
+          v[u] = (r < nb) ? hist[(int64_t)r * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          all += v[u];
+          pre += (r0 + u * nslice < b) ? v[u] : 0;
+        }
+      }
     }
-    run[e] = pre;
-    cnt[e] = all;
+    ppre[tid] = pre;
+    pall[tid] = all;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int P = 0, A = 0;
+    for (int s = 0; s < nslice; ++s) {
+      P += ppre[s * ep + tid];
+      A += pall[s * ep + tid];
+    }
+    run[tid] = P;
+    cnt[tid] = A;
   }
   __syncthreads();
 
-  // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread
-  //    tid owns buckets 4*tid .. 4*tid+3 (E <= 1024 = 4 * 256).
-  int c[4], sum = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = 4 * tid + q;
-    c[q] = (j < E) ? cnt[bucket_expert(j, R, L, LW)] : 0;
-    sum += c[q];
-  }
-  int incl = sum;
+  // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread j
+  //    owns bucket j.
+  const int cj = (tid < E) ? cnt[bucket_expert(tid, R, L, LW)] : 0;
+  int incl = cj;
   for (int o = 1; o < kWave; o <<= 1) {
     const int y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
   if (lane == kWave - 1) part[wid] = incl;
   __syncthreads();
-  int excl = incl - sum, total = 0;
+  int excl = incl - cj, total = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kWaves; ++q) {
     excl += (q < wid) ? part[q] : 0;
     total += part[q];
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = 4 * tid + q;
-    if (j < E) off[bucket_expert(j, R, L, LW)] = excl;
-    excl += c[q];
-  }
+  if (tid < E) off[bucket_expert(tid, R, L, LW)] = excl;
   __syncthreads();
 
   if (b == 0) {
-    for (int e = tid; e < E; e += kBlock) {
-      expert_counts[e] = cnt[e];
-      expert_offsets[e] = off[e];
+    if (tid < E) {
+      expert_counts[tid] = cnt[tid];
+      expert_offsets[tid] = off[tid];
     }
-    for (int q = tid; q < W * R; q += kBlock) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
+    for (int q = tid; q < W * R; q += kB) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
       int s = 0;
       for (int j = q * LW; j < q * LW + LW; ++j) s += cnt[bucket_expert(j, R, L, LW)];
       rank_counts[q] = s;
       rank_offsets[q] = off[bucket_expert(q * LW, R, L, LW)];
     }
-    for (int w = tid; w <= W; w += kBlock)
+    for (int w = tid; w <= W; w += kB)
       wave_offsets[w] = (w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total;
   }
-  for (int e = tid; e < E; e += kBlock) run[e] += off[e];
+  if (tid < E) run[tid] += off[tid];
   __syncthreads();
 
-  // 3. Stable ranks inside the chunk, 256 picks per batch.
+  // 3. Stable ranks inside the chunk, 1024 picks per batch.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const int64_t p0 = (int64_t)b * chunk;
   const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
-  for (int64_t base = p0; base < p1; base += kBlock) {
+  int e_next = (p0 + tid < p1) ? idx[p0 + tid] : -1;
+  for (int64_t base = p0; base < p1; base += kB) {
     const int64_t p = base + tid;
-    const int e = (p < p1) ? idx[p] : -1;
+    const int e = e_next;
+    e_next = (p + kB < p1) ? idx[p + kB] : -1;  // prefetch the next batch
     const bool valid = (p < p1) && ((unsigned)e < (unsigned)E);
     uint64_t peers = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -159,21 +189,24 @@ __global__ __launch_bounds__(kBlock) void place_kernel(
 }
 
 // send[pos[t][i]][c] = x[t][c] for 16-byte columns c; each x vector loaded once.
+constexpr int kCopyBlock = 256;
+
 template <int U>
-__global__ __launch_bounds__(kBlock) void copy_kernel(const uint4* __restrict__ x,
-                                                      const int32_t* __restrict__ pos, int k,
-                                                      uint32_t nvec, uint32_t total,
-                                                      uint32_t nrows, uint4* __restrict__ send) {
-  const uint32_t q0 = blockIdx.x * (uint32_t)(kBlock * U) + threadIdx.x;
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ pos, int k,
+                                                          uint32_t nvec, uint32_t total,
+                                                          uint32_t nrows,
+                                                          uint4* __restrict__ send) {
+  const uint32_t q0 = blockIdx.x * (uint32_t)(kCopyBlock * U) + threadIdx.x;
   uint4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t q = q0 + u * kBlock;
+    const uint32_t q = q0 + u * kCopyBlock;
     v[u] = (q < total) ? x[q] : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t q = q0 + u * kBlock;
+    const uint32_t q = q0 + u * kCopyBlock;
     if (q < total) {
       const uint32_t t = q / nvec, col = q - t * nvec;
       const int32_t* pp = pos + (size_t)t * k;
@@ -185,28 +218,32 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4* __restrict__ 
   }
 }
 
+int ilog2_ceil(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
 }  // namespace
 
 hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist,
                         hipStream_t s) {
-  const int64_t nb = num_chunks(npicks);
+  const int64_t nb = num_chunks(npicks, E);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(count_kernel, dim3((unsigned)nb), dim3(kBlock), 0, s, idx, npicks,
-                     chunk_picks(npicks), E, hist);
-  return hipGetLastError();
+  return launch(count_kernel, dim3((unsigned)nb), dim3(kB), 0, s, idx, npicks,
+                chunk_picks(npicks, E), E, hist);
 }
 
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
                         int32_t* pos, int32_t* row_token, hipStream_t s) {
-  const int64_t nb = num_chunks(npicks);
+  const int64_t nb = num_chunks(npicks, E);
   // With no picks one block still runs to publish zero counts and offsets.
   const unsigned grid = nb == 0 ? 1u : (unsigned)nb;
-  hipLaunchKernelGGL(place_kernel, dim3(grid), dim3(kBlock), 0, s, idx, npicks,
-                     chunk_picks(npicks), (int)nb, k, E, R, W, hist, expert_counts,
-                     expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token);
-  return hipGetLastError();
+  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, chunk_picks(npicks, E),
+                (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets,
+                rank_counts, rank_offsets, wave_offsets, pos, row_token);
 }
 
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
@@ -216,11 +253,9 @@ hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t 
   const uint32_t nvec = (uint32_t)(row_bytes / 16);
   const uint32_t total = (uint32_t)T * nvec;
   const uint32_t nrows = (uint32_t)T * (uint32_t)k;
-  const unsigned grid = (unsigned)((total + kBlock * U - 1) / (kBlock * U));
-  hipLaunchKernelGGL((copy_kernel<U>), dim3(grid), dim3(kBlock), 0, s,
-                     static_cast<const uint4*>(x), pos, k, nvec, total, nrows,
-                     static_cast<uint4*>(send));
-  return hipGetLastError();
+  const unsigned grid = (unsigned)((total + kCopyBlock * U - 1) / (kCopyBlock * U));
+  return launch(copy_kernel<U>, dim3(grid), dim3(kCopyBlock), 0, s, static_cast<const uint4*>(x),
+                pos, k, nvec, total, nrows, static_cast<uint4*>(send));
 }
 
 }  // namespace moe

@@ -3,27 +3,62 @@
 // launch on the given stream. Each returns hipSuccess or the launch error.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
 
-// The T*k picks are cut into chunks for counting and placing: at least
-// kMinChunkPicks picks each, at most kMaxChunks chunks, multiples of 256.
-constexpr int64_t kMinChunkPicks = 2048;
-constexpr int64_t kMaxChunks = 512;
+// ---------------------------------------------------------------- chunking
+// Counting and placing cut the T*k picks into chunks of whole 1024-pick
+// batches (one 1024-thread block per chunk). Every place block re-reads all
+// chunk histograms (chunks x E int32), so the chunk count is capped at
+// 65536 / pow2(E) (and 512) to keep that read at most 256 KiB per block.
+constexpr int kIndexBlock = 1024;
 
-inline int64_t chunk_picks(int64_t npicks) {
-  int64_t c = (npicks + kMaxChunks - 1) / kMaxChunks;
-  c = (c + 255) / 256 * 256;
-  return c < kMinChunkPicks ? kMinChunkPicks : c;
+inline int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
 }
 
-inline int64_t num_chunks(int64_t npicks) {
-  return npicks == 0 ? 0 : (npicks + chunk_picks(npicks) - 1) / chunk_picks(npicks);
+inline int64_t chunk_picks(int64_t npicks, int E) {
+  int64_t max_chunks = 65536 / pow2_at_least(E);
+  if (max_chunks > 512) max_chunks = 512;
+  int64_t c = (npicks + max_chunks - 1) / max_chunks;
+  c = (c + kIndexBlock - 1) / kIndexBlock * kIndexBlock;
+  return c < kIndexBlock ? kIndexBlock : c;
 }
 
+inline int64_t num_chunks(int64_t npicks, int E) {
+  if (npicks == 0) return 0;
+  const int64_t c = chunk_picks(npicks, E);
+  return (npicks + c - 1) / c;
+}
+
+// ------------------------------------------------------------ kernel timing
+// Optional per-thread start/stop events recorded by every launch (benchmark
+// hook; see moe_set_timing_events). Null events: plain launches.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem,
+                  hipStream_t s, Args... args) {
+  const LaunchTiming& tm = launch_timing();
+  if (tm.start != nullptr || tm.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, tm.start, tm.stop, 0u,
+                          static_cast<Params>(args)...);
+  else
+    kernel<<<grid, block, shmem, s>>>(static_cast<Params>(args)...);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- launchers
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         hipStream_t s);
 

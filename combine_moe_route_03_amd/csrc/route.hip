@@ -112,9 +112,8 @@ hipError_t go(const float* logits, int T, int E, int k, int G, int32_t* idx, flo
               hipStream_t s) {
   const int64_t threads = (int64_t)T * G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((route_kernel<V, kVec4>), dim3(blocks), dim3(256), 0, s, logits, T, E, k,
-                     ilog2(G), idx, w);
-  return hipGetLastError();
+  return launch(route_kernel<V, kVec4>, dim3(blocks), dim3(256), 0, s, logits, T, E, k, ilog2(G),
+                idx, w);
 }
 
 }  // namespace

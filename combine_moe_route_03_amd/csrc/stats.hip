@@ -113,9 +113,8 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s) {
-  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(kBlock), 0, s, counts, E, R,
-                     static_cast<moe_stats_t*>(out));
-  return hipGetLastError();
+  return launch(stats_kernel, dim3(1), dim3(kBlock), 0, s, counts, E, R,
+                static_cast<moe_stats_t*>(out));
 }
 
 }  // namespace moe

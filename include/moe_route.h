@@ -153,8 +153,10 @@ int moe_expert_scale(const moe_shape* shape, const void* send_buf,
  * the original token order, weight each expert output by its gate value):
  *   y[t][:] = round_dtype( fma-chain over i = 0..k-1 of
  *             topk_w[t][i] * expert_out[pos[t][i]][:] )
- * accumulated in fp32 in pick order with fused multiply-adds, rounded once to
- * nearest-even. Picks with pos outside [0, T*k) contribute nothing.
+ * accumulated in fp32 in pick order with fused multiply-adds starting from -0
+ * (the additive identity, so identity experts return x bit for bit, -0
+ * included), rounded once to nearest-even. Picks with pos outside [0, T*k)
+ * contribute nothing.
  * expert_out [T*k][H], topk_w [T][k] fp32, pos [T][k], y [T][H]. */
 int moe_combine(const moe_shape* shape, const void* expert_out,
                 const float* topk_w, const int32_t* pos, void* y,
@@ -169,6 +171,16 @@ int moe_combine(const moe_shape* shape, const void* expert_out,
  * Errors: MOE_ERR_ARG (null pointer, E outside the limits, E % R != 0). */
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
               moe_stats_t* out, moe_stream_t stream);
+
+/* Kernel timing hook for benchmarks (not a step of the path). While set, every
+ * kernel this library launches from the calling thread is launched with AMD's
+ * extended launch so that `start_event` is recorded when the kernel begins and
+ * `stop_event` when it ends; hipEventElapsedTime(start, stop) is then that
+ * kernel's execution time. Each launch overwrites the pair (an entry point
+ * that launches several kernels leaves the last one's times). Events are
+ * created by the caller (hipEventCreate) and are hipEvent_t handles passed as
+ * void*. The setting is thread-local; NULL, NULL turns it off. Returns MOE_OK. */
+int moe_set_timing_events(void* start_event, void* stop_event);
 
 /* Human-readable name of a moe_status value (static string, never NULL). */
 const char* moe_status_string(int status);

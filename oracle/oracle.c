@@ -190,7 +190,7 @@ void oracle_combine_f64(const void* expert_out, int32_t dtype, int64_t T,
                         const int32_t* pos, int64_t nrows, double* y) {
   for (int64_t t = 0; t < T; ++t)
     for (int64_t h = 0; h < H; ++h) {
-      double acc = 0.0;
+      double acc = -0.0; /* additive identity: -0 + v == v for every v */
       for (int32_t i = 0; i < k; ++i) {
         int32_t p = pos[t * k + i];
         if (p < 0 || p >= nrows) continue;
@@ -205,7 +205,7 @@ void oracle_combine_f32fma(const void* expert_out, int32_t dtype, int64_t T,
                            const int32_t* pos, int64_t nrows, void* y) {
   for (int64_t t = 0; t < T; ++t)
     for (int64_t h = 0; h < H; ++h) {
-      float acc = 0.0f;
+      float acc = -0.0f;
       for (int32_t i = 0; i < k; ++i) {
         int32_t p = pos[t * k + i];
         if (p < 0 || p >= nrows) continue;
@@ -223,8 +223,8 @@ void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
   for (int64_t j = 0; j < n; ++j) {
     int64_t t = tokens[j];
     for (int64_t h = 0; h < H; ++h) {
-      double acc = 0.0;
-      float acc32 = 0.0f;
+      double acc = -0.0; /* additive identity: -0 + v == v for every v */
+      float acc32 = -0.0f;
       for (int32_t i = 0; i < k; ++i) {
         int32_t e = idx[t * k + i];
         if (e < 0 || e >= E) continue; /* dropped pick */

@@ -302,3 +302,27 @@ def test_full_size_sampled(name):
     same_w = (host(w)[toks] == w32[toks]).all(axis=1)
     np.testing.assert_array_equal(yg[same_w], yq[same_w])
     assert same_w.mean() > 0.99
+
+
+def test_timing_events_hook():
+    # the benchmark hook records a kernel's own start/stop; results are unchanged
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    a, b = ctypes.c_void_p(), ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(a)) == 0 and hip.hipEventCreate(ctypes.byref(b)) == 0
+    wl = PARITY["zipf"]
+    logits = dev(synth.logits(wl))
+    ref_idx, ref_w = moe.route(logits, wl.k)
+    assert moe.lib().moe_set_timing_events(a, b) == 0
+    try:
+        idx, w = moe.route(logits, wl.k)
+    finally:
+        moe.lib().moe_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    assert 0.0 < ms.value < 100.0
+    assert torch.equal(idx, ref_idx) and torch.equal(w, ref_w)

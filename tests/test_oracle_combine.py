@@ -155,3 +155,20 @@ def test_scaled_tokens_equals_composed_path(dtype):
     s64, sq = oracle.scaled_tokens(x, idx, w, E, toks, w32=w32)
     np.testing.assert_array_equal(s64, y64[toks])
     np.testing.assert_array_equal(sq, yq[toks])
+
+
+def test_signed_zero_survives_identity_experts():
+    # -0 is the additive identity: a sum of -0 terms is -0, so identity experts
+    # give back a -0 input bit for bit; +0 stays +0.
+    x = np.array([[-0.0, 0.0, 1.5, -2.0]], np.float32)
+    idx = np.array([[0, 1]], np.int32)
+    w = np.array([[0.75, 0.25]])
+    d = oracle.dispatch(x, idx, 2, 1, 1)
+    y32 = oracle.combine_f32fma(d["send_buf"], w.astype(np.float32), d["pos"], 1)
+    assert y32.view(np.uint32).tolist() == x.view(np.uint32).tolist()
+    y64 = oracle.combine_f64(d["send_buf"], w, d["pos"], 1)
+    assert np.signbit(y64[0, 0]) and not np.signbit(y64[0, 1])
+    xb = synth.f32_to_bf16_bits(x)
+    yb = oracle.combine_f32fma(oracle.dispatch(xb, idx, 2, 1, 1)["send_buf"],
+                               w.astype(np.float32), d["pos"], 1)
+    assert yb.tolist() == xb.tolist()
