@@ -3,7 +3,8 @@
 // flow step 4: restore the original order, weight by the gate confidence).
 //
 // Flat over (token, 16-byte column): each thread gathers its column from the k
-// expert rows of its token (all k loads issued before any arithmetic), runs the
+// expert rows of its token (all k streaming loads issued before any
+// arithmetic; each expert row is read exactly once), runs the
 // fp32 fused multiply-add chain in pick order (seeded with -0, the additive
 // identity, so an all -0 sum stays -0), rounds once to the output dtype
 // and writes one 16-byte vector. Lanes of a wave cover consecutive columns of
@@ -17,74 +18,69 @@ namespace {
 constexpr int kBlock = 256;
 
 template <int KMAX, bool kBF16>
-__global__ __launch_bounds__(kBlock) void combine_kernel(const uint4* __restrict__ eo,
+__global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__ eo,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ pos, int k,
                                                          uint32_t nvec, uint32_t total,
-                                                         uint32_t nrows, uint4* __restrict__ y) {
+                                                         uint32_t nrows, v4u* __restrict__ y) {
   const uint32_t q = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
   if (q >= total) return;
   const uint32_t t = q / nvec, col = q - t * nvec;
   const int32_t* pp = pos + (size_t)t * k;
   const float* ww = w + (size_t)t * k;
 
-  uint4 v[KMAX];
+  v4u v[KMAX];
   float wt[KMAX];
   bool ok[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
     ok[i] = false;
     wt[i] = 0.f;
-    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    v[i] = v4u{0u, 0u, 0u, 0u};
     if (i < k) {
       const int32_t P = pp[i];
       wt[i] = ww[i];
       ok[i] = (uint32_t)P < nrows;
-      if (ok[i]) v[i] = eo[(size_t)P * nvec + col];
+      if (ok[i]) v[i] = load_stream(eo + (size_t)P * nvec + col);
     }
   }
 
-  uint4 out;
+  v4u out;
   if constexpr (kBF16) {
     float a[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};  // -0: additive identity
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k && ok[i]) {
-        const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          a[2 * j] = fmaf(wt[i], bf16_lo(c[j]), a[2 * j]);
-          a[2 * j + 1] = fmaf(wt[i], bf16_hi(c[j]), a[2 * j + 1]);
+          a[2 * j] = fmaf(wt[i], bf16_lo(v[i][j]), a[2 * j]);
+          a[2 * j + 1] = fmaf(wt[i], bf16_hi(v[i][j]), a[2 * j + 1]);
         }
       }
     }
-    out.x = pack_bf16x2(a[0], a[1]);
-    out.y = pack_bf16x2(a[2], a[3]);
-    out.z = pack_bf16x2(a[4], a[5]);
-    out.w = pack_bf16x2(a[6], a[7]);
+    out = v4u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+              pack_bf16x2(a[6], a[7])};
   } else {
     float a[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k && ok[i]) {
-        a[0] = fmaf(wt[i], __uint_as_float(v[i].x), a[0]);
-        a[1] = fmaf(wt[i], __uint_as_float(v[i].y), a[1]);
-        a[2] = fmaf(wt[i], __uint_as_float(v[i].z), a[2]);
-        a[3] = fmaf(wt[i], __uint_as_float(v[i].w), a[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = fmaf(wt[i], __uint_as_float(v[i][j]), a[j]);
       }
     }
-    out = make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
-                     __float_as_uint(a[3]));
+    out = v4u{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+              __float_as_uint(a[3])};
   }
-  y[q] = out;
+  store_stream(y + q, out);
 }
 
 template <int KMAX>
 hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int k,
               uint32_t nvec, uint32_t total, uint32_t nrows, void* y, hipStream_t s) {
   const unsigned grid = (total + kBlock - 1) / kBlock;
-  const uint4* in = static_cast<const uint4*>(eo);
-  uint4* out = static_cast<uint4*>(y);
+  const v4u* in = static_cast<const v4u*>(eo);
+  v4u* out = static_cast<v4u*>(y);
   if (bf16)
     return launch(combine_kernel<KMAX, true>, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec,
                   total, nrows, out);

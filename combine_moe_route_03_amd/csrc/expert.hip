@@ -2,7 +2,8 @@
 // multiplies its rows by (e + 1). Rows of one expert are contiguous in the send
 // buffer (survey section 1.1, EP flow step 3 runs on contiguous same-expert
 // rows), so a row's expert is found by binary search over the bucket starts
-// staged in LDS. Each thread streams U 16-byte vectors (all loads first).
+// staged in LDS. Each thread streams kU 16-byte vectors (all loads first,
+// streaming loads and stores: every row is touched once).
 #include "device.h"
 #include "launch.h"
 
@@ -11,38 +12,34 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kMaxE = 1024;
-constexpr int kU = 4;
+constexpr int kU = 2;
 
 template <bool kBF16>
-__device__ __forceinline__ uint4 scale_vec(uint4 v, float sc) {
-  uint4 o;
-  if constexpr (kBF16) {
-    o.x = pack_bf16x2(sc * bf16_lo(v.x), sc * bf16_hi(v.x));
-    o.y = pack_bf16x2(sc * bf16_lo(v.y), sc * bf16_hi(v.y));
-    o.z = pack_bf16x2(sc * bf16_lo(v.z), sc * bf16_hi(v.z));
-    o.w = pack_bf16x2(sc * bf16_lo(v.w), sc * bf16_hi(v.w));
-  } else {
-    o.x = __float_as_uint(sc * __uint_as_float(v.x));
-    o.y = __float_as_uint(sc * __uint_as_float(v.y));
-    o.z = __float_as_uint(sc * __uint_as_float(v.z));
-    o.w = __float_as_uint(sc * __uint_as_float(v.w));
+__device__ __forceinline__ v4u scale_vec(v4u v, float sc) {
+  v4u o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (kBF16)
+      o[j] = pack_bf16x2(sc * bf16_lo(v[j]), sc * bf16_hi(v[j]));
+    else
+      o[j] = __float_as_uint(sc * __uint_as_float(v[j]));
   }
   return o;
 }
 
 template <bool kBF16>
 __global__ __launch_bounds__(kBlock) void expert_scale_kernel(
-    const uint4* __restrict__ in, uint32_t nvec, uint32_t total, int E, int R, int W,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ cnts, uint4* __restrict__ out) {
+    const v4u* __restrict__ in, uint32_t nvec, uint32_t total, int E, int R, int W,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ cnts, v4u* __restrict__ out) {
   __shared__ int32_t start[kMaxE];  // bucket starts in (wave, rank, slot) order
   __shared__ int32_t stop[kMaxE];   // bucket ends
   __shared__ int32_t bexp[kMaxE];   // expert of each bucket
   const uint32_t q0 = blockIdx.x * (uint32_t)(kBlock * kU) + threadIdx.x;
-  uint4 v[kU];
+  v4u v[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const uint32_t q = q0 + u * kBlock;
-    v[u] = (q < total) ? in[q] : make_uint4(0u, 0u, 0u, 0u);
+    v[u] = (q < total) ? load_stream(in + q) : v4u{0u, 0u, 0u, 0u};
   }
   const int L = E / R, LW = L / W;
   for (int j = threadIdx.x; j < E; j += kBlock) {
@@ -64,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void expert_scale_kernel(
       else hi = mid - 1;
     }
     if (n < start[lo] || n >= stop[lo]) continue;  // row outside every bucket
-    out[q] = scale_vec<kBF16>(v[u], (float)(bexp[lo] + 1));
+    store_stream(out + q, scale_vec<kBF16>(v[u], (float)(bexp[lo] + 1)));
   }
 }
 
@@ -78,8 +75,8 @@ hipError_t launch_expert_scale(const void* in, int dtype, int64_t rows, int64_t 
   const uint32_t nvec = (uint32_t)(H * (bf16 ? 2 : 4) / 16);
   const uint32_t total = (uint32_t)rows * nvec;
   const unsigned grid = (total + kBlock * kU - 1) / (kBlock * kU);
-  const uint4* src = static_cast<const uint4*>(in);
-  uint4* dst = static_cast<uint4*>(out);
+  const v4u* src = static_cast<const v4u*>(in);
+  v4u* dst = static_cast<v4u*>(out);
   if (bf16)
     return launch(expert_scale_kernel<true>, dim3(grid), dim3(kBlock), 0, s, src, nvec, total, E,
                   R, W, expert_offsets, expert_counts, dst);
