@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_scaled_tokens.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, _i32p, _f64p, _f32p, _i64p,
                                            ctypes.c_int64, _f64p, _vp]
+        _u16p = ctypes.POINTER(ctypes.c_uint16)
+        L.oracle_expert_swiglu_rows.argtypes = [_u16p, _i32p, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, _u16p, _u16p, _f64p, _u16p]
         L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
         L.oracle_gini_i64.argtypes = [_i64p, ctypes.c_int32]
         L.oracle_gini_i64.restype = ctypes.c_double
@@ -226,6 +229,24 @@ def scaled_tokens(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, tokens,
                                _p(tok, _i64p), n, _p(y64, _f64p),
                                yq.ctypes.data if yq is not None else None)
     return y64, yq
+
+
+def expert_swiglu_rows(rows: np.ndarray, row_expert, w_gate_up: np.ndarray,
+                       w_down: np.ndarray):
+    """SwiGLU FFN of the given bf16 rows: (out_f64 [n,H], out_bf16 bits [n,H])."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    n, H = rows.shape
+    I = w_down.shape[2]
+    assert w_gate_up.shape[1:] == (2 * I, H) and w_down.shape[1:] == (H, I)
+    re = np.ascontiguousarray(np.asarray(row_expert, dtype=np.int32))
+    gu = np.ascontiguousarray(w_gate_up, dtype=np.uint16)
+    dn = np.ascontiguousarray(w_down, dtype=np.uint16)
+    o64 = np.empty((n, H), np.float64)
+    o16 = np.empty((n, H), np.uint16)
+    u16 = ctypes.POINTER(ctypes.c_uint16)
+    lib().oracle_expert_swiglu_rows(_p(rows, u16), _p(re, _i32p), n, H, I, _p(gu, u16),
+                                    _p(dn, u16), _p(o64, _f64p), _p(o16, u16))
+    return o64, o16
 
 
 def stats(expert_counts: np.ndarray, R: int) -> dict:

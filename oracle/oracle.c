@@ -183,6 +183,38 @@ void oracle_expert_scale(const void* in, int32_t dtype, int64_t H, int32_t E,
   }
 }
 
+void oracle_expert_swiglu_rows(const uint16_t* rows, const int32_t* row_expert,
+                               int64_t n, int64_t H, int64_t I,
+                               const uint16_t* w_gate_up,
+                               const uint16_t* w_down, double* out_f64,
+                               uint16_t* out_bf16) {
+  double* hmid = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int64_t r = 0; r < n; ++r) {
+    const uint16_t* s = rows + r * H;
+    const int64_t e = row_expert[r];
+    const uint16_t* wg = w_gate_up + e * 2 * I * H;
+    const uint16_t* wu = wg + I * H;
+    const uint16_t* wd = w_down + e * H * I;
+    for (int64_t j = 0; j < I; ++j) {
+      double g = 0.0, u = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        double sv = load_elem_bits_bf16(s[h]);
+        g += load_elem_bits_bf16(wg[j * H + h]) * sv;
+        u += load_elem_bits_bf16(wu[j * H + h]) * sv;
+      }
+      double silu = g / (1.0 + exp(-g));
+      hmid[j] = load_elem_bits_bf16(oracle_round_bf16(silu * u));
+    }
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < I; ++j) acc += load_elem_bits_bf16(wd[c * I + j]) * hmid[j];
+      if (out_f64) out_f64[r * H + c] = acc;
+      if (out_bf16) out_bf16[r * H + c] = oracle_round_bf16(acc);
+    }
+  }
+  free(hmid);
+}
+
 /* ----------------------------------------------------------------- combine */
 
 void oracle_combine_f64(const void* expert_out, int32_t dtype, int64_t T,

@@ -95,6 +95,21 @@ void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
                           const float* w32, const int64_t* tokens, int64_t n,
                           double* y_f64, void* y_q);
 
+/* SwiGLU expert FFN of the local-layer workload, on selected send-buffer rows
+ * (the pages name only an FFN; the workload fixes SwiGLU, intermediate size I,
+ * bf16 weights). For row n of expert e = row_expert[n], in double:
+ *   g_j = sum_h Wg[e][j][h] s[h],  u_j = sum_h Wu[e][j][h] s[h]   (j < I)
+ *   h_j = round_bf16( g_j / (1 + exp(-g_j)) * u_j )   (bf16 intermediate)
+ *   out[c] = sum_j Wd[e][c][j] h_j                     (c < H)
+ * w_gate_up [E][2I][H] bf16 (rows 0..I-1 gate, I..2I-1 up); w_down [E][H][I].
+ * out_f64 [n][H] is the double sum, out_bf16 [n][H] its bf16 rounding (either
+ * may be NULL). */
+void oracle_expert_swiglu_rows(const uint16_t* rows, const int32_t* row_expert,
+                               int64_t n, int64_t H, int64_t I,
+                               const uint16_t* w_gate_up,
+                               const uint16_t* w_down, double* out_f64,
+                               uint16_t* out_bf16);
+
 /* Skew statistics of S, DODOCO summary ("metrics"): per-expert max/mean and
  * Gini coefficient of per-rank loads (per-expert Gini alongside). */
 typedef struct {
