@@ -53,6 +53,9 @@ SIGNATURES = {
     "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_expert_swiglu_workspace_bytes": ([_shp, _i32], ctypes.c_size_t),
+    "moe_expert_swiglu": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                          ctypes.c_int),
     "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "moe_set_timing_events": ([_vp, _vp], ctypes.c_int),
@@ -207,6 +210,29 @@ def expert_scale(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
     _check(lib().moe_expert_scale(ctypes.byref(sh), _ptr(send_buf), _ptr(expert_offsets),
                                   _ptr(expert_counts), _ptr(expert_out), _stream()),
            "moe_expert_scale")
+    return expert_out
+
+
+def expert_swiglu_workspace_bytes(shape: Shape, I: int) -> int:
+    sh = shape.c()
+    return int(lib().moe_expert_swiglu_workspace_bytes(ctypes.byref(sh), I))
+
+
+def expert_swiglu(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
+                  expert_counts: torch.Tensor, shape: Shape, w_gate_up: torch.Tensor,
+                  w_down: torch.Tensor, expert_out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """SwiGLU expert FFN on MFMA; w_gate_up [E,2I,H], w_down [E,H,I] bf16."""
+    I = w_down.shape[2]
+    expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
+    if workspace is None:
+        workspace = _empty((max(expert_swiglu_workspace_bytes(shape, I), 1),), torch.uint8,
+                           send_buf.device)
+    sh = shape.c()
+    _check(lib().moe_expert_swiglu(ctypes.byref(sh), I, _ptr(send_buf), _ptr(expert_offsets),
+                                   _ptr(expert_counts), _ptr(w_gate_up), _ptr(w_down),
+                                   _ptr(expert_out), _ptr(workspace), workspace.numel(),
+                                   _stream()), "moe_expert_swiglu")
     return expert_out
 
 

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "csrc")
 LIB = os.path.join(PKG, "libmoe_route.so")
 
-SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "combine.hip", "expert.hip", "stats.hip"]
+SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "combine.hip", "expert.hip", "ffn.hip",
+           "stats.hip"]
 
 # -packed-fp32-ops off: plain fp32 VALU code only (no v_pk_*_f32 forms).
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

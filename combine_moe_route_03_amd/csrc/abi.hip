@@ -171,6 +171,35 @@ int moe_expert_scale(const moe_shape* shape, const void* send_buf, const int32_t
                                             expert_out, as_stream(stream)));
 }
 
+size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I) {
+  if (check_shape(shape) != MOE_OK || I < 64 || I % 64 != 0) return 0;
+  const int64_t bytes = int64_t(shape->T) * shape->k * I * 2;
+  return size_t((bytes < 256 ? 256 : bytes + 255) / 256 * 256);
+}
+
+int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
+                      const int32_t* expert_offsets, const int32_t* expert_counts,
+                      const void* w_gate_up, const void* w_down, void* expert_out,
+                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (I < 64 || I % 64 != 0 || shape->H % 128 != 0) return MOE_ERR_ARG;
+  if (int64_t(shape->E) * 2 * I * shape->H >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+  if (!expert_offsets || !expert_counts || !w_gate_up || !w_down || !workspace) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!send_buf || !expert_out)) return MOE_ERR_ARG;
+  if (!aligned(send_buf, 16) || !aligned(expert_out, 16) || !aligned(w_gate_up, 16) ||
+      !aligned(w_down, 16) || !aligned(workspace, 16) || !aligned(expert_offsets, 4) ||
+      !aligned(expert_counts, 4))
+    return MOE_ERR_ALIGN;
+  if (int64_t(shape->T) * shape->k * I >= kIndexLimit) return MOE_ERR_ARG;
+  if (workspace_bytes_given < moe_expert_swiglu_workspace_bytes(shape, I)) return MOE_ERR_WORKSPACE;
+  const int64_t rows = int64_t(shape->T) * shape->k;
+  return status_of(moe::launch_expert_swiglu(send_buf, rows, shape->H, I, shape->E,
+                                             expert_offsets, expert_counts, w_gate_up, w_down,
+                                             workspace, expert_out, as_stream(stream)));
+}
+
 int moe_combine(const moe_shape* shape, const void* expert_out, const float* topk_w,
                 const int32_t* pos, void* y, moe_stream_t stream) {
   int st = check_shape(shape);

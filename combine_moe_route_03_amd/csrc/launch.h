@@ -83,6 +83,13 @@ hipError_t launch_combine(const void* expert_out, int dtype, const float* w, con
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s);
 
+// Grouped SwiGLU FFN (bf16): gate/up GEMM with fused SiLU*up into hbuf
+// [rows][I], then the down GEMM into out [rows][H]. Needs I % 64 == 0 and
+// H % 128 == 0.
+hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, int E,
+                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
+                                const void* w_down, void* hbuf, void* out, hipStream_t s);
+
 // Expert id of the j-th bucket when buckets run in (wave, rank, slot) order:
 // L = E / R slots per rank, LW = L / W slots per wave.
 __host__ __device__ __forceinline__ int bucket_expert(int j, int R, int L, int LW) {

@@ -149,6 +149,28 @@ int moe_expert_scale(const moe_shape* shape, const void* send_buf,
                      const int32_t* expert_counts, void* expert_out,
                      moe_stream_t stream);
 
+/* Bytes of device workspace moe_expert_swiglu needs (the bf16 intermediate,
+ * T*k x I); 0 for an invalid shape or I. Host-only, pure. */
+size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I);
+
+/* SwiGLU expert FFN on each expert's contiguous rows (expert compute, survey
+ * section 1.1 EP flow step 3; per-expert variable-size GEMMs driven by the
+ * counts, survey section 4.1), on MFMA:
+ *   g = s . Wg[e][j], u = s . Wu[e][j]      (fp32 accumulation over H)
+ *   h_j = round_bf16( g / (1 + exp(-g)) * u )   (stored in the workspace)
+ *   expert_out[n][c] = round_bf16( sum_j Wd[e][c][j] h_j )  (fp32 accumulation)
+ * for every row n in [expert_offsets[e], + expert_counts[e]); other rows are
+ * untouched. bf16 only (shape->dtype == MOE_BF16); I % 64 == 0, H % 128 == 0.
+ * w_gate_up [E][2I][H] bf16 (rows 0..I-1 gate, I..2I-1 up), w_down [E][H][I]
+ * bf16, send_buf and expert_out [T*k][H], all 16-byte aligned. workspace:
+ * moe_expert_swiglu_workspace_bytes(shape, I) bytes, clobbered.
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
+ *         MOE_ERR_DEVICE. */
+int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
+                      const int32_t* expert_offsets, const int32_t* expert_counts,
+                      const void* w_gate_up, const void* w_down, void* expert_out,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* Combine, MoE systems survey section 1.1 eq. (1) and EP flow step 4 (restore
  * the original token order, weight each expert output by its gate value):
  *   y[t][:] = round_dtype( fma-chain over i = 0..k-1 of
