@@ -3,16 +3,19 @@
 
 One step = the whole path on one batch of synthetic input, inputs already in
 HBM: route (top-k gating) -> dispatch index (counts, offsets, positions) ->
-dispatch copy (permute into the send buffer) -> identity-scaled experts ->
-combine -> skew statistics. Every step runs in the library's HIP kernels on
-torch's current stream; torch only provides memory, the stream and events.
+dispatch copy (permute into the send buffer) -> experts (identity-scaled, or
+the SwiGLU FFN on MFMA for the local-layer workload) -> combine -> skew
+statistics. Every step runs in the library's HIP kernels on torch's current
+stream; torch only provides memory and the stream.
 
-Prints ONE JSON line. `value` is whole-step tokens/s over the K timed steps
-(wall clock, bracketed by synchronisations). Per-stage kernel times come from
-HIP events recorded on the launch stream inside the same timed region; the
-dominant kernel's algorithmic bytes / its average duration gives `roofline`.
-A second, untimed-for-`value` loop repeats the steps after evicting the 256 MB
-Infinity Cache (512 MiB scratch write) to report cold-cache stage times.
+Prints ONE JSON line. `value` is whole-step tokens/s over K timed steps (wall
+clock, bracketed by synchronisations, no instrumentation). A second K-step
+loop, right after it, times every stage on the GPU itself: the library's timing
+hook launches the stage's kernels with start/stop events (extended launches on
+the launch stream), so a stage's time is its kernels' execution time. The
+dominant kernel's algorithmic bytes (or flops) over its average duration is
+`roofline`. A third loop repeats the instrumented steps after evicting the
+256 MB Infinity Cache (a 512 MiB scratch write) for cold-cache stage times.
 """
 from __future__ import annotations
 
@@ -29,12 +32,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine", "stats")
-# Stages that are exactly one kernel launch (roofline candidates).
-SINGLE_KERNEL = {"route": "route_kernel", "dispatch_copy": "copy_kernel",
-                 "expert": "expert_scale_kernel", "combine": "combine_kernel",
-                 "stats": "stats_kernel"}
+KERNEL_OF = {"route": "route_kernel", "dispatch_index": "count_kernel+place_kernel",
+             "dispatch_copy": "copy_kernel", "expert": "expert_scale_kernel",
+             "combine": "combine_kernel", "stats": "stats_kernel"}
 
 
 class HipEvents:
@@ -45,7 +48,6 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
@@ -62,7 +64,8 @@ class HipEvents:
 
 
 def parse_args():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -76,37 +79,62 @@ def parse_args():
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Minimum HBM bytes each stage must move (per launch)."""
+    """Minimum HBM bytes each stage must move per launch (b = element bytes)."""
     T, H, E, k, b = wl.T, wl.H, wl.E, wl.k, wl.elem_bytes
-    return {
-        "route": T * E * 4 + T * k * 8,                  # logits in; idx + w out
-        "dispatch_index": 12 * T * k,                    # idx in; pos + row_token out
+    out = {
+        "route": T * E * 4 + T * k * 8,                          # logits in; idx + w out
+        "dispatch_index": 12 * T * k,                            # idx in; pos + row_token out
         "dispatch_copy": T * H * b + T * k * H * b + 4 * T * k,  # x once, k copies, pos
-        "expert": 2 * T * k * H * b,                     # send rows in, expert rows out
-        "combine": T * k * H * b + 8 * T * k + T * H * b,  # k rows, w + pos in; y out
+        "expert": 2 * T * k * H * b,                             # rows in, rows out
+        "combine": T * k * H * b + 8 * T * k + T * H * b,        # k rows, w + pos in; y out
         "stats": 4 * E,
     }
+    if wl.expert == "swiglu":  # + the expert weights, read once
+        out["expert"] += 3 * wl.E * wl.H * wl.I * 2
+    return out
 
 
-def cpu_baseline(wl, logits, x, seconds: float) -> dict:
-    """The oracle, as it stands, timed on the host on whole passes of the workload."""
+def ffn_flops(wl) -> int:
+    return 6 * wl.T * wl.k * wl.H * wl.I  # gate/up (2*2I*H) + down (2*H*I) per row
+
+
+def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None) -> dict:
+    """The oracle, as it stands, timed on the host (single thread)."""
+    import numpy as np
+
     import oracle
 
-    passes, t_used = 0, 0.0
-    while passes < 2 or t_used < seconds:
-        t0 = time.perf_counter()
-        idx, w = oracle.route(logits, wl.k)
-        d = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
-        out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
-        oracle.combine_f64(out, w, d["pos"], wl.T)
-        oracle.stats(d["expert_counts"], wl.R)
-        t_used += time.perf_counter() - t0
-        passes += 1
-    return {"value": round(wl.T * passes / t_used, 1), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{passes} full passes of the {wl.name} workload (T={wl.T}) through the "
-                      f"single-threaded C oracle: route, dispatch, expert, combine (fp64), stats; "
-                      f"{t_used:.1f} s on {platform.processor() or platform.machine()}"}
+    if ffn_weights is None:
+        passes, t_used = 0, 0.0
+        while passes < 2 or t_used < seconds:
+            t0 = time.perf_counter()
+            idx, w = oracle.route(logits, wl.k)
+            d = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
+            out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
+            oracle.combine_f64(out, w, d["pos"], wl.T)
+            oracle.stats(d["expert_counts"], wl.R)
+            t_used += time.perf_counter() - t0
+            passes += 1
+        tokens = wl.T * passes
+        sample = (f"{passes} full passes of the {wl.name} workload (T={wl.T}) through the "
+                  f"single-threaded C oracle: route, dispatch, expert, combine (fp64), stats")
+    else:
+        gu, dn = ffn_weights
+        tokens, t_used = 0, 0.0
+        t = 0
+        while t_used < seconds or tokens < 2:
+            t0 = time.perf_counter()
+            lt = logits[t:t + 1]
+            idx, w = oracle.route(lt, wl.k)
+            o64, _ = oracle.expert_swiglu_rows(np.repeat(x[t:t + 1], wl.k, 0), idx[0], gu, dn)
+            (w[0][:, None] * o64).sum(0)
+            t_used += time.perf_counter() - t0
+            tokens += 1
+            t = (t + 1) % wl.T
+        sample = (f"{tokens} tokens of the {wl.name} workload one at a time through the "
+                  f"single-threaded C oracle: route, SwiGLU FFN of the k picks (fp64), combine")
+    return {"value": round(tokens / t_used, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; {t_used:.1f} s on {platform.processor() or platform.machine()}"}
 
 
 def main() -> int:
@@ -125,19 +153,21 @@ def main() -> int:
     import synth
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.expert != "scale":
-        wl = wl.with_(expert="scale")
+    swiglu = wl.expert == "swiglu"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     T, H, E, k, R, W = wl.T, wl.H, wl.E, wl.k, wl.R, wl.W
-    print(f"[bench] workload {wl.name}: T={T} H={H} E={E} k={k} R={R} W={W} {wl.dtype}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] workload {wl.name}: T={T} H={H} E={E} k={k} R={R} W={W} {wl.dtype} "
+          f"expert={wl.expert}", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
 
     logits_np, x_np = synth.logits(wl), synth.hidden(wl)
-    logits = torch.from_numpy(logits_np).to(dev)
-    x = (torch.from_numpy(x_np).to(dev) if wl.dtype == "f32"
-         else torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16))
+    logits, x = to_dev(logits_np), to_dev(x_np)
     shape = moe.Shape(T, H, E, k, R, W, tdt)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -145,6 +175,12 @@ def main() -> int:
     expert_out = torch.empty_like(buf["send_buf"])
     y = torch.empty((T, H), dtype=tdt, device=dev)
     stats_raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=dev)
+    ffn_np = None
+    if swiglu:
+        ffn_np = synth.swiglu_weights(wl)
+        w_gu, w_dn = to_dev(ffn_np[0]), to_dev(ffn_np[1])
+        ffn_ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
+                             device=dev)
 
     # Pre-marshalled C-ABI calls: the per-step host cost is six foreign calls.
     L = moe.lib()
@@ -165,78 +201,77 @@ def main() -> int:
         "combine": (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream)),
         "stats": (L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream)),
     }
+    if swiglu:
+        calls["expert"] = (L.moe_expert_swiglu, (
+            shp, wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
+            P(w_gu), P(w_dn), P(expert_out), P(ffn_ws), ffn_ws.numel(), stream))
+    kernel_of = dict(KERNEL_OF)
+    if swiglu:
+        kernel_of["expert"] = "ffn_gemm_kernel<gate_up>+ffn_gemm_kernel<down>"
 
     hipev = HipEvents()
     set_events = L.moe_set_timing_events
 
-    def step(kev=None, iev=None):
-        """One pass of the path. kev[name] = (start, stop) raw events filled by the
-        library's extended launches (kernel execution time); iev = torch events
-        around the two-kernel index stage."""
+    def step(evs=None):
+        """One pass of the path; evs[name] = (start, stop) events for the hook."""
         for name in STAGES:
             fn, a = calls[name]
-            if name == "dispatch_index" and iev is not None:
-                iev[0].record()
-            if kev is not None and name in kev:
-                set_events(*kev[name])
+            if evs is not None:
+                set_events(*evs[name])
             st = fn(*a)
-            if kev is not None and name in kev:
+            if evs is not None:
                 set_events(None, None)
-            if name == "dispatch_index" and iev is not None:
-                iev[1].record()
             if st != 0:
                 raise RuntimeError(f"{name}: {moe.status_string(st)}")
 
-    def timed_events(n):
-        kev = [{nm: (hipev.create(), hipev.create()) for nm in SINGLE_KERNEL} for _ in range(n)]
-        iev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        return kev, iev
+    def new_events(n):
+        return [{nm: (hipev.create(), hipev.create()) for nm in STAGES} for _ in range(n)]
 
-    def stage_means(kev, iev):
-        out = {nm: float(np.mean([hipev.ms(*kv[nm]) for kv in kev])) for nm in SINGLE_KERNEL}
-        out["dispatch_index"] = float(np.mean([a.elapsed_time(b) for a, b in iev]))
-        return out
+    def stage_means(evs):
+        return {nm: float(np.mean([hipev.ms(*e[nm]) for e in evs])) for nm in STAGES}
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # ---- timed region 1: K plain steps -> value
     K = args.steps
-    kev, iev = timed_events(K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(kev[i], iev[i])
+    for _ in range(K):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {K} timed steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
-    stage_ms = stage_means(kev, iev)
-    nbytes = algorithmic_bytes(wl)
 
-    # Same steps without any timing events (host launch cost only).
+    # ---- timed region 2: K instrumented steps -> per-stage kernel times
+    evs = new_events(K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step()
+        step(evs[i])
     torch.cuda.synchronize()
-    wall_plain = time.perf_counter() - t0
+    wall_instr = time.perf_counter() - t0
+    stage_ms = stage_means(evs)
+    nbytes = algorithmic_bytes(wl)
 
     graph_wall = None
     if args.graph:
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
+        stream_c = ctypes.c_void_p(side.cuda_stream)
+        saved = dict(calls)
+        for nm in calls:  # rebind the stream argument to the capture stream
+            fn, a = calls[nm]
+            calls[nm] = (fn, tuple(stream_c if v is stream else v for v in a))
         with torch.cuda.stream(side):
-            stream_c = ctypes.c_void_p(side.cuda_stream)
-            for nm in calls:  # rebind the stream argument to the capture stream
-                fn, a = calls[nm]
-                calls[nm] = (fn, tuple(stream_c if x is stream else x for x in a))
             step()
             torch.cuda.current_stream().synchronize()
             with torch.cuda.graph(g, stream=side):
                 step()
         torch.cuda.synchronize()
+        calls.update(saved)
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
@@ -245,12 +280,9 @@ def main() -> int:
             g.replay()
         torch.cuda.synchronize()
         graph_wall = time.perf_counter() - t0
-        for nm in calls:
-            fn, a = calls[nm]
-            calls[nm] = (fn, tuple(stream if x is stream_c else x for x in a))
 
-    # Plain device copy of 1 GiB (beyond the Infinity Cache): the bandwidth a
-    # trivial streaming kernel reaches on this machine.
+    # Plain device copy of 1 GiB (beyond the Infinity Cache) with the HIP
+    # runtime's own copy kernel: a reference streaming rate on this machine.
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -267,25 +299,48 @@ def main() -> int:
     if not args.no_cold:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         Kc = max(5, min(K, 50))
-        ckev, ciev = timed_events(Kc)
+        cevs = new_events(Kc)
         for i in range(Kc):
             flush.fill_(i & 0xFF)
-            step(ckev[i], ciev[i])
+            step(cevs[i])
         torch.cuda.synchronize()
-        cold_ms = stage_means(ckev, ciev)
+        cold_ms = stage_means(cevs)
         del flush
 
-    dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
-    dom_gbs = nbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    dc_ms = stage_ms["dispatch_index"] + stage_ms["dispatch_copy"] + stage_ms["combine"]
-    dc_bytes = nbytes["dispatch_index"] + nbytes["dispatch_copy"] + nbytes["combine"]
+    def gbs(name, ms):
+        return nbytes[name] / (ms * 1e-3) / 1e9
 
     def stage_report(ms):
-        return {n: {"us": round(ms[n] * 1e3, 2),
-                    "GB/s": round(nbytes[n] / (ms[n] * 1e-3) / 1e9, 1),
-                    "frac_hbm_peak": round(nbytes[n] / (ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-                for n in STAGES}
+        rep = {}
+        for n in STAGES:
+            rep[n] = {"us": round(ms[n] * 1e3, 2), "GB/s": round(gbs(n, ms[n]), 1),
+                      "frac_hbm_peak": round(gbs(n, ms[n]) / HBM_PEAK_GBS, 4),
+                      "kernels": kernel_of[n]}
+        if swiglu:
+            tf = ffn_flops(wl) / (ms["expert"] * 1e-3) / 1e12
+            rep["expert"]["TFLOP/s"] = round(tf, 1)
+            rep["expert"]["frac_mfma_bf16_peak"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        return rep
 
+    # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
+    single = [n for n in ("route", "dispatch_copy", "expert", "combine", "stats")
+              if not (swiglu and n == "expert")]
+    dom = max(single, key=lambda n: stage_ms[n])
+    roofline = {"bound": "hbm", "kernel": kernel_of[dom],
+                "achieved": round(gbs(dom, stage_ms[dom]), 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs(dom, stage_ms[dom]) / HBM_PEAK_GBS, 4),
+                "traffic": None, "bytes_per_launch": nbytes[dom],
+                "avg_us": round(stage_ms[dom] * 1e3, 2)}
+    if swiglu and stage_ms["expert"] > stage_ms[dom]:
+        tf = ffn_flops(wl) / (stage_ms["expert"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": kernel_of["expert"], "achieved": round(tf, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
+
+    dc_keys = ("dispatch_index", "dispatch_copy", "combine")
+    dc_ms = sum(stage_ms[n] for n in dc_keys)
+    dc_bytes = sum(nbytes[n] for n in dc_keys)
     result = {
         "metric": METRIC,
         "value": round(T * K / wall, 1),
@@ -298,9 +353,10 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded logits and hidden states; identity-scaled experts)",
+        "data": "synthetic (seeded logits and hidden states"
+                + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
         "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
-                   "waves": W, "routing": wl.routing,
+                   "waves": W, "routing": wl.routing, "expert": wl.expert,
                    "step": "route+dispatch_index+dispatch_copy+expert+combine+stats"},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
@@ -309,29 +365,29 @@ def main() -> int:
             "frac_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes": dc_bytes,
         },
-        "roofline": {"bound": "hbm", "kernel": SINGLE_KERNEL[dom], "achieved": round(dom_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": nbytes[dom], "avg_us": round(stage_ms[dom] * 1e3, 2)},
+        "roofline": roofline,
         "stages": stage_report(stage_ms),
-        "wall_ms_per_step_without_timing_events": round(wall_plain * 1e3 / K, 4),
+        "stage_timing": "GPU execution time of each stage's kernels, from start/stop events "
+                        "recorded by the library's extended launches (instrumented loop of "
+                        f"{K} steps, {wall_instr * 1e3 / K:.4f} ms/step wall)",
         "plain_copy_GBs": round(copy_gbs, 1),
-        "stage_timing": "kernel start/stop events from the library's extended launches; "
-                        "dispatch_index = torch events around its two kernels",
     }
+    if swiglu:
+        result["config"]["I"] = wl.I
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}
     if cold_ms is not None:
-        cdc = cold_ms["dispatch_index"] + cold_ms["dispatch_copy"] + cold_ms["combine"]
+        cdc = sum(cold_ms[n] for n in dc_keys)
         result["cold_cache"] = {
             "stages": stage_report(cold_ms),
             "dispatch_combine": {"us": round(cdc * 1e3, 2),
                                  "tokens_per_s": round(T / (cdc * 1e-3), 1),
                                  "GB/s": round(dc_bytes / (cdc * 1e-3) / 1e9, 1),
-                                 "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+                                 "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9
+                                                        / HBM_PEAK_GBS, 4)}}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, logits_np, x_np, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, logits_np, x_np, args.cpu_seconds, ffn_np)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -77,6 +77,7 @@ int moe_set_timing_events(void* start_event, void* stop_event) {
   moe::LaunchTiming& t = moe::launch_timing();
   t.start = reinterpret_cast<hipEvent_t>(start_event);
   t.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  t.started = false;
   return MOE_OK;
 }
 

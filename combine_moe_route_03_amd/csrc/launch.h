@@ -38,22 +38,27 @@ inline int64_t num_chunks(int64_t npicks, int E) {
 }
 
 // ------------------------------------------------------------ kernel timing
-// Optional per-thread start/stop events recorded by every launch (benchmark
-// hook; see moe_set_timing_events). Null events: plain launches.
+// Optional per-thread timing events (benchmark hook; see
+// moe_set_timing_events): the first kernel launched while they are set records
+// `start` when it begins, every launch records `stop` when it ends, so the pair
+// brackets the execution of all of them. Null events: plain launches.
 struct LaunchTiming {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
+  bool started = false;
 };
 LaunchTiming& launch_timing();
 
 template <typename... Params, typename... Args>
 hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem,
                   hipStream_t s, Args... args) {
-  const LaunchTiming& tm = launch_timing();
-  if (tm.start != nullptr || tm.stop != nullptr)
-    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, tm.start, tm.stop, 0u,
+  LaunchTiming& tm = launch_timing();
+  if (tm.start != nullptr || tm.stop != nullptr) {
+    hipEvent_t first = tm.started ? nullptr : tm.start;
+    tm.started = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, first, tm.stop, 0u,
                           static_cast<Params>(args)...);
-  else
+  } else
     kernel<<<grid, block, shmem, s>>>(static_cast<Params>(args)...);
   return hipGetLastError();
 }

@@ -194,14 +194,15 @@ int moe_combine(const moe_shape* shape, const void* expert_out,
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
               moe_stats_t* out, moe_stream_t stream);
 
-/* Kernel timing hook for benchmarks (not a step of the path). While set, every
- * kernel this library launches from the calling thread is launched with AMD's
- * extended launch so that `start_event` is recorded when the kernel begins and
- * `stop_event` when it ends; hipEventElapsedTime(start, stop) is then that
- * kernel's execution time. Each launch overwrites the pair (an entry point
- * that launches several kernels leaves the last one's times). Events are
- * created by the caller (hipEventCreate) and are hipEvent_t handles passed as
- * void*. The setting is thread-local; NULL, NULL turns it off. Returns MOE_OK. */
+/* Kernel timing hook for benchmarks (not a step of the path). While set, the
+ * kernels this library launches from the calling thread use AMD's extended
+ * launch: the first one records `start_event` when it begins executing and
+ * every one records `stop_event` when it ends, so hipEventElapsedTime(start,
+ * stop) is the GPU time from the first kernel's start to the last one's end
+ * (one kernel's execution time for the single-kernel entry points). Calling
+ * this again re-arms `start`. Events are created by the caller (hipEventCreate)
+ * and passed as void* hipEvent_t handles. The setting is thread-local; NULL,
+ * NULL turns it off. Returns MOE_OK. */
 int moe_set_timing_events(void* start_event, void* stop_event);
 
 /* Human-readable name of a moe_status value (static string, never NULL). */

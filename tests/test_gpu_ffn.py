@@ -131,12 +131,16 @@ def test_local_layer_full_size_sampled():
     got = host(eo_gpu[torch.from_numpy(rows).to(DEV)])
     _check_rows(got, o64, atol=1e-3)
 
-    # combined tokens: y_t = sum_i w_ti * FFN_{e_ti}(x_t)
+    # combined tokens: y_t = sum_i w_ti * bf16(FFN_{e_ti}(x_t)) (expert rows are
+    # stored in bf16); each term carries the FFN tolerance, y its own rounding
     toks = np.unique(np.concatenate([[0, wl.T - 1], g.integers(0, wl.T, 6)]))
     y_ref = np.zeros((len(toks), wl.H))
+    bound = np.zeros((len(toks), wl.H))
     for j, t in enumerate(toks):
-        f64, _ = oracle.expert_swiglu_rows(np.repeat(x[t:t + 1], wl.k, 0), idx_o[t], gu, dn)
-        y_ref[j] = (w_o[t][:, None] * f64).sum(0)
+        o64, o16 = oracle.expert_swiglu_rows(np.repeat(x[t:t + 1], wl.k, 0), idx_o[t], gu, dn)
+        terms = w_o[t][:, None] * oracle.bf16_to_f64(o16)
+        y_ref[j] = terms.sum(0)
+        bound[j] = (w_o[t][:, None] * (2.0**-7 * np.abs(o64) + 1e-3)).sum(0)
     yg = oracle.bf16_to_f64(host(y[torch.from_numpy(toks).to(DEV)]))
     err = np.abs(yg - y_ref)
-    assert (err <= 2.0**-7 * np.abs(y_ref) + 1e-3).all(), f"max combine err {err.max()}"
+    assert (err <= bound + 2.0**-8 * np.abs(y_ref)).all(), f"max combine err {err.max()}"
