@@ -2,10 +2,10 @@
 """Benchmark of the one-GPU MoE routing path on an MI355X.
 
 One step = the whole path on one batch of synthetic input, inputs already in
-HBM: route (top-k gating) -> dispatch index (counts, offsets, positions) ->
-dispatch copy (permute into the send buffer) -> experts (identity-scaled, or
-the SwiGLU FFN on MFMA for the local-layer workload) -> combine -> skew
-statistics. Every step runs in the library's HIP kernels on torch's current
+HBM: route (top-k gating) -> dispatch index (counts, offsets, positions and the
+skew statistics of S) -> dispatch copy (permute into the send buffer) ->
+experts (identity-scaled, or the SwiGLU FFN on MFMA for the local-layer
+workload) -> combine. Every step runs in the library's HIP kernels on torch's current
 stream; torch only provides memory and the stream.
 
 Prints ONE JSON line. `value` is whole-step tokens/s over K timed steps (wall
@@ -34,10 +34,11 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine", "stats")
-KERNEL_OF = {"route": "route_kernel", "dispatch_index": "count_kernel+place_kernel",
+# The skew statistics of S are produced inside dispatch_index (place kernel).
+STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine")
+KERNEL_OF = {"route": "route_kernel", "dispatch_index": "place_kernel (+count_kernel above 64K picks)",
              "dispatch_copy": "copy_kernel", "expert": "expert_scale_kernel",
-             "combine": "combine_kernel", "stats": "stats_kernel"}
+             "combine": "combine_kernel"}
 
 
 class HipEvents:
@@ -83,11 +84,10 @@ def algorithmic_bytes(wl) -> dict:
     T, H, E, k, b = wl.T, wl.H, wl.E, wl.k, wl.elem_bytes
     out = {
         "route": T * E * 4 + T * k * 8,                          # logits in; idx + w out
-        "dispatch_index": 12 * T * k,                            # idx in; pos + row_token out
+        "dispatch_index": 12 * T * k + 4 * E,                    # idx in; pos, row_token, S out
         "dispatch_copy": T * H * b + T * k * H * b + 4 * T * k,  # x once, k copies, pos
         "expert": 2 * T * k * H * b,                             # rows in, rows out
         "combine": T * k * H * b + 8 * T * k + T * H * b,        # k rows, w + pos in; y out
-        "stats": 4 * E,
     }
     if wl.expert == "swiglu":  # + the expert weights, read once
         out["expert"] += 3 * wl.E * wl.H * wl.I * 2
@@ -193,13 +193,13 @@ def main() -> int:
         "dispatch_index": (L.moe_dispatch_index, (
             shp, P(topk_idx), P(buf["expert_counts"]), P(buf["expert_offsets"]),
             P(buf["rank_counts"]), P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
-            P(buf["row_token"]), P(buf["workspace"]), buf["workspace"].numel(), stream)),
+            P(buf["row_token"]), P(stats_raw), P(buf["workspace"]), buf["workspace"].numel(),
+            stream)),
         "dispatch_copy": (L.moe_dispatch_copy, (shp, P(x), P(buf["pos"]), P(buf["send_buf"]),
                                                 stream)),
         "expert": (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
                                         P(buf["expert_counts"]), P(expert_out), stream)),
         "combine": (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream)),
-        "stats": (L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream)),
     }
     if swiglu:
         calls["expert"] = (L.moe_expert_swiglu, (
@@ -323,7 +323,7 @@ def main() -> int:
         return rep
 
     # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
-    single = [n for n in ("route", "dispatch_copy", "expert", "combine", "stats")
+    single = [n for n in ("route", "dispatch_copy", "expert", "combine")
               if not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
@@ -357,7 +357,7 @@ def main() -> int:
                 + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
         "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
                    "waves": W, "routing": wl.routing, "expert": wl.expert,
-                   "step": "route+dispatch_index+dispatch_copy+expert+combine+stats"},
+                   "step": "route+dispatch_index(+stats)+dispatch_copy+expert+combine"},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
             "tokens_per_s": round(T / (dc_ms * 1e-3), 1),

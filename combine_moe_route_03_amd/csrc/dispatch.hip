@@ -5,21 +5,25 @@
 // products by count + scan + index (MoE systems survey section 4.1) and places
 // same-expert rows contiguously (survey section 1.1, EP flow step 2).
 //
-// Three kernels, all on the caller's stream:
+// Up to three kernels, all on the caller's stream:
 //   count_kernel  one 1024-thread block per chunk of picks: LDS histogram ->
 //                 hist[chunk][E] (LDS integer atomics: order-free, exact).
+//                 Skipped up to kFusedCountPicks picks: each place block then
+//                 counts all picks itself (they are few and L2-resident).
 //   place_kernel  one 1024-thread block per chunk. Each block re-derives what it
 //                 needs from the small hist matrix instead of waiting for a
 //                 separate scan launch: the prefix of earlier chunks and the
 //                 totals (threads laid out as (row slice, expert) so all loads
 //                 are independent), then the bucket-order exclusive scan (one
-//                 bucket per thread). Block 0 publishes counts and offsets.
+//                 bucket per thread). Block 0 publishes counts and offsets
+//                 and, when asked, the skew statistics of S.
 //                 Stable in-chunk ranks come from wave64 ballots (bit-sliced
 //                 match on the expert id, popcount of lower lanes) and an LDS
 //                 prefix across the block's 16 waves; the next batch of ids is
 //                 prefetched while the current one is placed.
 //   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
 //                 k stores.
+#include "block_stats.h"
 #include "device.h"
 #include "launch.h"
 
@@ -54,12 +58,13 @@ __global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ i
   if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = h[tid];
 }
 
+template <bool kFusedCount>
 __global__ __launch_bounds__(kB) void place_kernel(
     const int32_t* __restrict__ idx, int64_t npicks, int64_t chunk, int nb, int k, int E,
     int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ row_token) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_token, moe_stats_t* __restrict__ stats) {
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
@@ -67,6 +72,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
   __shared__ int32_t pall[kB];             // (slice, expert) partial total
   __shared__ int32_t wcnt[kWaves][kMaxE];  // per-wave counts of one 1024-pick batch
   __shared__ int32_t part[kWaves];
+  __shared__ StatsScratch st_scratch;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = blockIdx.x;
@@ -79,6 +85,32 @@ __global__ __launch_bounds__(kB) void place_kernel(
     for (int q = 0; q < kWaves; ++q) wcnt[q][tid] = 0;
   }
 
+  if constexpr (kFusedCount) {
+    // 1. Count every pick (the whole index array is small and L2-resident):
+    //    totals in cnt, picks before this chunk in run.
+    if (tid < E) {
+      run[tid] = 0;
+      cnt[tid] = 0;
+    }
+    __syncthreads();
+    const int64_t pstart = (int64_t)b * chunk;
+    for (int64_t base = 0; base < npicks; base += 8 * kB) {
+      int ev[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t p = base + u * kB + tid;
+        ev[u] = (p < npicks) ? idx[p] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if ((unsigned)ev[u] < (unsigned)E) {
+          atomicAdd(&cnt[ev[u]], 1);
+          if (base + u * kB + tid < pstart) atomicAdd(&run[ev[u]], 1);
+        }
+      }
+    }
+    __syncthreads();
+  } else {
   // 1. Picks of each expert in earlier chunks and in all chunks. Thread
   //    (s, e) = (tid >> elog, tid & (ep-1)) sums rows s, s+nslice, ...
   {
@@ -113,6 +145,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
     cnt[tid] = A;
   }
   __syncthreads();
+  }
 
   // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread j
   //    owns bucket j.
@@ -146,6 +179,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
     }
     for (int w = tid; w <= W; w += kB)
       wave_offsets[w] = (w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total;
+    if (stats != nullptr) block_stats(cnt, E, R, st_scratch, stats);
   }
   if (tid < E) run[tid] += off[tid];
   __syncthreads();
@@ -228,13 +262,17 @@ hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
-                        int32_t* pos, int32_t* row_token, hipStream_t s) {
+                        int32_t* pos, int32_t* row_token, moe_stats_t* stats, hipStream_t s) {
   const int64_t nb = num_chunks(npicks, E);
   // With no picks one block still runs to publish zero counts and offsets.
   const unsigned grid = nb == 0 ? 1u : (unsigned)nb;
-  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, chunk_picks(npicks, E),
-                (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets,
-                rank_counts, rank_offsets, wave_offsets, pos, row_token);
+  if (hist == nullptr)
+    return launch(place_kernel<true>, dim3(grid), dim3(kB), 0, s, idx, npicks,
+                  chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
+                  expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats);
+  return launch(place_kernel<false>, dim3(grid), dim3(kB), 0, s, idx, npicks,
+                chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
+                expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats);
 }
 
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,

@@ -4,6 +4,8 @@
 #pragma once
 
 #include <hip/hip_ext.h>
+
+#include "../../include/moe_route.h"
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -30,6 +32,10 @@ inline int64_t chunk_picks(int64_t npicks, int E) {
   c = (c + kIndexBlock - 1) / kIndexBlock * kIndexBlock;
   return c < kIndexBlock ? kIndexBlock : c;
 }
+
+// Up to this many picks, every place block counts all picks itself (they sit
+// in L2) instead of reading per-chunk histograms from a separate count launch.
+constexpr int64_t kFusedCountPicks = 65536;
 
 inline int64_t num_chunks(int64_t npicks, int E) {
   if (npicks == 0) return 0;
@@ -70,10 +76,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 // hist: [num_chunks][E] int32 workspace.
 hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist, hipStream_t s);
 
+// hist == nullptr: count in the place kernel itself (npicks <= kFusedCountPicks).
+// stats (nullable): skew statistics of S, written by block 0.
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
-                        int32_t* pos, int32_t* row_token, hipStream_t s);
+                        int32_t* pos, int32_t* row_token, moe_stats_t* stats, hipStream_t s);
 
 // Row copies; row_bytes is a multiple of 16.
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
