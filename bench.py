@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 # The skew statistics of S are produced inside dispatch_index (place kernel).
 STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine")
-KERNEL_OF = {"route": "route_kernel", "dispatch_index": "place_kernel (+count_kernel above 64K picks)",
+KERNEL_OF = {"route": "route_kernel", "dispatch_index": "count_kernel+place_kernel",
              "dispatch_copy": "copy_kernel", "expert": "expert_scale_kernel",
              "combine": "combine_kernel"}
 

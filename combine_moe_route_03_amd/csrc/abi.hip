@@ -121,12 +121,9 @@ int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   if (!aligned(stats, 8)) return MOE_ERR_ALIGN;
   const int64_t npicks = int64_t(shape->T) * shape->k;
   hipStream_t s = as_stream(stream);
-  int32_t* hist = nullptr;  // small problems: the place kernel counts by itself
-  if (npicks > moe::kFusedCountPicks) {
-    hist = static_cast<int32_t*>(workspace);
-    st = status_of(moe::launch_count(topk_idx, npicks, shape->E, hist, s));
-    if (st != MOE_OK) return st;
-  }
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  st = status_of(moe::launch_count(topk_idx, npicks, shape->E, hist, s));
+  if (st != MOE_OK) return st;
   return status_of(moe::launch_place(topk_idx, npicks, shape->k, shape->E, shape->R, shape->W,
                                      hist, expert_counts, expert_offsets, rank_counts,
                                      rank_offsets, wave_offsets, pos, row_token, stats, s));

@@ -5,11 +5,9 @@
 // products by count + scan + index (MoE systems survey section 4.1) and places
 // same-expert rows contiguously (survey section 1.1, EP flow step 2).
 //
-// Up to three kernels, all on the caller's stream:
+// Three kernels, all on the caller's stream:
 //   count_kernel  one 1024-thread block per chunk of picks: LDS histogram ->
 //                 hist[chunk][E] (LDS integer atomics: order-free, exact).
-//                 Skipped up to kFusedCountPicks picks: each place block then
-//                 counts all picks itself (they are few and L2-resident).
 //   place_kernel  one 1024-thread block per chunk. Each block re-derives what it
 //                 needs from the small hist matrix instead of waiting for a
 //                 separate scan launch: the prefix of earlier chunks and the
@@ -58,7 +56,6 @@ __global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ i
   if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = h[tid];
 }
 
-template <bool kFusedCount>
 __global__ __launch_bounds__(kB) void place_kernel(
     const int32_t* __restrict__ idx, int64_t npicks, int64_t chunk, int nb, int k, int E,
     int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
@@ -79,38 +76,17 @@ __global__ __launch_bounds__(kB) void place_kernel(
   const int L = E / R, LW = L / W;
   const int ep = 1 << elog;        // E rounded up to a power of two
   const int nslice = kB >> elog;   // row slices of the hist matrix
+  // This chunk's first batch of ids, loaded now so that its latency overlaps
+  // the histogram read and the scans below.
+  const int64_t p0 = (int64_t)b * chunk;
+  const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
+  int e_next = (p0 + tid < p1) ? idx[p0 + tid] : -1;
 
   if (tid < E) {
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) wcnt[q][tid] = 0;
   }
 
-  if constexpr (kFusedCount) {
-    // 1. Count every pick (the whole index array is small and L2-resident):
-    //    totals in cnt, picks before this chunk in run.
-    if (tid < E) {
-      run[tid] = 0;
-      cnt[tid] = 0;
-    }
-    __syncthreads();
-    const int64_t pstart = (int64_t)b * chunk;
-    for (int64_t base = 0; base < npicks; base += 8 * kB) {
-      int ev[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t p = base + u * kB + tid;
-        ev[u] = (p < npicks) ? idx[p] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if ((unsigned)ev[u] < (unsigned)E) {
-          atomicAdd(&cnt[ev[u]], 1);
-          if (base + u * kB + tid < pstart) atomicAdd(&run[ev[u]], 1);
-        }
-      }
-    }
-    __syncthreads();
-  } else {
   // 1. Picks of each expert in earlier chunks and in all chunks. Thread
   //    (s, e) = (tid >> elog, tid & (ep-1)) sums rows s, s+nslice, ...
   {
@@ -145,7 +121,6 @@ __global__ __launch_bounds__(kB) void place_kernel(
     cnt[tid] = A;
   }
   __syncthreads();
-  }
 
   // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread j
   //    owns bucket j.
@@ -186,9 +161,6 @@ __global__ __launch_bounds__(kB) void place_kernel(
 
   // 3. Stable ranks inside the chunk, 1024 picks per batch.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-  const int64_t p0 = (int64_t)b * chunk;
-  const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
-  int e_next = (p0 + tid < p1) ? idx[p0 + tid] : -1;
   for (int64_t base = p0; base < p1; base += kB) {
     const int64_t p = base + tid;
     const int e = e_next;
@@ -266,11 +238,7 @@ hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R,
   const int64_t nb = num_chunks(npicks, E);
   // With no picks one block still runs to publish zero counts and offsets.
   const unsigned grid = nb == 0 ? 1u : (unsigned)nb;
-  if (hist == nullptr)
-    return launch(place_kernel<true>, dim3(grid), dim3(kB), 0, s, idx, npicks,
-                  chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
-                  expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats);
-  return launch(place_kernel<false>, dim3(grid), dim3(kB), 0, s, idx, npicks,
+  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks,
                 chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
                 expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats);
 }

@@ -33,10 +33,6 @@ inline int64_t chunk_picks(int64_t npicks, int E) {
   return c < kIndexBlock ? kIndexBlock : c;
 }
 
-// Up to this many picks, every place block counts all picks itself (they sit
-// in L2) instead of reading per-chunk histograms from a separate count launch.
-constexpr int64_t kFusedCountPicks = 65536;
-
 inline int64_t num_chunks(int64_t npicks, int E) {
   if (npicks == 0) return 0;
   const int64_t c = chunk_picks(npicks, E);
@@ -76,7 +72,6 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 // hist: [num_chunks][E] int32 workspace.
 hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist, hipStream_t s);
 
-// hist == nullptr: count in the place kernel itself (npicks <= kFusedCountPicks).
 // stats (nullable): skew statistics of S, written by block 0.
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
