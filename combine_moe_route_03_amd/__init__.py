@@ -58,7 +58,8 @@ SIGNATURES = {
                           ctypes.c_int),
     "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
-    "moe_set_timing_events": ([_vp, _vp], ctypes.c_int),
+    "moe_set_timing_events": ([_vp, _vp, _i32], ctypes.c_int),
+    "moe_timed_launches": ([], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 

@@ -73,13 +73,20 @@ LaunchTiming& launch_timing() {
 
 extern "C" {
 
-int moe_set_timing_events(void* start_event, void* stop_event) {
+int moe_set_timing_events(void* const* start_events, void* const* stop_events, int32_t n) {
   moe::LaunchTiming& t = moe::launch_timing();
-  t.start = reinterpret_cast<hipEvent_t>(start_event);
-  t.stop = reinterpret_cast<hipEvent_t>(stop_event);
-  t.started = false;
+  if (n < 0 || n > moe::kMaxTimedLaunches) return MOE_ERR_ARG;
+  if (n > 0 && (!start_events || !stop_events)) return MOE_ERR_ARG;
+  for (int i = 0; i < n; ++i) {
+    t.start[i] = reinterpret_cast<hipEvent_t>(start_events[i]);
+    t.stop[i] = reinterpret_cast<hipEvent_t>(stop_events[i]);
+  }
+  t.n = n;
+  t.launched = 0;
   return MOE_OK;
 }
+
+int moe_timed_launches(void) { return moe::launch_timing().launched; }
 
 const char* moe_status_string(int status) {
   switch (status) {

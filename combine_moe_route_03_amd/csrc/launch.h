@@ -41,13 +41,14 @@ inline int64_t num_chunks(int64_t npicks, int E) {
 
 // ------------------------------------------------------------ kernel timing
 // Optional per-thread timing events (benchmark hook; see
-// moe_set_timing_events): the first kernel launched while they are set records
-// `start` when it begins, every launch records `stop` when it ends, so the pair
-// brackets the execution of all of them. Null events: plain launches.
+// moe_set_timing_events): while armed, the i-th kernel launched (i < n) records
+// start[i] when it begins executing and stop[i] when it ends.
+constexpr int kMaxTimedLaunches = 8;
 struct LaunchTiming {
-  hipEvent_t start = nullptr;
-  hipEvent_t stop = nullptr;
-  bool started = false;
+  hipEvent_t start[kMaxTimedLaunches] = {};
+  hipEvent_t stop[kMaxTimedLaunches] = {};
+  int n = 0;         // armed pairs
+  int launched = 0;  // kernels launched since arming
 };
 LaunchTiming& launch_timing();
 
@@ -55,13 +56,14 @@ template <typename... Params, typename... Args>
 hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem,
                   hipStream_t s, Args... args) {
   LaunchTiming& tm = launch_timing();
-  if (tm.start != nullptr || tm.stop != nullptr) {
-    hipEvent_t first = tm.started ? nullptr : tm.start;
-    tm.started = true;
-    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, first, tm.stop, 0u,
-                          static_cast<Params>(args)...);
-  } else
+  if (tm.n > 0) {
+    const int i = tm.launched++;
+    hipEvent_t a = i < tm.n ? tm.start[i] : nullptr;
+    hipEvent_t b = i < tm.n ? tm.stop[i] : nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, a, b, 0u, static_cast<Params>(args)...);
+  } else {
     kernel<<<grid, block, shmem, s>>>(static_cast<Params>(args)...);
+  }
   return hipGetLastError();
 }
 

@@ -197,16 +197,20 @@ int moe_combine(const moe_shape* shape, const void* expert_out,
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
               moe_stats_t* out, moe_stream_t stream);
 
-/* Kernel timing hook for benchmarks (not a step of the path). While set, the
- * kernels this library launches from the calling thread use AMD's extended
- * launch: the first one records `start_event` when it begins executing and
- * every one records `stop_event` when it ends, so hipEventElapsedTime(start,
- * stop) is the GPU time from the first kernel's start to the last one's end
- * (one kernel's execution time for the single-kernel entry points). Calling
- * this again re-arms `start`. Events are created by the caller (hipEventCreate)
- * and passed as void* hipEvent_t handles. The setting is thread-local; NULL,
- * NULL turns it off. Returns MOE_OK. */
-int moe_set_timing_events(void* start_event, void* stop_event);
+/* Kernel timing hook for benchmarks (not a step of the path). After
+ * moe_set_timing_events(starts, stops, n), the kernels this library launches
+ * from the calling thread use AMD's extended launch: the i-th one (i < n, at
+ * most 8) records starts[i] when it begins executing and stops[i] when it
+ * ends, so hipEventElapsedTime(starts[i], stops[i]) is that kernel's execution
+ * time. Later launches are not timed. Events are created by the caller
+ * (hipEventCreate) and passed as void* hipEvent_t handles. Thread-local;
+ * n = 0 turns it off. Errors: MOE_ERR_ARG (n outside [0, 8], NULL arrays). */
+int moe_set_timing_events(void* const* start_events, void* const* stop_events,
+                          int32_t n);
+
+/* Number of kernels launched from the calling thread since the last
+ * moe_set_timing_events call (counted only while n > 0). */
+int moe_timed_launches(void);
 
 /* Human-readable name of a moe_status value (static string, never NULL). */
 const char* moe_status_string(int status);

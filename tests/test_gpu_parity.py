@@ -318,11 +318,14 @@ def test_timing_events_hook():
     wl = PARITY["zipf"]
     logits = dev(synth.logits(wl))
     ref_idx, ref_w = moe.route(logits, wl.k)
-    assert moe.lib().moe_set_timing_events(a, b) == 0
+    arr = ctypes.c_void_p * 1
+    assert moe.lib().moe_set_timing_events(arr(a), arr(b), 1) == 0
     try:
         idx, w = moe.route(logits, wl.k)
+        assert moe.lib().moe_timed_launches() == 1
     finally:
-        moe.lib().moe_set_timing_events(None, None)
+        moe.lib().moe_set_timing_events(None, None, 0)
+    assert moe.lib().moe_set_timing_events(None, None, 9) == -1
     torch.cuda.synchronize()
     ms = ctypes.c_float()
     assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
