@@ -2,10 +2,10 @@
 """Benchmark of the one-GPU MoE routing path on an MI355X.
 
 One step = the whole path on one batch of synthetic input, inputs already in
-HBM: route (top-k gating) -> dispatch index (counts, offsets, positions and the
-skew statistics of S) -> dispatch copy (permute into the send buffer) ->
-experts (identity-scaled, or the SwiGLU FFN on MFMA for the local-layer
-workload) -> combine. Every step runs in the library's HIP kernels on torch's current
+HBM: route (top-k gating) -> dispatch index (counts, offsets, positions) ->
+dispatch copy (permute into the send buffer) -> experts (identity-scaled, or
+the SwiGLU FFN on MFMA for the local-layer workload) -> combine -> skew
+statistics of S. Every step runs in the library's HIP kernels on torch's current
 stream; torch only provides memory and the stream.
 
 Prints ONE JSON line. `value` is whole-step tokens/s over K timed steps (wall
@@ -34,11 +34,10 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-# The skew statistics of S are produced inside dispatch_index (place kernel).
-STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine")
+STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine", "stats")
 KERNEL_OF = {"route": "route_kernel", "dispatch_index": "count_kernel+place_kernel",
              "dispatch_copy": "copy_kernel", "expert": "expert_scale_kernel",
-             "combine": "combine_kernel"}
+             "combine": "combine_kernel", "stats": "stats_kernel"}
 
 
 class HipEvents:
@@ -85,6 +84,7 @@ def algorithmic_bytes(wl) -> dict:
     out = {
         "route": T * E * 4 + T * k * 8,                          # logits in; idx + w out
         "dispatch_index": 12 * T * k + 4 * E,                    # idx in; pos, row_token, S out
+        "stats": 4 * E,                                          # S in
         "dispatch_copy": T * H * b + T * k * H * b + 4 * T * k,  # x once, k copies, pos
         "expert": 2 * T * k * H * b,                             # rows in, rows out
         "combine": T * k * H * b + 8 * T * k + T * H * b,        # k rows, w + pos in; y out
@@ -193,14 +193,15 @@ def main() -> int:
         "dispatch_index": (L.moe_dispatch_index, (
             shp, P(topk_idx), P(buf["expert_counts"]), P(buf["expert_offsets"]),
             P(buf["rank_counts"]), P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
-            P(buf["row_token"]), P(stats_raw), P(buf["workspace"]), buf["workspace"].numel(),
-            stream)),
+            P(buf["row_token"]), P(buf["workspace"]), buf["workspace"].numel(), stream)),
         "dispatch_copy": (L.moe_dispatch_copy, (shp, P(x), P(buf["pos"]), P(buf["send_buf"]),
                                                 stream)),
         "expert": (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
                                         P(buf["expert_counts"]), P(expert_out), stream)),
         "combine": (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream)),
+        "stats": (L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream)),
     }
+    STAGES_RUN = STAGES
     if swiglu:
         calls["expert"] = (L.moe_expert_swiglu, (
             shp, wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
@@ -217,7 +218,7 @@ def main() -> int:
 
     def step(evs=None):
         """One pass of the path; evs[name] = (starts, stops) event arrays for the hook."""
-        for name in STAGES:
+        for name in STAGES_RUN:
             fn, a = calls[name]
             if evs is not None:
                 set_events(evs[name][0], evs[name][1], NPAIR)
@@ -231,12 +232,12 @@ def main() -> int:
     def new_events(n):
         def arr():
             return (ctypes.c_void_p * NPAIR)(*[hipev.create() for _ in range(NPAIR)])
-        return [{nm: (arr(), arr()) for nm in STAGES} for _ in range(n)]
+        return [{nm: (arr(), arr()) for nm in STAGES_RUN} for _ in range(n)]
 
     def stage_means(evs):
         """Per stage: summed execution time of its kernels, averaged over steps."""
         out = {}
-        for nm in STAGES:
+        for nm in STAGES_RUN:
             n = launched[nm]
             out[nm] = float(np.mean([sum(hipev.ms(e[nm][0][j], e[nm][1][j]) for j in range(n))
                                      for e in evs]))
@@ -322,9 +323,10 @@ def main() -> int:
     def gbs(name, ms):
         return nbytes[name] / (ms * 1e-3) / 1e9
 
+
     def stage_report(ms):
         rep = {}
-        for n in STAGES:
+        for n in STAGES_RUN:
             rep[n] = {"us": round(ms[n] * 1e3, 2), "GB/s": round(gbs(n, ms[n]), 1),
                       "frac_hbm_peak": round(gbs(n, ms[n]) / HBM_PEAK_GBS, 4),
                       "kernels": kernel_of[n]}
@@ -335,7 +337,7 @@ def main() -> int:
         return rep
 
     # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
-    single = [n for n in ("route", "dispatch_copy", "expert", "combine")
+    single = [n for n in ("route", "dispatch_copy", "expert", "combine", "stats")
               if not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
@@ -369,7 +371,7 @@ def main() -> int:
                 + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
         "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
                    "waves": W, "routing": wl.routing, "expert": wl.expert,
-                   "step": "route+dispatch_index(+stats)+dispatch_copy+expert+combine"},
+                   "step": "route+dispatch_index+dispatch_copy+expert+combine+stats"},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
             "tokens_per_s": round(T / (dc_ms * 1e-3), 1),

@@ -47,10 +47,10 @@ _shp = ctypes.POINTER(MoeShape)
 SIGNATURES = {
     "moe_route": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe_dispatch_workspace_bytes": ([_shp], ctypes.c_size_t),
-    "moe_dispatch_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                            ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_dispatch_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                            _vp], ctypes.c_int),
     "moe_dispatch_copy": ([_shp, _vp, _vp, _vp, _vp], ctypes.c_int),
-    "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_swiglu_workspace_bytes": ([_shp, _i32], ctypes.c_size_t),
@@ -164,17 +164,16 @@ def alloc_dispatch(shape: Shape, device) -> dict:
         rank_counts=_empty((W * R,), i32, device), rank_offsets=_empty((W * R,), i32, device),
         wave_offsets=_empty((W + 1,), i32, device), pos=_empty((T, k), i32, device),
         row_token=_empty((T * k,), i32, device),
-        stats=_empty((STATS_BYTES,), torch.uint8, device),
         workspace=_empty((max(dispatch_workspace_bytes(shape), 1),), torch.uint8, device))
 
 
 def dispatch_index(topk_idx: torch.Tensor, shape: Shape, out: dict):
-    """Counts, offsets, positions (and S's statistics into out["stats"] when present)."""
+    """Counts, offsets and positions into the buffers of `out` (see alloc_dispatch)."""
     sh = shape.c()
     _check(lib().moe_dispatch_index(
         ctypes.byref(sh), _ptr(topk_idx), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
         _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]),
-        _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(out.get("stats")), _ptr(out["workspace"]),
+        _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(out["workspace"]),
         out["workspace"].numel(), _stream()), "moe_dispatch_index")
     return out
 
@@ -188,8 +187,7 @@ def dispatch_copy(x: torch.Tensor, pos: torch.Tensor, shape: Shape, send_buf: to
 
 def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
              out: dict | None = None) -> dict:
-    """Counts, offsets, positions, S's statistics (out["stats"], raw moe_stats_t) and the
-    permuted send buffer, in one call."""
+    """Counts, offsets, positions and the permuted send buffer (one call)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     shape = Shape(T, H, E, k, R, W, x.dtype)
@@ -199,8 +197,8 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
         ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]),
         _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
         _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]), _ptr(out["pos"]),
-        _ptr(out["row_token"]), _ptr(out.get("stats")), _ptr(out["workspace"]),
-        out["workspace"].numel(), _stream()), "moe_dispatch")
+        _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
+        "moe_dispatch")
     return out
 
 

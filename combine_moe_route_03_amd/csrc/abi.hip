@@ -116,16 +116,14 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* shape) {
 
 int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_counts,
                        int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
-                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
-                       moe_stats_t* stats, void* workspace, size_t workspace_bytes_given,
-                       moe_stream_t stream) {
+                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token, void* workspace,
+                       size_t workspace_bytes_given, moe_stream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
                         rank_offsets, wave_offsets, pos, row_token, workspace,
                         workspace_bytes_given);
   if (st != MOE_OK) return st;
-  if (!aligned(stats, 8)) return MOE_ERR_ALIGN;
   const int64_t npicks = int64_t(shape->T) * shape->k;
   hipStream_t s = as_stream(stream);
   int32_t* hist = static_cast<int32_t*>(workspace);
@@ -133,7 +131,7 @@ int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   if (st != MOE_OK) return st;
   return status_of(moe::launch_place(topk_idx, npicks, shape->k, shape->E, shape->R, shape->W,
                                      hist, expert_counts, expert_offsets, rank_counts,
-                                     rank_offsets, wave_offsets, pos, row_token, stats, s));
+                                     rank_offsets, wave_offsets, pos, row_token, s));
 }
 
 int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos, void* send_buf,
@@ -150,8 +148,7 @@ int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos,
 int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx, void* send_buf,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* rank_counts,
                  int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
-                 moe_stats_t* stats, void* workspace, size_t workspace_bytes_given,
-                 moe_stream_t stream) {
+                 void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
@@ -160,9 +157,8 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
   if (st != MOE_OK) return st;
   st = check_copy_args(shape, x, pos, send_buf);
   if (st != MOE_OK) return st;
-  if (!aligned(stats, 8)) return MOE_ERR_ALIGN;
   st = moe_dispatch_index(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
-                          rank_offsets, wave_offsets, pos, row_token, stats, workspace,
+                          rank_offsets, wave_offsets, pos, row_token, workspace,
                           workspace_bytes_given, stream);
   if (st != MOE_OK) return st;
   return moe_dispatch_copy(shape, x, pos, send_buf, stream);

@@ -13,15 +13,13 @@
 //                 separate scan launch: the prefix of earlier chunks and the
 //                 totals (threads laid out as (row slice, expert) so all loads
 //                 are independent), then the bucket-order exclusive scan (one
-//                 bucket per thread). Block 0 publishes counts and offsets
-//                 and, when asked, the skew statistics of S.
+//                 bucket per thread). Block 0 publishes counts and offsets.
 //                 Stable in-chunk ranks come from wave64 ballots (bit-sliced
 //                 match on the expert id, popcount of lower lanes) and an LDS
 //                 prefix across the block's 16 waves; the next batch of ids is
 //                 prefetched while the current one is placed.
 //   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
 //                 k stores.
-#include "block_stats.h"
 #include "device.h"
 #include "launch.h"
 
@@ -61,7 +59,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
     int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ row_token, moe_stats_t* __restrict__ stats) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_token) {
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
@@ -69,7 +67,6 @@ __global__ __launch_bounds__(kB) void place_kernel(
   __shared__ int32_t pall[kB];             // (slice, expert) partial total
   __shared__ int32_t wcnt[kWaves][kMaxE];  // per-wave counts of one 1024-pick batch
   __shared__ int32_t part[kWaves];
-  __shared__ StatsScratch st_scratch;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = blockIdx.x;
@@ -154,7 +151,6 @@ __global__ __launch_bounds__(kB) void place_kernel(
     }
     for (int w = tid; w <= W; w += kB)
       wave_offsets[w] = (w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total;
-    if (stats != nullptr) block_stats(cnt, E, R, st_scratch, stats);
   }
   if (tid < E) run[tid] += off[tid];
   __syncthreads();
@@ -234,13 +230,13 @@ hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
-                        int32_t* pos, int32_t* row_token, moe_stats_t* stats, hipStream_t s) {
+                        int32_t* pos, int32_t* row_token, hipStream_t s) {
   const int64_t nb = num_chunks(npicks, E);
   // With no picks one block still runs to publish zero counts and offsets.
   const unsigned grid = nb == 0 ? 1u : (unsigned)nb;
   return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks,
                 chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
-                expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats);
+                expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token);
 }
 
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,

@@ -74,11 +74,10 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, 
 // hist: [num_chunks][E] int32 workspace.
 hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist, hipStream_t s);
 
-// stats (nullable): skew statistics of S, written by block 0.
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
-                        int32_t* pos, int32_t* row_token, moe_stats_t* stats, hipStream_t s);
+                        int32_t* pos, int32_t* row_token, hipStream_t s);
 
 // Row copies; row_bytes is a multiple of 16.
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,

@@ -113,9 +113,6 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* shape);
  * wave_offsets   [W+1] out: first row of each wave; wave_offsets[W] = rows.
  * pos            [T][k] out: send-buffer row of pick (t, i).
  * row_token      [T*k] out: token of each row (rows >= sum c are untouched).
- * stats          optional (NULL to skip) DEVICE pointer to one moe_stats_t:
- *                S's skew statistics, exactly as moe_stats computes them,
- *                written by the same launch.
  * workspace      device scratch of moe_dispatch_workspace_bytes(shape) bytes
  *                (contents need not be initialised; clobbered by the call).
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
@@ -124,7 +121,7 @@ int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx,
                        int32_t* expert_counts, int32_t* expert_offsets,
                        int32_t* rank_counts, int32_t* rank_offsets,
                        int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
-                       moe_stats_t* stats, void* workspace, size_t workspace_bytes,
+                       void* workspace, size_t workspace_bytes,
                        moe_stream_t stream);
 
 /* The permute copy (explainer section 3 item 5: rows are reordered by
@@ -140,8 +137,8 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                  void* send_buf, int32_t* expert_counts,
                  int32_t* expert_offsets, int32_t* rank_counts,
                  int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
-                 int32_t* row_token, moe_stats_t* stats, void* workspace,
-                 size_t workspace_bytes, moe_stream_t stream);
+                 int32_t* row_token, void* workspace, size_t workspace_bytes,
+                 moe_stream_t stream);
 
 /* Identity-scaled experts (the experts of the synthetic workloads):
  * expert_out[n][:] = round_dtype((e(n) + 1) * send_buf[n][:]) for every row n

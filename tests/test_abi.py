@@ -70,15 +70,12 @@ def test_workspace_size_and_errors():
     ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
     assert ws >= 256 * 4 and ws % 256 == 0
     args = [FAKE] * 8
-    st = L.moe_dispatch_index(ctypes.byref(sh), *args, None, FAKE, ws - 1, None)
+    st = L.moe_dispatch_index(ctypes.byref(sh), *args, FAKE, ws - 1, None)
     assert st == WORKSPACE
-    st = L.moe_dispatch_index(ctypes.byref(sh), FAKE, None, *args[2:], None, FAKE, ws, None)
+    st = L.moe_dispatch_index(ctypes.byref(sh), FAKE, None, *args[2:], FAKE, ws, None)
     assert st == ARG
-    st = L.moe_dispatch_index(ctypes.byref(sh), ctypes.c_void_p((1 << 20) + 2), *args[1:], None,
-                              FAKE, ws, None)
-    assert st == ALIGN
-    st = L.moe_dispatch_index(ctypes.byref(sh), *args, ctypes.c_void_p((1 << 20) + 4), FAKE, ws,
-                              None)
+    st = L.moe_dispatch_index(ctypes.byref(sh), ctypes.c_void_p((1 << 20) + 2), *args[1:], FAKE,
+                              ws, None)
     assert st == ALIGN
 
 
@@ -89,7 +86,7 @@ def test_copy_and_combine_alignment():
     assert L.moe_dispatch_copy(ctypes.byref(sh), odd, FAKE, FAKE, None) == ALIGN
     assert L.moe_combine(ctypes.byref(sh), FAKE, FAKE, FAKE, odd, None) == ALIGN
     assert L.moe_expert_scale(ctypes.byref(sh), FAKE, None, FAKE, FAKE, None) == ARG
-    assert L.moe_dispatch(None, *[FAKE] * 12, 1 << 20, None) == ARG
+    assert L.moe_dispatch(None, *[FAKE] * 11, 1 << 20, None) == ARG
 
 
 def test_route_validation():

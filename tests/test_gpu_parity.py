@@ -81,8 +81,6 @@ def run_path(wl, logits, x):
     y = moe.combine(eo, w, out["pos"], shape)
     st = moe.stats(out["expert_counts"], wl.R)
     torch.cuda.synchronize()
-    # the statistics fused into dispatch equal the standalone kernel's
-    assert moe.stats_to_dict(out["stats"]) == st
     return idx, w, out, eo, y, st
 
 
