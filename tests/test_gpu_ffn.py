@@ -67,14 +67,15 @@ def test_swiglu_small_full(T, E, H, I, k, seed):
     _check_rows(host(eo_gpu), o64, atol=2e-3)
 
 
-def test_swiglu_empty_and_ragged_experts():
-    # experts with 0, 1 and 129 rows (m-tile tails), routed by hand
-    E, H, I, k = 4, 128, 64, 1
-    T = 131
+@pytest.mark.parametrize("H,I", [(128, 64), (256, 128)])  # 128- and 256-row tile paths
+def test_swiglu_empty_and_ragged_experts(H, I):
+    # experts with 0, 1 and 257 rows (m-tile tails of both tile sizes), routed by hand
+    E, k = 4, 1
+    T = 259
     idx = np.zeros((T, k), np.int32)
-    idx[:129, 0] = 2
-    idx[129, 0] = 0
-    idx[130, 0] = 3
+    idx[:257, 0] = 2
+    idx[257, 0] = 0
+    idx[258, 0] = 3
     wl = synth.Workload("ffn", T=T, H=H, dtype="bf16", E=E, k=k, R=1, W=1, routing="iid",
                         expert="swiglu", I=I, seed=4)
     x = synth.hidden(wl)
