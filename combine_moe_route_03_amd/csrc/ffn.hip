@@ -16,16 +16,16 @@
 //   small: 128 x 128 x 64, each wave 64 x 64 (2 x 2 tiles); any I % 64 == 0 and
 //          H % 128 == 0.
 // LDS holds each K step's A and B tiles double-buffered; a tile row is 64 bf16
-// = eight 16-byte chunks and chunk c of row r sits at chunk c ^ (r & 7), so the
-// eight lanes that read one fragment column in the same cycle hit distinct
+// = eight 16-byte chunks and chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
+// so the 16 lanes that read one fragment column in the same cycle hit distinct
 // banks. One barrier per K step; the next step's global loads are in flight
 // during the MFMAs. A gate/up tile takes BN/2 gate rows of w_gate_up and the
 // matching BN/2 up rows, so g and u of the same (row, j) land in the same lane
 // and register and SiLU(g) * u is applied in the epilogue. Blocks map to
-// (expert, m-tile, n-tile) with the n-tile outermost and a wave-level scan over
-// the per-expert row counts; logical block ids are remapped so that consecutive
-// ones run on the same XCD (workgroups are dealt to the 8 XCDs round-robin),
-// keeping the weight tile they share in that XCD's L2.
+// (expert, m-tile, n-tile) by a wave-level scan over the per-expert row
+// counts. Workgroups are dealt to the 8 XCDs round-robin;
+// each XCD takes one contiguous share of the m-major tile order, so it reads
+// its rows once and the weights of the experts they belong to through its L2.
 #include "device.h"
 #include "launch.h"
 
@@ -42,7 +42,11 @@ constexpr int kXCD = 8;
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
 // Element offset of 16-byte chunk c of tile row r (XOR swizzle, no padding).
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 3); }
+// A 64-bf16 row is 128 bytes = half of the 64 x 4-byte banks; a fragment read
+// (ds_read_b128) services 16 lanes = 16 consecutive rows at once, so rows r and
+// r+1 share the chunk permutation and land in opposite bank halves, while
+// (r >> 1) & 7 gives the 8 row pairs 8 distinct chunk slots.
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
 // BM x BN block tile; each of the 2 x 2 waves computes (BM/2) x (BN/2) as
 // MI x NI tiles of 32 x 32.
@@ -50,21 +54,24 @@ template <bool kGateUp, int BM, int BN>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, const uint16_t* __restrict__ Bw, int64_t bstride,
-    int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int mt_bound) {
+    int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles) {
   constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
   constexpr int AL = BM * 8 / kThreads;      // 16-byte A chunks per thread per K step
   constexpr int BL = BN * 8 / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kBK];
-  __shared__ int info[3];  // expert, first row, rows in tile
+  __shared__ int info[4];  // expert, first row, rows in tile, n-tile
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int wm = wid >> 1, wn = wid & 1;
 
-  // ---- which tile: logical id, XCD-contiguous
-  const int G = gridDim.x;  // a multiple of kXCD
-  const int logical = (blockIdx.x % kXCD) * (G / kXCD) + blockIdx.x / kXCD;
-  const int ntile = logical / mt_bound, mtg = logical - ntile * mt_bound;
+  // ---- which tile. Tiles are numbered m-major (all n-tiles of m-tile 0, then
+  // of m-tile 1, ...) and each XCD takes one contiguous share of that order, so
+  // an XCD reads its share of the rows once and the weights of the few experts
+  // those rows belong to; blocks of one XCD share tiles through its L2.
+  // gridDim.x is a multiple of kXCD with at least ceil(tiles / kXCD) slots per XCD.
+  const int xcd = blockIdx.x % kXCD, slot = blockIdx.x / kXCD;
+  int ntile = 0;
   if (wid == 0) {
     if (lane == 0) info[0] = -1;  // no tile, unless a lane below finds one
     // Expert e owns m-tiles [base_e, base_e + ceil(cnt[e] / BM)); lane l scans
@@ -78,8 +85,14 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
       const int y = __shfl_up(incl, o);
       if (lane >= o) incl += y;
     }
+    const int total = __shfl(incl, kWave - 1) * ntiles;  // tiles that exist
+    const int share = (total + kXCD - 1) / kXCD;         // <= slots per XCD
+    const int logical = xcd * share + slot;
+    const bool live = slot < share && logical < total;
+    const int mtg = live ? logical / ntiles : -1;
+    ntile = live ? logical - mtg * ntiles : 0;
     int base = incl - mine;
-    if (ntile < ntiles && mtg >= base && mtg < incl) {
+    if (live && mtg >= base && mtg < incl) {
       for (int e = e0; e < e1; ++e) {
         const int mt = (cnts[e] + BM - 1) / BM;
         if (mtg < base + mt) {
@@ -88,6 +101,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
           info[0] = e;
           info[1] = offs[e] + m0;
           info[2] = rows < BM ? rows : BM;
+          info[3] = ntile;
           break;
         }
         base += mt;
@@ -98,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
   const int e = info[0];
   if (e < 0) return;  // uniform over the block
   const int row0 = info[1], rows = info[2];
+  ntile = info[3];
 
   const uint16_t* Bexp = Bw + (int64_t)e * bstride;
   // Global -> LDS: 16-byte chunk q = tid + 256*i is tile row (tid >> 3) + 32*i,
@@ -213,13 +228,13 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, const in
   hipError_t err = launch(ffn_gemm_kernel<true, BM, BN>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E,
                           static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
-                          static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, mtb);
+                          static_cast<uint16_t*>(hbuf), (int64_t)I, nt1);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
   return launch(ffn_gemm_kernel<false, BM, BN>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E,
                 static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
-                static_cast<uint16_t*>(out), (int64_t)H, nt2, mtb);
+                static_cast<uint16_t*>(out), (int64_t)H, nt2);
 }
 
 }  // namespace
