@@ -194,6 +194,10 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
   if (shape->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (I < 64 || I % 64 != 0 || shape->H % 128 != 0) return MOE_ERR_ARG;
   if (int64_t(shape->E) * 2 * I * shape->H >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+  // the kernels address one expert's weights and one 256-row tile through
+  // buffer descriptors with a 31-bit byte range
+  if (int64_t(4) * I * shape->H >= (int64_t(1) << 31) || int64_t(512) * shape->H >= (int64_t(1) << 31))
+    return MOE_ERR_ARG;
   if (!expert_offsets || !expert_counts || !w_gate_up || !w_down || !workspace) return MOE_ERR_ARG;
   if (shape->T > 0 && (!send_buf || !expert_out)) return MOE_ERR_ARG;
   if (!aligned(send_buf, 16) || !aligned(expert_out, 16) || !aligned(w_gate_up, 16) ||

@@ -15,17 +15,21 @@
 //          and H % 256 == 0.
 //   small: 128 x 128 x 64, each wave 64 x 64 (2 x 2 tiles); any I % 64 == 0 and
 //          H % 128 == 0.
-// LDS holds each K step's A and B tiles double-buffered; a tile row is 64 bf16
-// = eight 16-byte chunks and chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
-// so the 16 lanes that read one fragment column in the same cycle hit distinct
-// banks. One barrier per K step; the next step's global loads are in flight
-// during the MFMAs. A gate/up tile takes BN/2 gate rows of w_gate_up and the
-// matching BN/2 up rows, so g and u of the same (row, j) land in the same lane
-// and register and SiLU(g) * u is applied in the epilogue. Blocks map to
-// (expert, m-tile, n-tile) by a wave-level scan over the per-expert row
-// counts. Workgroups are dealt to the 8 XCDs round-robin;
-// each XCD takes one contiguous share of the m-major tile order, so it reads
-// its rows once and the weights of the experts they belong to through its L2.
+// Global -> LDS moves go through buffer loads with the LDS bit (16 bytes a
+// lane straight into LDS, no registers, hardware range check for partial
+// m-tiles). LDS holds two K steps of A and B; a tile row is 64 bf16 = eight
+// 16-byte chunks and chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so the
+// 16 lanes that read one fragment column in the same cycle hit distinct banks.
+// Software pipeline: the loads of step kt+2 are issued right after the one
+// barrier of step kt and land while steps kt and kt+1 compute; fragment reads
+// are double-buffered in registers and interleaved one per MFMA. A gate/up
+// tile takes BN/2 gate rows of w_gate_up and the matching BN/2 up rows, so g
+// and u of the same (row, j) land in the same lane and register and
+// SiLU(g) * u is applied in the epilogue. Blocks map to (expert, m-tile,
+// n-tile) by a wave-level scan over the per-expert row counts. Workgroups are
+// dealt to the 8 XCDs round-robin; each XCD takes one contiguous share of the
+// m-major tile order, so it reads its rows once and the weights of the experts
+// they belong to through its L2.
 #include "device.h"
 #include "launch.h"
 
@@ -35,31 +39,57 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kXCD = 8;
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
-// Element offset of 16-byte chunk c of tile row r (XOR swizzle, no padding).
-// A 64-bf16 row is 128 bytes = half of the 64 x 4-byte banks; a fragment read
-// (ds_read_b128) services 16 lanes = 16 consecutive rows at once, so rows r and
-// r+1 share the chunk permutation and land in opposite bank halves, while
-// (r >> 1) & 7 gives the 8 row pairs 8 distinct chunk slots.
+// K step: 64 bf16 = 128 bytes of every tile row, eight 16-byte chunks.
+constexpr int kBK = 64;
+
+// Element offset of 16-byte chunk c of tile row r in an LDS tile (XOR swizzle,
+// no padding). The 64 four-byte banks span 256 bytes = two tile rows; a
+// fragment read (ds_read_b128) services 16 lanes = 16 consecutive rows at
+// once. Rows r and r + 1 fall in opposite bank halves, and the key
+// (r >> 1) & 7 gives the 8 row pairs distinct chunk slots, so the 16 lanes hit
+// 64 distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format,
+// no swizzle, no index stride).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// s_waitcnt with vmcnt = 0 and the other counters left free (gfx9 encoding:
+// vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Buffer-instruction helpers (plain device functions, so that the kernel's
+// lambdas stay valid in the host compilation pass).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// 16 bytes a lane from base + voff + soff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds, 16, voff, soff, 0, 0);
+}
 
 // BM x BN block tile; each of the 2 x 2 waves computes (BM/2) x (BN/2) as
 // MI x NI tiles of 32 x 32.
-template <bool kGateUp, int BM, int BN>
-__global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
+template <bool kGateUp, int BM, int BN, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, const uint16_t* __restrict__ Bw, int64_t bstride,
     int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles) {
   constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
-  constexpr int AL = BM * 8 / kThreads;      // 16-byte A chunks per thread per K step
-  constexpr int BL = BN * 8 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kBK];
+  constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave per K step
+  constexpr int kStage = (BM + BN) * kBK;    // elements of one A + B stage
+  // Two stages as two arrays, so the compiler can tell the loads into one stage
+  // from the fragment reads of the other and need not wait for them.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds1[kStage];
   __shared__ int info[4];  // expert, first row, rows in tile, n-tile
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -114,39 +144,49 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
   const int row0 = info[1], rows = info[2];
   ntile = info[3];
 
+  // ---- global -> LDS without registers (global_load_lds_dwordx4): one wave
+  // instruction fills 64 consecutive 16-byte LDS slots, lane l slot l, i.e.
+  // 8 tile rows. Lane l therefore fetches the global chunk that the swizzle
+  // puts in slot l & 7 of row (l >> 3). Wave w fills A rows [w*BM/4, (w+1)*BM/4)
+  // and B rows [w*BN/4, (w+1)*BN/4). A rows past the tile's last row re-read
+  // that row: MFMA output rows depend on their own A row only, and those rows
+  // are never stored.
   const uint16_t* Bexp = Bw + (int64_t)e * bstride;
-  // Global -> LDS: 16-byte chunk q = tid + 256*i is tile row (tid >> 3) + 32*i,
-  // chunk (tid & 7) of the K step.
-  const int lrow = tid >> 3, lc = tid & 7;
-  v4u ra[AL], rb[BL];
   auto brow = [&](int r) -> int {
     if constexpr (kGateUp)
       return r < BN / 2 ? ntile * (BN / 2) + r : I + ntile * (BN / 2) + (r - BN / 2);
     else
       return ntile * BN + r;
   };
-  auto gload = [&](int k0) {
+  const int lr = lane >> 3, ls = lane & 7;
+  // Buffer descriptors over this tile's A rows and this expert's weights. The
+  // descriptor's range check returns zeros for A rows past the tile's last row
+  // (those MFMA output rows are never stored), so no clamping is needed.
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + (int64_t)row0 * lda, (int64_t)rows * lda * 2);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      make_rsrc(Bexp, (int64_t)(kGateUp ? 2 * I : ntiles * BN) * K * 2);
+  // Per-lane byte offsets of the K = 0 chunks; the K step goes in the scalar offset.
+  uint32_t aoff[AI], boff[BI];
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-      const int r = lrow + 32 * i;
-      ra[i] = (r < rows)
-                  ? *reinterpret_cast<const v4u*>(A + (int64_t)(row0 + r) * lda + k0 + lc * 8)
-                  : v4u{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < AI; ++i) {
+    const int r = wid * (BM / 4) + 8 * i + lr;
+    aoff[i] = (uint32_t)(((int64_t)r * lda + ((ls ^ ((r >> 1) & 7)) << 3)) * 2);
+  }
 #pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const int r = lrow + 32 * i;
-      rb[i] = *reinterpret_cast<const v4u*>(Bexp + (int64_t)brow(r) * K + k0 + lc * 8);
-    }
+  for (int i = 0; i < BI; ++i) {
+    const int r = wid * (BN / 4) + 8 * i + lr;
+    boff[i] = (uint32_t)(((int64_t)brow(r) * K + ((ls ^ ((r >> 1) & 7)) << 3)) * 2);
+  }
+  auto issue = [&](uint16_t* As, int k0) __attribute__((always_inline)) {
+    uint16_t* Bs = As + BM * kBK;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      load_lds16(arsrc, As + (wid * (BM / 4) + 8 * i) * kBK, aoff[i], 2 * k0);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      load_lds16(brsrc, Bs + (wid * (BN / 4) + 8 * i) * kBK, boff[i], 2 * k0);
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AL; ++i)
-      *reinterpret_cast<v4u*>(&As[buf][swz(lrow + 32 * i, lc)]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BL; ++i)
-      *reinterpret_cast<v4u*>(&Bs[buf][swz(lrow + 32 * i, lc)]) = rb[i];
-  };
+
   // B tile row of fragment ni for this wave: gate/up tiles put the wave's gate
   // columns in ni < NI/2 and the matching up columns in ni >= NI/2.
   auto bfrag_row = [&](int ni) -> int {
@@ -162,33 +202,79 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
 
-  const int nk = K / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+  // Fragments of K sub-step kk (16 wide): lane l feeds row l % 32 with chunk
+  // 2*kk + l / 32. Double-buffered in registers: the reads of sub-step kk+1
+  // are in flight during the MFMAs of kk.
+  bf16x8 fa[2][MI], fb[2][NI];
+  auto fload = [&](int f, const uint16_t* As, int kk) __attribute__((always_inline)) {
+    const uint16_t* Bs = As + BM * kBK;
+    const int kc = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int kc = kk * 2 + (lane >> 5);  // 16-byte chunk this lane feeds
-      bf16x8 af[MI], bfr[NI];
+    for (int mi = 0; mi < MI; ++mi)
+      fa[f][mi] = *reinterpret_cast<const bf16x8*>(
+          &As[swz(wm * (BM / 2) + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][swz(wm * (BM / 2) + mi * 32 + (lane & 31), kc)]);
+    for (int ni = 0; ni < NI; ++ni)
+      fb[f][ni] = *reinterpret_cast<const bf16x8*>(&Bs[swz(bfrag_row(ni) + (lane & 31), kc)]);
+  };
+  auto mfmas = [&](int f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8*>(&Bs[buf][swz(bfrag_row(ni) + (lane & 31), kc)]);
+        acc[mi][ni] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][mi], fb[f][ni], acc[mi][ni], 0, 0, 0);
+  };
+  constexpr int kMF = MI * NI, kFR = MI + NI;  // MFMAs and fragment reads per sub-step
+
+  // Software pipeline over K steps, two LDS stages. In step kt (stage s = kt&1):
+  // sub-steps 0..2 run their MFMAs while reading the next sub-step's fragments;
+  // then, once this wave's stage-s reads and its loads of step kt+1 are done,
+  // one barrier, after which the loads of step kt+2 refill stage s while
+  // sub-step 3's MFMAs run alongside the first fragment reads of step kt+1.
+  // Past the last step the loads repeat step nk-1 into a stage nobody reads
+  // again, which keeps the loop free of branches around them.
+  const int nk = K / kBK;
+  auto step = [&](const uint16_t* cur, const uint16_t* nxt, int kt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+      fload((kk + 1) & 1, cur, kk + 1);
+      mfmas(kk & 1);
+      // the reads go out early, one per MFMA, so they land before sub-step kk+1
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      for (int i = 0; i < kFR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      if constexpr (kMF > kFR) __builtin_amdgcn_sched_group_barrier(0x008, kMF - kFR, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+    issue(const_cast<uint16_t*>(cur), kn * kBK);
+    fload(0, nxt, 0);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < kFR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, (AI + BI) / kFR, 0);  // global -> LDS
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // LDS read
+    }
+    if constexpr (kMF > kFR) __builtin_amdgcn_sched_group_barrier(0x008, kMF - kFR, 0);
+  };
+  issue(lds0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  issue(lds1, (nk > 1 ? 1 : 0) * kBK);
+  fload(0, lds0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(lds0, lds1, kt);
+    step(lds1, lds0, kt + 1);
   }
+  if (kt < nk) step(lds0, lds1, kt);
+  // the trailing loads must land before the block's LDS is released
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- epilogue: result (row, col) of register r of a 32x32 tile is
   // row 8*(r/4) + 4*(lane/32) + r%4, col lane%32.
@@ -215,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int OCC>
 hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, const int32_t* offs,
                    const int32_t* cnts, const void* w_gate_up, const void* w_down, void* hbuf,
                    void* out, hipStream_t s) {
@@ -225,13 +311,13 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, const in
     return (unsigned)((n + kXCD - 1) / kXCD * kXCD);
   };
   const int nt1 = I / (BN / 2);
-  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
+  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E,
                           static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
                           static_cast<uint16_t*>(hbuf), (int64_t)I, nt1);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
-  return launch(ffn_gemm_kernel<false, BM, BN>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
+  return launch(ffn_gemm_kernel<false, BM, BN, OCC>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E,
                 static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
                 static_cast<uint16_t*>(out), (int64_t)H, nt2);
@@ -244,8 +330,8 @@ hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, in
                                 const void* w_down, void* hbuf, void* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (I % 128 == 0 && H % 256 == 0)
-    return run_ffn<256, 256>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
-  return run_ffn<128, 128>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
+    return run_ffn<256, 256, 1>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
+  return run_ffn<128, 128, 2>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
 }
 
 }  // namespace moe

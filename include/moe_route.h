@@ -160,7 +160,9 @@ size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I);
  *   h_j = round_bf16( g / (1 + exp(-g)) * u )   (stored in the workspace)
  *   expert_out[n][c] = round_bf16( sum_j Wd[e][c][j] h_j )  (fp32 accumulation)
  * for every row n in [expert_offsets[e], + expert_counts[e]); other rows are
- * untouched. bf16 only (shape->dtype == MOE_BF16); I % 64 == 0, H % 128 == 0.
+ * untouched. bf16 only (shape->dtype == MOE_BF16); I % 64 == 0, H % 128 == 0,
+ * 4*I*H < 2^31 and 512*H < 2^31 (one expert's weights and one 256-row tile are
+ * addressed with 31-bit byte offsets).
  * w_gate_up [E][2I][H] bf16 (rows 0..I-1 gate, I..2I-1 up), w_down [E][H][I]
  * bf16, send_buf and expert_out [T*k][H], all 16-byte aligned. workspace:
  * moe_expert_swiglu_workspace_bytes(shape, I) bytes, clobbered.

@@ -113,3 +113,13 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.h" not in text, f
+
+
+def test_swiglu_size_limits():
+    L = moe.lib()
+    sh = _shape(T=8, H=4096, E=16, k=2, R=1)
+    # one expert's gate/up weights past the 31-bit byte range of the kernels' descriptors
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1 << 17, *[FAKE] * 7, 1 << 40, None) == ARG
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1408 + 32, *[FAKE] * 7, 1 << 40, None) == ARG
+    sh32 = _shape(T=8, H=4096, E=16, k=2, R=1, dtype=moe.MOE_F32)
+    assert L.moe_expert_swiglu(ctypes.byref(sh32), 1408, *[FAKE] * 7, 1 << 40, None) == UNSUPPORTED
