@@ -5,7 +5,11 @@ One step = the whole path on one batch of synthetic input, inputs already in
 HBM: route (top-k gating) -> dispatch index (counts, offsets, positions) ->
 dispatch copy (permute into the send buffer) -> experts (identity-scaled, or
 the SwiGLU FFN on MFMA for the local-layer workload) -> combine -> skew
-statistics of S. Every step runs in the library's HIP kernels on torch's current
+statistics of S. By default route, index and statistics go through the fused
+entry point moe_route_index (the counting pass inside the routing kernel, the
+statistics from one extra block of the placing kernel: 5 kernels a step);
+--unfused calls moe_route, moe_dispatch_index and moe_stats instead (7
+kernels). Every step runs in the library's HIP kernels on torch's current
 stream; torch only provides memory and the stream.
 
 Prints ONE JSON line. `value` is whole-step tokens/s over K timed steps (wall
@@ -35,9 +39,6 @@ METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI3
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine", "stats")
-KERNEL_OF = {"route": "route_kernel", "dispatch_index": "count_kernel+place_kernel",
-             "dispatch_copy": "copy_kernel", "expert": "expert_scale_kernel",
-             "combine": "combine_kernel", "stats": "stats_kernel"}
 
 
 class HipEvents:
@@ -75,6 +76,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--graph", action="store_true",
                     help="also time K steps replayed from one captured HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate route / dispatch_index / stats calls (7 kernels a step)")
     return ap.parse_args()
 
 
@@ -84,6 +87,7 @@ def algorithmic_bytes(wl) -> dict:
     out = {
         "route": T * E * 4 + T * k * 8,                          # logits in; idx + w out
         "dispatch_index": 12 * T * k + 4 * E,                    # idx in; pos, row_token, S out
+        # (fused path: the counting pass moves no HBM bytes beyond route's)
         "stats": 4 * E,                                          # S in
         "dispatch_copy": T * H * b + T * k * H * b + 4 * T * k,  # x once, k copies, pos
         "expert": 2 * T * k * H * b,                             # rows in, rows out
@@ -188,60 +192,80 @@ def main() -> int:
     shp = ctypes.byref(sh)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    calls = {
-        "route": (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream)),
-        "dispatch_index": (L.moe_dispatch_index, (
-            shp, P(topk_idx), P(buf["expert_counts"]), P(buf["expert_offsets"]),
-            P(buf["rank_counts"]), P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
-            P(buf["row_token"]), P(buf["workspace"]), buf["workspace"].numel(), stream)),
-        "dispatch_copy": (L.moe_dispatch_copy, (shp, P(x), P(buf["pos"]), P(buf["send_buf"]),
-                                                stream)),
-        "expert": (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
-                                        P(buf["expert_counts"]), P(expert_out), stream)),
-        "combine": (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream)),
-        "stats": (L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream)),
-    }
-    STAGES_RUN = STAGES
+    index_args = (P(buf["expert_counts"]), P(buf["expert_offsets"]), P(buf["rank_counts"]),
+                  P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
+                  P(buf["row_token"]))
     if swiglu:
-        calls["expert"] = (L.moe_expert_swiglu, (
+        expert_call = (L.moe_expert_swiglu, (
             shp, wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
             P(w_gu), P(w_dn), P(expert_out), P(ffn_ws), ffn_ws.numel(), stream))
-    kernel_of = dict(KERNEL_OF)
-    if swiglu:
-        kernel_of["expert"] = "ffn_gemm_kernel<gate_up>+ffn_gemm_kernel<down>"
+        expert_kernels = [("expert", "ffn_gemm_kernel<gate_up>"),
+                          ("expert", "ffn_gemm_kernel<down>")]
+    else:
+        expert_call = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
+                                            P(buf["expert_counts"]), P(expert_out), stream))
+        expert_kernels = [("expert", "expert_scale_kernel")]
+    # Each call: (C function, arguments, [(stage, kernel) per kernel it launches, in order]).
+    if args.unfused:
+        calls = [
+            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
+             [("route", "route_kernel")]),
+            (L.moe_dispatch_index, (shp, P(topk_idx), *index_args, P(buf["workspace"]),
+                                    buf["workspace"].numel(), stream),
+             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel")]),
+        ]
+    else:
+        calls = [
+            (L.moe_route_index, (shp, P(logits), P(topk_idx), P(topk_w), *index_args,
+                                 P(stats_raw), P(buf["workspace"]), buf["workspace"].numel(),
+                                 stream),
+             [("route", "route_count_kernel"), ("dispatch_index", "place_kernel(+stats block)")]),
+        ]
+    calls += [
+        (L.moe_dispatch_copy, (shp, P(x), P(buf["pos"]), P(buf["send_buf"]), stream),
+         [("dispatch_copy", "copy_kernel")]),
+        (*expert_call, expert_kernels),
+        (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream),
+         [("combine", "combine_kernel")]),
+    ]
+    if args.unfused:
+        calls.append((L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream),
+                      [("stats", "stats_kernel")]))
+    STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
+    kernel_of = {st: "+".join(kn for c in calls for g, kn in c[2] if g == st) for st in STAGES_RUN}
 
     hipev = HipEvents()
     set_events = L.moe_set_timing_events
 
-    NPAIR = 4  # event pairs per stage (a stage launches at most 2 kernels)
-    launched = {}
+    NPAIR = 4  # event pairs per call (a call launches at most 2 kernels)
 
     def step(evs=None):
-        """One pass of the path; evs[name] = (starts, stops) event arrays for the hook."""
-        for name in STAGES_RUN:
-            fn, a = calls[name]
+        """One pass of the path; evs[i] = (starts, stops) event arrays of call i."""
+        for i, (fn, a, kernels) in enumerate(calls):
             if evs is not None:
-                set_events(evs[name][0], evs[name][1], NPAIR)
+                set_events(evs[i][0], evs[i][1], NPAIR)
             st = fn(*a)
             if evs is not None:
-                launched[name] = L.moe_timed_launches()
+                n = L.moe_timed_launches()
                 set_events(None, None, 0)
+                if n != len(kernels):
+                    raise RuntimeError(f"call {i} launched {n} kernels, expected {len(kernels)}")
             if st != 0:
-                raise RuntimeError(f"{name}: {moe.status_string(st)}")
+                raise RuntimeError(f"call {i}: {moe.status_string(st)}")
 
     def new_events(n):
         def arr():
             return (ctypes.c_void_p * NPAIR)(*[hipev.create() for _ in range(NPAIR)])
-        return [{nm: (arr(), arr()) for nm in STAGES_RUN} for _ in range(n)]
+        return [[(arr(), arr()) for _ in calls] for _ in range(n)]
 
     def stage_means(evs):
         """Per stage: summed execution time of its kernels, averaged over steps."""
-        out = {}
-        for nm in STAGES_RUN:
-            n = launched[nm]
-            out[nm] = float(np.mean([sum(hipev.ms(e[nm][0][j], e[nm][1][j]) for j in range(n))
-                                     for e in evs]))
-        return out
+        tot = {st: 0.0 for st in STAGES_RUN}
+        for e in evs:
+            for i, (_, _, kernels) in enumerate(calls):
+                for j, (st, _) in enumerate(kernels):
+                    tot[st] += hipev.ms(e[i][0][j], e[i][1][j])
+        return {st: v / len(evs) for st, v in tot.items()}
 
     for _ in range(args.warmup):
         step()
@@ -274,17 +298,16 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         stream_c = ctypes.c_void_p(side.cuda_stream)
-        saved = dict(calls)
-        for nm in calls:  # rebind the stream argument to the capture stream
-            fn, a = calls[nm]
-            calls[nm] = (fn, tuple(stream_c if v is stream else v for v in a))
+        saved = list(calls)
+        for i, (fn, a, kn) in enumerate(calls):  # rebind the stream argument
+            calls[i] = (fn, tuple(stream_c if v is stream else v for v in a), kn)
         with torch.cuda.stream(side):
             step()
             torch.cuda.current_stream().synchronize()
             with torch.cuda.graph(g, stream=side):
                 step()
         torch.cuda.synchronize()
-        calls.update(saved)
+        calls[:] = saved
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
@@ -338,7 +361,7 @@ def main() -> int:
 
     # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
     single = [n for n in ("route", "dispatch_copy", "expert", "combine", "stats")
-              if not (swiglu and n == "expert")]
+              if n in STAGES_RUN and not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
                 "achieved": round(gbs(dom, stage_ms[dom]), 1), "peak": HBM_PEAK_GBS,
@@ -371,13 +394,17 @@ def main() -> int:
                 + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
         "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
                    "waves": W, "routing": wl.routing, "expert": wl.expert,
-                   "step": "route+dispatch_index+dispatch_copy+expert+combine+stats"},
+                   "step": ("route+dispatch_index+stats (moe_route_index)" if not args.unfused
+                            else "route+dispatch_index+stats (separate calls)")
+                           + "+dispatch_copy+expert+combine",
+                   "kernels_per_step": sum(len(c[2]) for c in calls)},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
             "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
             "GB/s": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes": dc_bytes,
+            "kernels": "+".join(kernel_of[n] for n in dc_keys),
         },
         "roofline": roofline,
         "stages": stage_report(stage_ms),

@@ -7,7 +7,8 @@ library must be built (``__graft_entry__.build()``); importing the functions
 without it raises, there is no fallback.
 
 Entry points mirror include/moe_route.h: ``route``, ``dispatch_index``,
-``dispatch_copy``, ``dispatch``, ``expert_scale``, ``combine``, ``stats``.
+``route_index``, ``dispatch_copy``, ``dispatch``, ``expert_scale``,
+``expert_swiglu``, ``combine``, ``stats``.
 """
 from __future__ import annotations
 
@@ -49,6 +50,8 @@ SIGNATURES = {
     "moe_dispatch_workspace_bytes": ([_shp], ctypes.c_size_t),
     "moe_dispatch_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                             _vp], ctypes.c_int),
+    "moe_route_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_dispatch_copy": ([_shp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
@@ -175,6 +178,21 @@ def dispatch_index(topk_idx: torch.Tensor, shape: Shape, out: dict):
         _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]),
         _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(out["workspace"]),
         out["workspace"].numel(), _stream()), "moe_dispatch_index")
+    return out
+
+
+def route_index(logits: torch.Tensor, shape: Shape, out: dict, topk_idx: torch.Tensor,
+                topk_w: torch.Tensor, stats_out: torch.Tensor | None = None) -> dict:
+    """Routing + counts, offsets, positions (+ statistics into the raw device
+    struct `stats_out` when given) in two launches; buffers as alloc_dispatch."""
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    sh = shape.c()
+    _check(lib().moe_route_index(
+        ctypes.byref(sh), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(out["expert_counts"]),
+        _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
+        _ptr(out["wave_offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(stats_out),
+        _ptr(out["workspace"]), out["workspace"].numel(), _stream()), "moe_route_index")
     return out
 
 

@@ -34,8 +34,17 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; 
 
 hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Histogram rows of the fused routing + counting pass (one per routing block).
+int64_t route_index_blocks(const moe_shape* sh) {
+  if (sh->T == 0) return 0;
+  const int64_t tpb = moe::route_count_tokens_per_block(sh->T, sh->E, sh->k);
+  return (sh->T + tpb - 1) / tpb;
+}
+
 size_t workspace_bytes(const moe_shape* sh) {
-  const int64_t nb = moe::num_chunks(int64_t(sh->T) * sh->k, sh->E);
+  int64_t nb = moe::num_chunks(int64_t(sh->T) * sh->k, sh->E);
+  const int64_t nr = route_index_blocks(sh);
+  if (nr > nb) nb = nr;
   const int64_t bytes = (nb < 1 ? 1 : nb) * int64_t(sh->E) * 4;
   return size_t((bytes + 255) / 256 * 256);
 }
@@ -132,6 +141,33 @@ int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   return status_of(moe::launch_place(topk_idx, npicks, shape->k, shape->E, shape->R, shape->W,
                                      hist, expert_counts, expert_offsets, rank_counts,
                                      rank_offsets, wave_offsets, pos, row_token, s));
+}
+
+int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_idx,
+                    float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                    int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
+                    int32_t* pos, int32_t* row_token, moe_stats_t* stats, void* workspace,
+                    size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (int64_t(shape->T) * shape->E >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!logits || !topk_w)) return MOE_ERR_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_w, 4) || !aligned(stats, 8)) return MOE_ERR_ALIGN;
+  st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                        rank_offsets, wave_offsets, pos, row_token, workspace,
+                        workspace_bytes_given);
+  if (st != MOE_OK) return st;
+  const int64_t npicks = int64_t(shape->T) * shape->k;
+  const int64_t tpb = moe::route_count_tokens_per_block(shape->T, shape->E, shape->k);
+  hipStream_t s = as_stream(stream);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  st = status_of(moe::launch_route_count(logits, shape->T, shape->E, shape->k, topk_idx, topk_w,
+                                         hist, s));
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_place_chunks(
+      topk_idx, npicks, tpb * shape->k, (int)route_index_blocks(shape), shape->k, shape->E,
+      shape->R, shape->W, hist, expert_counts, expert_offsets, rank_counts, rank_offsets,
+      wave_offsets, pos, row_token, stats, s));
 }
 
 int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos, void* send_buf,

@@ -19,62 +19,89 @@ struct StatsScratch {
 
 namespace stats_detail {
 
-__device__ __forceinline__ int64_t wave_sum(int64_t v) {
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_down(v, o);
-  return v;
+// Wave-wide reductions (DPP within rows, scalar lane reads across rows).
+template <typename V>
+__device__ __forceinline__ V wave_sum(V v) {
+  return group_reduce(v, kWave, [](V x, V y) { return x + y; });
 }
-__device__ __forceinline__ int64_t wave_max(int64_t v) {
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const int64_t u = __shfl_down(v, o);
-    v = u > v ? u : v;
-  }
-  return v;
+template <typename V>
+__device__ __forceinline__ V wave_max(V v) {
+  return group_reduce(v, kWave, [](V x, V y) { return x > y ? x : y; });
 }
-__device__ __forceinline__ int64_t wave_min(int64_t v) {
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const int64_t u = __shfl_down(v, o);
-    v = u < v ? u : v;
+template <typename V>
+__device__ __forceinline__ V wave_min(V v) {
+  return group_reduce(v, kWave, [](V x, V y) { return x < y ? x : y; });
+}
+
+// Sum over ordered pairs (a, b) of |v[a] - v[b]| for n values in LDS, spread
+// over all nt threads: with n <= nt, thread t takes a = t mod n and one of the
+// nt / n slices of b; otherwise a strides over the threads. |difference| fits
+// in 32 bits (values are counts below 2^31), the running sum is 64-bit.
+template <typename V>
+__device__ __forceinline__ int64_t pair_abs_sum(const V* v, int n, int tid, int nt) {
+  int64_t acc = 0;
+  if (n <= nt) {
+    const int S = nt / n;
+    if (tid < S * n) {
+      const int a = tid % n, sl = tid / n;
+      const int len = (n + S - 1) / S, b0 = sl * len, b1 = (b0 + len < n) ? b0 + len : n;
+      const int64_t va = v[a];
+#pragma unroll 8
+      for (int b = b0; b < b1; ++b) {
+        const int64_t d = va - (int64_t)v[b];
+        acc += d < 0 ? -d : d;
+      }
+    }
+  } else {
+    for (int a = tid; a < n; a += nt) {
+      const int64_t va = v[a];
+#pragma unroll 8
+      for (int b = 0; b < n; ++b) {
+        const int64_t d = va - (int64_t)v[b];
+        acc += d < 0 ? -d : d;
+      }
+    }
   }
-  return v;
+  return acc;
 }
 
 }  // namespace stats_detail
 
 // Statistics of the E counts in LDS `cnt`, written to `out` by thread 0. Every
-// thread of the block must call it (it has barriers); E <= 1024, blockDim <= 1024.
+// thread of the block must call it (it has barriers); E <= 1024, blockDim a
+// multiple of 64 and <= 1024.
+// Counts are below 2^31 in total, so totals, maxima and minima are 32-bit; only
+// the two pair sums need 64 bits.
 __device__ inline void block_stats(const int32_t* cnt, int E, int R, StatsScratch& sc,
                                    moe_stats_t* out) {
   using namespace stats_detail;
   const int nt = blockDim.x, tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nw = (nt + kWave - 1) / kWave;
   const int L = E / R;
+  // per-rank loads: one rank per thread, its L slots summed with independent loads
   for (int r = tid; r < R; r += nt) {
     int64_t s = 0;
+#pragma unroll 8
     for (int j = 0; j < L; ++j) s += cnt[r * L + j];
     sc.vr[r] = s;
   }
   __syncthreads();
 
-  int64_t ge = 0, gr = 0, tot = 0;
-  int64_t emax = INT64_MIN, emin = INT64_MAX, rmax = INT64_MIN, rmin = INT64_MAX;
+  int64_t ge = pair_abs_sum(cnt, E, tid, nt);
+  int64_t gr = pair_abs_sum(sc.vr, R, tid, nt);
+  int32_t tot = 0, emax = INT32_MIN, emin = INT32_MAX, rmax = INT32_MIN, rmin = INT32_MAX;
   for (int a = tid; a < E; a += nt) {
-    const int64_t va = cnt[a];
-    for (int b = 0; b < E; ++b) {
-      const int64_t d = va - cnt[b];
-      ge += d < 0 ? -d : d;
-    }
+    const int32_t va = cnt[a];
     tot += va;
     emax = va > emax ? va : emax;
     emin = va < emin ? va : emin;
   }
   for (int a = tid; a < R; a += nt) {
-    const int64_t va = sc.vr[a];
-    for (int b = 0; b < R; ++b) {
-      const int64_t d = va - sc.vr[b];
-      gr += d < 0 ? -d : d;
-    }
+    const int32_t va = (int32_t)sc.vr[a];
     rmax = va > rmax ? va : rmax;
     rmin = va < rmin ? va : rmin;
   }
+  // two-level reduction: within each wave, then wave 0 over the per-wave partials
   ge = wave_sum(ge);
   gr = wave_sum(gr);
   tot = wave_sum(tot);
@@ -92,29 +119,29 @@ __device__ inline void block_stats(const int32_t* cnt, int E, int R, StatsScratc
     sc.red[6][wid] = rmin;
   }
   __syncthreads();
-  if (tid == 0) {
-    const int nw = (nt + kWave - 1) / kWave;
-    for (int q = 1; q < nw; ++q) {
-      sc.red[0][0] += sc.red[0][q];
-      sc.red[1][0] += sc.red[1][q];
-      sc.red[2][0] += sc.red[2][q];
-      sc.red[3][0] = sc.red[3][q] > sc.red[3][0] ? sc.red[3][q] : sc.red[3][0];
-      sc.red[4][0] = sc.red[4][q] < sc.red[4][0] ? sc.red[4][q] : sc.red[4][0];
-      sc.red[5][0] = sc.red[5][q] > sc.red[5][0] ? sc.red[5][q] : sc.red[5][0];
-      sc.red[6][0] = sc.red[6][q] < sc.red[6][0] ? sc.red[6][q] : sc.red[6][0];
+  if (wid == 0) {
+    const bool in = lane < nw;
+    ge = wave_sum(in ? sc.red[0][lane] : (int64_t)0);
+    gr = wave_sum(in ? sc.red[1][lane] : (int64_t)0);
+    tot = wave_sum(in ? (int32_t)sc.red[2][lane] : 0);
+    emax = wave_max(in ? (int32_t)sc.red[3][lane] : INT32_MIN);
+    emin = wave_min(in ? (int32_t)sc.red[4][lane] : INT32_MAX);
+    rmax = wave_max(in ? (int32_t)sc.red[5][lane] : INT32_MIN);
+    rmin = wave_min(in ? (int32_t)sc.red[6][lane] : INT32_MAX);
+    if (lane == 0) {
+      const int64_t T = tot;
+      moe_stats_t st;
+      st.total = T;
+      st.expert_max = emax;
+      st.expert_min = emin;
+      st.rank_max = rmax;
+      st.rank_min = rmin;
+      st.expert_max_over_mean = T ? (double)((int64_t)E * emax) / (double)T : 0.0;
+      st.rank_max_over_mean = T ? (double)((int64_t)R * rmax) / (double)T : 0.0;
+      st.expert_gini = T ? (double)ge / (double)(2 * (int64_t)E * T) : 0.0;
+      st.rank_gini = T ? (double)gr / (double)(2 * (int64_t)R * T) : 0.0;
+      *out = st;
     }
-    const int64_t T = sc.red[2][0];
-    moe_stats_t st;
-    st.total = T;
-    st.expert_max = (int32_t)sc.red[3][0];
-    st.expert_min = (int32_t)sc.red[4][0];
-    st.rank_max = (int32_t)sc.red[5][0];
-    st.rank_min = (int32_t)sc.red[6][0];
-    st.expert_max_over_mean = T ? (double)((int64_t)E * sc.red[3][0]) / (double)T : 0.0;
-    st.rank_max_over_mean = T ? (double)((int64_t)R * sc.red[5][0]) / (double)T : 0.0;
-    st.expert_gini = T ? (double)sc.red[0][0] / (double)(2 * (int64_t)E * T) : 0.0;
-    st.rank_gini = T ? (double)sc.red[1][0] / (double)(2 * (int64_t)R * T) : 0.0;
-    *out = st;
   }
 }
 

@@ -36,6 +36,65 @@ __device__ __forceinline__ float order_key_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// ---- cross-lane moves without LDS round trips (DPP). Within each row of 16
+// lanes: quad_perm [1,0,3,2] and [2,3,0,1] read lanes i^1 and i^2; once quads
+// are uniform, row_half_mirror (lane i <- 7-i of its half-row) reads the other
+// quad, and once half-rows are uniform, row_mirror (lane i <- 15-i) the other
+// half-row. Rows are combined through scalar lane reads.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v) {
+  return ((uint64_t)dpp_move<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_move<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_move(int32_t v) {
+  return (int32_t)dpp_move<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_move(int64_t v) {
+  return (int64_t)dpp_move<CTRL>((uint64_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  return __longlong_as_double((long long)dpp_move<CTRL>((uint64_t)__double_as_longlong(v)));
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int l) {
+  return ((uint64_t)lane_value((uint32_t)(v >> 32), l) << 32) | lane_value((uint32_t)v, l);
+}
+__device__ __forceinline__ int32_t lane_value(int32_t v, int l) {
+  return (int32_t)lane_value((uint32_t)v, l);
+}
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l) {
+  return (int64_t)lane_value((uint64_t)v, l);
+}
+__device__ __forceinline__ double lane_value(double v, int l) {
+  return __longlong_as_double((long long)lane_value((uint64_t)__double_as_longlong(v), l));
+}
+
+// op-reduction over aligned groups of G lanes (G a power of two <= 64); every
+// lane of a group ends with the same result. The whole wave must be active.
+template <typename V, typename Op>
+__device__ __forceinline__ V group_reduce(V v, int G, Op op) {
+  if (G >= 2) v = op(v, dpp_move<kDppXor1>(v));
+  if (G >= 4) v = op(v, dpp_move<kDppXor2>(v));
+  if (G >= 8) v = op(v, dpp_move<kDppHalfMirror>(v));
+  if (G >= 16) v = op(v, dpp_move<kDppMirror>(v));
+  if (G >= 32) {
+    const V lo = op(lane_value(v, 0), lane_value(v, 16));
+    const V hi = op(lane_value(v, 32), lane_value(v, 48));
+    v = (G == 64) ? op(lo, hi) : ((__lane_id() < 32) ? lo : hi);
+  }
+  return v;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const uint32_t lane = __lane_id();
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));

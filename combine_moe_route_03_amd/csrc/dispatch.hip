@@ -20,6 +20,7 @@
 //                 prefetched while the current one is placed.
 //   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
 //                 k stores.
+#include "block_stats.h"
 #include "device.h"
 #include "launch.h"
 
@@ -59,13 +60,14 @@ __global__ __launch_bounds__(kB) void place_kernel(
     int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ row_token) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_token, moe_stats_t* __restrict__ stats,
+    int sblock) {
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
   __shared__ int32_t ppre[kB];             // (slice, expert) partial prefix
   __shared__ int32_t pall[kB];             // (slice, expert) partial total
-  __shared__ int32_t wcnt[kWaves][kMaxE];  // per-wave counts of one 1024-pick batch
+  __shared__ __attribute__((aligned(16))) int32_t wcnt[kWaves][kMaxE];  // per-wave counts of a batch
   __shared__ int32_t part[kWaves];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -118,6 +120,10 @@ __global__ __launch_bounds__(kB) void place_kernel(
     cnt[tid] = A;
   }
   __syncthreads();
+  if (b == sblock) {  // the statistics block (only launched when stats is non-null)
+    block_stats(cnt, E, R, *reinterpret_cast<StatsScratch*>(&wcnt[0][0]), stats);
+    return;
+  }
 
   // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread j
   //    owns bucket j.
@@ -227,16 +233,27 @@ hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist
                 chunk_picks(npicks, E), E, hist);
 }
 
+hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk, int nb, int k,
+                               int E, int R, int W, const int32_t* hist, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* rank_counts,
+                               int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                               int32_t* row_token, moe_stats_t* stats, hipStream_t s) {
+  // With no picks one block still runs to publish zero counts and offsets; the
+  // statistics block, if any, comes after the placing blocks.
+  const int sblock = nb == 0 ? 1 : nb;
+  const unsigned grid = (unsigned)sblock + (stats != nullptr ? 1u : 0u);
+  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, chunk, nb, k, E,
+                ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
+                rank_offsets, wave_offsets, pos, row_token, stats, sblock);
+}
+
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
                         int32_t* pos, int32_t* row_token, hipStream_t s) {
-  const int64_t nb = num_chunks(npicks, E);
-  // With no picks one block still runs to publish zero counts and offsets.
-  const unsigned grid = nb == 0 ? 1u : (unsigned)nb;
-  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks,
-                chunk_picks(npicks, E), (int)nb, k, E, ilog2_ceil(E), R, W, hist, expert_counts,
-                expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token);
+  return launch_place_chunks(idx, npicks, chunk_picks(npicks, E), (int)num_chunks(npicks, E), k,
+                             E, R, W, hist, expert_counts, expert_offsets, rank_counts,
+                             rank_offsets, wave_offsets, pos, row_token, nullptr, s);
 }
 
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,

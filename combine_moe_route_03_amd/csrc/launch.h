@@ -25,9 +25,14 @@ inline int pow2_at_least(int v) {
   return p;
 }
 
+// Most chunks (hist rows) a placing pass reads for E experts.
+inline int64_t max_index_chunks(int E) {
+  const int64_t m = 65536 / pow2_at_least(E);
+  return m > 512 ? 512 : m;
+}
+
 inline int64_t chunk_picks(int64_t npicks, int E) {
-  int64_t max_chunks = 65536 / pow2_at_least(E);
-  if (max_chunks > 512) max_chunks = 512;
+  const int64_t max_chunks = max_index_chunks(E);
   int64_t c = (npicks + max_chunks - 1) / max_chunks;
   c = (c + kIndexBlock - 1) / kIndexBlock * kIndexBlock;
   return c < kIndexBlock ? kIndexBlock : c;
@@ -78,6 +83,19 @@ hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R,
                         const int32_t* hist, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
                         int32_t* pos, int32_t* row_token, hipStream_t s);
+
+// Routing fused with counting: hist[b][E] for blocks of
+// route_count_tokens_per_block(T, E, k) tokens (at most max_index_chunks(E)
+// blocks), then placing with chunks of that many tokens' picks; with `stats`
+// non-null one extra place block writes the skew statistics.
+int route_count_tokens_per_block(int T, int E, int k);
+hipError_t launch_route_count(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                              int32_t* hist, hipStream_t s);
+hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk, int nb, int k,
+                               int E, int R, int W, const int32_t* hist, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* rank_counts,
+                               int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                               int32_t* row_token, moe_stats_t* stats, hipStream_t s);
 
 // Row copies; row_bytes is a multiple of 16.
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,

@@ -3,18 +3,75 @@
 // (MoE systems survey, crad.ict.ac.cn, section 1.1, eq. (2): the non-kept
 // logits act as -inf, so only the k kept ones enter the softmax).
 //
-// One aligned group of G = 2^glog lanes of a wave64 handles one token. Lane g
-// holds V consecutive logits (experts g*V .. g*V+V-1) as order-preserving
-// uint32 keys. Each of the k rounds takes the lane-local maximum (first index
-// on ties), a butterfly max over the group, and a ballot: the lowest lane
-// holding the maximum also holds the lowest expert id with that value. G >= k,
-// so lane i keeps pick i and writes it. The softmax is evaluated in double and
-// rounded once to fp32.
+// One aligned group of G = 2^glog lanes of a wave64 handles one token; lane g
+// holds V consecutive logits (experts g*V .. g*V+V-1). G >= k, so lane i keeps
+// pick i and writes it. The fused variant also histograms the picks of its
+// block for the placing pass.
 #include "device.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
+
+// Top-k of token t by the G-lane group this lane belongs to (lane g of the
+// group). Each logit becomes a 64-bit key: the order-preserving uint32 of the
+// value above ~e, so the larger key is the larger logit and, on equal logits,
+// the lower expert id; key 0 marks "empty or taken" (every finite float maps
+// above it). Each of the k rounds takes the lane-local maximum and a DPP max
+// over the group; the lane holding that key clears it. Lane g < k keeps pick g.
+// The softmax over the k kept logits is evaluated in double (group sum by DPP,
+// identical on every lane) and rounded once to fp32. Returns id -1 on lanes
+// g >= k and for inactive tokens.
+template <int V, bool kVec4>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int64_t t,
+                                            bool active, int E, int k, int G, int g,
+                                            int& pick_id, float& pick_w) {
+  uint64_t key[V];
+  const float* row = logits + t * (int64_t)E;
+  auto make = [](float f, int e) -> uint64_t {
+    return ((uint64_t)float_order_key(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+  };
+  if constexpr (kVec4) {
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const int e0 = g * V + 4 * j;
+      const bool ok = active && e0 < E;  // E % 4 == 0: the four are all in range or all out
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) f = *reinterpret_cast<const float4*>(row + e0);
+      key[4 * j + 0] = ok ? make(f.x, e0 + 0) : 0ull;
+      key[4 * j + 1] = ok ? make(f.y, e0 + 1) : 0ull;
+      key[4 * j + 2] = ok ? make(f.z, e0 + 2) : 0ull;
+      key[4 * j + 3] = ok ? make(f.w, e0 + 3) : 0ull;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = g * V + v;
+      key[v] = (active && e < E) ? make(row[e], e) : 0ull;
+    }
+  }
+
+  const auto kmax = [](uint64_t x, uint64_t y) { return x > y ? x : y; };
+  uint64_t top = 0, mine = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) best = kmax(best, key[v]);
+    const uint64_t gm = group_reduce(best, G, kmax);
+    if (r == 0) top = gm;
+    if (g == r) mine = gm;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (key[v] == gm) key[v] = 0ull;  // keys are unique: one slot of the group
+  }
+
+  const float vtop = order_key_float((uint32_t)(top >> 32));
+  const float vmine = order_key_float((uint32_t)(mine >> 32));
+  const double ex = (g < k) ? exp((double)vmine - (double)vtop) : 0.0;
+  const double s = group_reduce(ex, G, [](double x, double y) { return x + y; });
+  pick_id = (active && g < k) ? (int)(0xFFFFFFFFu - (uint32_t)mine) : -1;
+  pick_w = (float)(ex / s);
+}
 
 template <int V, bool kVec4>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
@@ -25,74 +82,44 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t t = gtid >> glog;
   const int g = (int)(gtid & (G - 1));
-  const bool active = t < T;
-  const int gbase = (int)(threadIdx.x & (kWave - 1)) & ~(G - 1);
-  const uint64_t gbits = (G == 64) ? ~0ull : ((1ull << G) - 1ull);
+  int id;
+  float wt;
+  route_token<V, kVec4>(logits, t, t < T, E, k, G, g, id, wt);
+  if (id >= 0) {
+    idx[t * k + g] = id;
+    w[t * k + g] = wt;
+  }
+}
 
-  uint32_t key[V];
-  const float* row = logits + t * (int64_t)E;
-  if constexpr (kVec4) {
-#pragma unroll
-    for (int j = 0; j < V / 4; ++j) {
-      const int e0 = g * V + 4 * j;
-      const bool ok = active && e0 < E;  // E % 4 == 0: the four are all in range or all out
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok) f = *reinterpret_cast<const float4*>(row + e0);
-      key[4 * j + 0] = ok ? float_order_key(f.x) : 0u;
-      key[4 * j + 1] = ok ? float_order_key(f.y) : 0u;
-      key[4 * j + 2] = ok ? float_order_key(f.z) : 0u;
-      key[4 * j + 3] = ok ? float_order_key(f.w) : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int e = g * V + v;
-      key[v] = (active && e < E) ? float_order_key(row[e]) : 0u;
+// Routing fused with the counting pass of dispatch: block b routes tokens
+// [b*tpb, (b+1)*tpb) (1024/G tokens per pass) and writes the histogram of its
+// picks to hist[b][0..E) (LDS integer atomics: order-free, exact). Its picks
+// are exactly chunk b of the placing pass when chunks are tpb*k picks long.
+template <int V, bool kVec4>
+__global__ __launch_bounds__(kIndexBlock) void route_count_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int glog, int tpb,
+    int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ hist) {
+  __shared__ int32_t h[1024];
+  const int G = 1 << glog;
+  const int tid = threadIdx.x;
+  if (tid < E) h[tid] = 0;
+  __syncthreads();
+  const int g = tid & (G - 1);
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t1 = (t0 + tpb < T) ? t0 + tpb : T;
+  for (int64_t tb = t0; tb < t1; tb += kIndexBlock >> glog) {
+    const int64_t t = tb + (tid >> glog);
+    int id;
+    float wt;
+    route_token<V, kVec4>(logits, t, t < t1, E, k, G, g, id, wt);
+    if (id >= 0) {
+      idx[t * k + g] = id;
+      w[t * k + g] = wt;
+      atomicAdd(&h[id], 1);
     }
   }
-
-  // Key 0 marks "empty or taken": every finite float maps above it.
-  float top = 0.f, mine = 0.f;
-  int mine_id = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = key[0];
-    int bi = 0;
-#pragma unroll
-    for (int v = 1; v < V; ++v) {
-      if (key[v] > best) {
-        best = key[v];
-        bi = v;
-      }
-    }
-    uint32_t gm = best;
-    for (int off = 1; off < G; off <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)gm, off);
-      gm = o > gm ? o : gm;
-    }
-    const uint64_t holders = (__ballot(best == gm) >> gbase) & gbits;
-    const int wl = __ffsll((unsigned long long)holders) - 1;
-    const int wbi = __shfl(bi, gbase + wl);
-    const int e = wl * V + wbi;
-    const float val = order_key_float(gm);
-    if (r == 0) top = val;
-    if (g == r) {
-      mine = val;
-      mine_id = e;
-    }
-    if (g == wl) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (v == wbi) key[v] = 0u;
-    }
-  }
-
-  const double ex = (g < k) ? exp((double)mine - (double)top) : 0.0;
-  double s = ex;
-  for (int off = 1; off < G; off <<= 1) s += __shfl_xor(s, off);
-  if (active && g < k) {
-    idx[t * k + g] = mine_id;
-    w[t * k + g] = (float)(ex / s);
-  }
+  __syncthreads();
+  if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = h[tid];
 }
 
 int next_pow2(int v) {
@@ -116,14 +143,69 @@ hipError_t go(const float* logits, int T, int E, int k, int G, int32_t* idx, flo
                 idx, w);
 }
 
+template <int V, bool kVec4>
+hipError_t go_count(const float* logits, int T, int E, int k, int G, int tpb, int32_t* idx,
+                    float* w, int32_t* hist, hipStream_t s) {
+  const unsigned blocks = (unsigned)((T + tpb - 1) / tpb);
+  return launch(route_count_kernel<V, kVec4>, dim3(blocks), dim3(kIndexBlock), 0, s, logits, T, E,
+                k, ilog2(G), tpb, idx, w, hist);
+}
+
+// Lanes per token: enough for E/4 logits a lane, at least k (k <= 32), <= 64.
+int route_group(int E, int k) {
+  int ge = next_pow2((E + 3) / 4);
+  if (ge > kWave) ge = kWave;
+  return ge > next_pow2(k) ? ge : next_pow2(k);
+}
+
+// Fused routing + counting: at most max_index_chunks(E) blocks of 1024 threads
+// (the placing pass reads one histogram row per block). Lanes per token shrink
+// (down to k and E/16, i.e. V <= 16 logits a lane) until one pass of a block
+// covers its tokens, then extra passes are added.
+void route_count_geometry(int T, int E, int k, int& G, int& tpb) {
+  const int64_t max_blocks = max_index_chunks(E);
+  const int gmin_k = next_pow2(k), gmin_e = next_pow2((E + 15) / 16);
+  const int gmin = gmin_k > gmin_e ? gmin_k : gmin_e;
+  G = route_group(E, k);
+  while (G > gmin && (int64_t)T > max_blocks * (kIndexBlock / G)) G >>= 1;
+  const int per_pass = kIndexBlock / G;
+  int64_t passes = 1;
+  while ((int64_t)T > max_blocks * per_pass * passes) ++passes;
+  tpb = (int)(per_pass * passes);
+}
+
 }  // namespace
+
+int route_count_tokens_per_block(int T, int E, int k) {
+  int G, tpb;
+  route_count_geometry(T, E, k, G, tpb);
+  return tpb;
+}
+
+hipError_t launch_route_count(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                              int32_t* hist, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int G, tpb;
+  route_count_geometry(T, E, k, G, tpb);
+  const int V = next_pow2((E + G - 1) / G);  // G >= E/16, so V <= 16
+  const bool vec4 = (V % 4 == 0) && (E % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+  switch (V) {
+    case 1: return go_count<1, false>(logits, T, E, k, G, tpb, idx, w, hist, s);
+    case 2: return go_count<2, false>(logits, T, E, k, G, tpb, idx, w, hist, s);
+    case 4: return vec4 ? go_count<4, true>(logits, T, E, k, G, tpb, idx, w, hist, s)
+                        : go_count<4, false>(logits, T, E, k, G, tpb, idx, w, hist, s);
+    case 8: return vec4 ? go_count<8, true>(logits, T, E, k, G, tpb, idx, w, hist, s)
+                        : go_count<8, false>(logits, T, E, k, G, tpb, idx, w, hist, s);
+    case 16: return vec4 ? go_count<16, true>(logits, T, E, k, G, tpb, idx, w, hist, s)
+                         : go_count<16, false>(logits, T, E, k, G, tpb, idx, w, hist, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                         hipStream_t s) {
   if (T == 0) return hipSuccess;
-  int ge = next_pow2((E + 3) / 4);
-  if (ge > kWave) ge = kWave;
-  const int G = ge > next_pow2(k) ? ge : next_pow2(k);  // k <= 32, so G <= 64
+  const int G = route_group(E, k);
   const int V = next_pow2((E + G - 1) / G);              // E <= 1024, so V <= 16
   const bool vec4 = (V % 4 == 0) && (E % 4 == 0) && ((uintptr_t)logits % 16 == 0);
   switch (V) {

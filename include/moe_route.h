@@ -124,6 +124,21 @@ int moe_dispatch_index(const moe_shape* shape, const int32_t* topk_idx,
                        void* workspace, size_t workspace_bytes,
                        moe_stream_t stream);
 
+/* Routing, the index stage and (optionally) the skew statistics in two
+ * launches: moe_route, then moe_dispatch_index, then moe_stats on the counts
+ * when stats is non-NULL, with identical results, but the counting pass runs
+ * inside the routing kernel (each routing block histograms its own picks) and
+ * the statistics come from one extra block of the placing kernel.
+ * logits [T][E] fp32 in; topk_idx, topk_w [T][k] out (as moe_route); the
+ * index outputs as moe_dispatch_index; stats: NULL or one device moe_stats_t
+ * (8-byte aligned). workspace: moe_dispatch_workspace_bytes(shape) bytes.
+ * Errors: as moe_route and moe_dispatch_index. */
+int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_idx,
+                    float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                    int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
+                    int32_t* pos, int32_t* row_token, moe_stats_t* stats, void* workspace,
+                    size_t workspace_bytes, moe_stream_t stream);
+
 /* The permute copy (explainer section 3 item 5: rows are reordered by
  * destination and packed before sending): send_buf[pos[t][i]][:] = x[t][:],
  * a bit copy. Each x row is read once and written k times; picks with

@@ -123,3 +123,27 @@ def test_swiglu_size_limits():
     assert L.moe_expert_swiglu(ctypes.byref(sh), 1408 + 32, *[FAKE] * 7, 1 << 40, None) == ARG
     sh32 = _shape(T=8, H=4096, E=16, k=2, R=1, dtype=moe.MOE_F32)
     assert L.moe_expert_swiglu(ctypes.byref(sh32), 1408, *[FAKE] * 7, 1 << 40, None) == UNSUPPORTED
+
+
+def test_route_index_validation():
+    L = moe.lib()
+    sh = _shape(T=64, E=8, k=2, R=4)
+    ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
+    args = [FAKE] * 9  # topk_idx .. row_token
+    assert L.moe_route_index(ctypes.byref(sh), None, *args, None, FAKE, ws, None) == ARG
+    assert L.moe_route_index(ctypes.byref(sh), FAKE, *args, ctypes.c_void_p((1 << 20) + 4), FAKE,
+                             ws, None) == ALIGN
+    assert L.moe_route_index(ctypes.byref(sh), FAKE, *args, None, FAKE, ws - 1, None) == WORKSPACE
+    bad = _shape(T=64, E=8, k=9, R=4)
+    assert L.moe_route_index(ctypes.byref(bad), FAKE, *args, None, FAKE, 1 << 20, None) == ARG
+
+
+def test_workspace_covers_fused_histograms():
+    # the fused path keeps one histogram row per routing block: at most
+    # 65536 / pow2(E) (and 512) rows of E counts
+    L = moe.lib()
+    for T, E, k in ((4096, 64, 6), (16384, 256, 8), (300000, 16, 4), (128, 128, 8)):
+        sh = _shape(T=T, H=16, E=E, k=k, R=1)
+        ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
+        cap = min(512, 65536 // (1 << (E - 1).bit_length()))
+        assert E * 4 <= ws <= cap * E * 4 + 255

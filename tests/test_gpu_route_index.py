@@ -1,0 +1,111 @@
+"""moe_route_index (routing with the counting pass fused into the routing
+kernel, then placing, plus the statistics block) against the oracle and against
+the separate moe_route + moe_dispatch_index + moe_stats calls, on the GPU.
+
+Bars: indices, counts, offsets, positions, row maps and statistics bit-exact;
+weights within 1e-6 relative of the oracle and identical to moe_route's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_03_amd as moe
+import oracle
+import synth
+from test_gpu_parity import (DEV, EDGES, INDEX_KEYS, PARITY, assert_weights, check_index, dev,
+                             host, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {**PARITY, **{f"edge_{n}": wl for n, wl in EDGES.items()}}
+
+
+def _fused(wl, logits_d, stats=True):
+    shape = shape_of(wl, logits_d.shape[0])
+    out = moe.alloc_dispatch(shape, DEV)
+    idx = torch.empty((shape.T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((shape.T, wl.k), dtype=torch.float32, device=DEV)
+    raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=DEV) if stats else None
+    moe.route_index(logits_d, shape, out, idx, w, stats_out=raw)
+    return idx, w, out, raw
+
+
+def _oracle_index(wl, logits):
+    idx_o, w_o = oracle.route(logits, wl.k)
+    ec, rc = oracle.counts(idx_o, wl.E, wl.R, wl.W)
+    eo, ro, wo = oracle.offsets(ec, wl.R, wl.W)
+    nrows = int(ec.sum())
+    pos, rt = oracle.positions(idx_o, wl.E, eo, nrows)
+    ref = dict(expert_counts=ec, rank_counts=rc, expert_offsets=eo, rank_offsets=ro,
+               wave_offsets=wo, pos=pos, row_token=rt, nrows=nrows)
+    return idx_o, w_o, ref
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_index_parity(name):
+    wl = CASES[name]
+    print(f"[route_index] {name}: T={wl.T} E={wl.E} k={wl.k} R={wl.R} W={wl.W}", flush=True)
+    logits = synth.logits(wl)
+    idx_o, w_o, ref = _oracle_index(wl, logits)
+    ld = dev(logits)
+    idx, w, out, raw = _fused(wl, ld)
+    # the separate calls on the same logits
+    idx_s, w_s = moe.route(ld, wl.k)
+    sep = moe.alloc_dispatch(shape_of(wl), DEV)
+    moe.dispatch_index(idx_s, shape_of(wl), sep)
+    st_s = moe.stats(sep["expert_counts"], wl.R)
+    torch.cuda.synchronize()
+
+    np.testing.assert_array_equal(host(idx), idx_o)
+    assert_weights(host(w), w_o)
+    check_index(out, ref)
+    assert moe.stats_to_dict(raw) == oracle.stats(ref["expert_counts"], wl.R)
+    assert torch.equal(idx, idx_s) and torch.equal(w, w_s)
+    for key in INDEX_KEYS:
+        assert torch.equal(out[key], sep[key]), key
+    n = ref["nrows"]
+    assert torch.equal(out["row_token"][:n], sep["row_token"][:n])
+    assert moe.stats_to_dict(raw) == st_s
+
+
+@pytest.mark.parametrize("name", ["dirichlet_waves", "local_layer"])
+def test_route_index_full_size(name):
+    """Full-size workloads, every output in full (dirichlet_waves routes four
+    passes of 16 tokens per routing block)."""
+    wl = synth.WORKLOADS[name]
+    print(f"[route_index] full {name}: T={wl.T} E={wl.E} k={wl.k}", flush=True)
+    logits = synth.logits(wl)
+    idx_o, w_o, ref = _oracle_index(wl, logits)
+    idx, w, out, raw = _fused(wl, dev(logits))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(idx), idx_o)
+    assert_weights(host(w), w_o)
+    check_index(out, ref)
+    assert moe.stats_to_dict(raw) == oracle.stats(ref["expert_counts"], wl.R)
+
+
+def test_route_index_without_stats_and_empty():
+    wl = PARITY["zipf"]
+    logits = synth.logits(wl)
+    _, _, ref = _oracle_index(wl, logits)
+    idx, w, out, raw = _fused(wl, dev(logits), stats=False)
+    torch.cuda.synchronize()
+    assert raw is None
+    check_index(out, ref)
+
+    empty = synth.Workload("edge", T=0, H=16, dtype="bf16", E=8, k=2, R=4, W=2, routing="iid",
+                           seed=1)
+    shape = shape_of(empty)
+    out = moe.alloc_dispatch(shape, DEV)
+    for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "wave_offsets"):
+        out[key].fill_(-7)
+    raw = torch.full((moe.STATS_BYTES,), 0xAB, dtype=torch.uint8, device=DEV)
+    idx = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    moe.route_index(torch.empty((0, 8), dtype=torch.float32, device=DEV), shape, out, idx, w,
+                    stats_out=raw)
+    torch.cuda.synchronize()
+    for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "wave_offsets"):
+        assert (host(out[key]) == 0).all(), key
+    st = moe.stats_to_dict(raw)
+    assert st["total"] == 0 and st["rank_gini"] == 0.0 and st["expert_max"] == 0
