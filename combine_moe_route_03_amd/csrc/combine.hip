@@ -3,8 +3,9 @@
 // flow step 4: restore the original order, weight by the gate confidence).
 //
 // Flat over (token, 16-byte column): each thread gathers its column from the k
-// expert rows of its token (all k streaming loads issued before any
-// arithmetic; each expert row is read exactly once), runs the
+// expert rows of its token (all k loads issued before any arithmetic; each
+// expert row is read exactly once, through the caches: the expert stage has
+// just written them and they are still in the Infinity Cache), runs the
 // fp32 fused multiply-add chain in pick order (seeded with -0, the additive
 // identity, so an all -0 sum stays -0), rounds once to the output dtype
 // and writes one 16-byte vector. Lanes of a wave cover consecutive columns of
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__
       const int32_t P = pp[i];
       wt[i] = ww[i];
       ok[i] = (uint32_t)P < nrows;
-      if (ok[i]) v[i] = load_stream(eo + (size_t)P * nvec + col);
+      if (ok[i]) v[i] = eo[(size_t)P * nvec + col];
     }
   }
 
