@@ -98,6 +98,37 @@ def algorithmic_bytes(wl) -> dict:
     return out
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the counters' reading of a plain 1 GiB copy),
+    or None when there is no record or the kernel's sources changed since."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    fields = lambda ln: dict(kv.split("=", 1) for kv in ln.split()[1:])  # noqa: E731
+    scale = next((fields(ln) for ln in lines if ln.startswith("scale ")), None)
+    for ln in lines:
+        if not ln.startswith("traffic "):
+            continue
+        f = fields(ln)
+        if f.get("workload") != workload or f.get("kernel") != kernel or scale is None:
+            continue
+        h = hashlib.sha256()
+        for src in f["sources"].split(","):
+            with open(os.path.join(ROOT, "combine_moe_route_03_amd", "csrc", src), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest()[:16] != f["sha256"]:
+            return None
+        kib = float(f["fetch_kib"]) * float(scale["fetch"]) + float(f["write_kib"]) * float(scale["write"])
+        return int(round(kib * 1024))
+    return None
+
+
 def ffn_flops(wl) -> int:
     return 6 * wl.T * wl.k * wl.H * wl.I  # gate/up (2*2I*H) + down (2*H*I) per row
 
@@ -366,13 +397,14 @@ def main() -> int:
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
                 "achieved": round(gbs(dom, stage_ms[dom]), 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs(dom, stage_ms[dom]) / HBM_PEAK_GBS, 4),
-                "traffic": None, "bytes_per_launch": nbytes[dom],
+                "traffic": stored_traffic(wl.name, kernel_of[dom]), "bytes_per_launch": nbytes[dom],
                 "avg_us": round(stage_ms[dom] * 1e3, 2)}
     if swiglu and stage_ms["expert"] > stage_ms[dom]:
         tf = ffn_flops(wl) / (stage_ms["expert"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": kernel_of["expert"], "achieved": round(tf, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": stored_traffic(wl.name, "ffn_gemm_kernel<gate_up>+ffn_gemm_kernel<down>"),
                     "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
 
     dc_keys = ("dispatch_index", "dispatch_copy", "combine")

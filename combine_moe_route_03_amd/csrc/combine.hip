@@ -4,8 +4,9 @@
 //
 // Flat over (token, 16-byte column): each thread gathers its column from the k
 // expert rows of its token (all k loads issued before any arithmetic; each
-// expert row is read exactly once, through the caches: the expert stage has
-// just written them and they are still in the Infinity Cache), runs the
+// expert row is read exactly once; through the caches when the expert rows fit
+// the cache-reuse budget, as the expert stage has just written them there,
+// streaming otherwise), runs the
 // fp32 fused multiply-add chain in pick order (seeded with -0, the additive
 // identity, so an all -0 sum stays -0), rounds once to the output dtype
 // and writes one 16-byte vector. Lanes of a wave cover consecutive columns of
@@ -18,7 +19,7 @@ namespace {
 
 constexpr int kBlock = 256;
 
-template <int KMAX, bool kBF16>
+template <int KMAX, bool kBF16, bool kCacheIn>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__ eo,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ pos, int k,
@@ -42,7 +43,10 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__
       const int32_t P = pp[i];
       wt[i] = ww[i];
       ok[i] = (uint32_t)P < nrows;
-      if (ok[i]) v[i] = eo[(size_t)P * nvec + col];
+      if (ok[i]) {
+        const v4u* src = eo + (size_t)P * nvec + col;
+        v[i] = kCacheIn ? *src : load_stream(src);
+      }
     }
   }
 
@@ -82,11 +86,13 @@ hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int
   const unsigned grid = (total + kBlock - 1) / kBlock;
   const v4u* in = static_cast<const v4u*>(eo);
   v4u* out = static_cast<v4u*>(y);
-  if (bf16)
-    return launch(combine_kernel<KMAX, true>, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec,
-                  total, nrows, out);
-  return launch(combine_kernel<KMAX, false>, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec,
-                total, nrows, out);
+  // the expert rows (nrows x nvec vectors) decide the policy, as in the expert stage
+  const bool cache = (int64_t)nrows * nvec * 16 <= kCacheReuseBytes;
+  auto run = [&](auto kernel) {
+    return launch(kernel, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec, total, nrows, out);
+  };
+  if (bf16) return cache ? run(combine_kernel<KMAX, true, true>) : run(combine_kernel<KMAX, true, false>);
+  return cache ? run(combine_kernel<KMAX, false, true>) : run(combine_kernel<KMAX, false, false>);
 }
 
 }  // namespace

@@ -4,8 +4,8 @@
 // rows), so a row's expert is found by binary search over the bucket starts
 // staged in LDS. Each thread moves kU 16-byte vectors (all loads first). The
 // send rows are read once (streaming loads); the output rows are stored through
-// the caches, so the combine that reads them next finds them in the 256 MB
-// Infinity Cache (measured: the pair is faster than with streaming stores).
+// the caches when the whole output fits the cache-reuse budget (the combine
+// then finds them in the Infinity Cache), streamed otherwise.
 #include "device.h"
 #include "launch.h"
 
@@ -29,7 +29,7 @@ __device__ __forceinline__ v4u scale_vec(v4u v, float sc) {
   return o;
 }
 
-template <bool kBF16>
+template <bool kBF16, bool kCacheOut>
 __global__ __launch_bounds__(kBlock) void expert_scale_kernel(
     const v4u* __restrict__ in, uint32_t nvec, uint32_t total, int E, int R, int W,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ cnts, v4u* __restrict__ out) {
@@ -63,7 +63,9 @@ __global__ __launch_bounds__(kBlock) void expert_scale_kernel(
       else hi = mid - 1;
     }
     if (n < start[lo] || n >= stop[lo]) continue;  // row outside every bucket
-    out[q] = scale_vec<kBF16>(v[u], (float)(bexp[lo] + 1));
+    const v4u o = scale_vec<kBF16>(v[u], (float)(bexp[lo] + 1));
+    if constexpr (kCacheOut) out[q] = o;
+    else store_stream(out + q, o);
   }
 }
 
@@ -79,11 +81,13 @@ hipError_t launch_expert_scale(const void* in, int dtype, int64_t rows, int64_t 
   const unsigned grid = (total + kBlock * kU - 1) / (kBlock * kU);
   const v4u* src = static_cast<const v4u*>(in);
   v4u* dst = static_cast<v4u*>(out);
-  if (bf16)
-    return launch(expert_scale_kernel<true>, dim3(grid), dim3(kBlock), 0, s, src, nvec, total, E,
-                  R, W, expert_offsets, expert_counts, dst);
-  return launch(expert_scale_kernel<false>, dim3(grid), dim3(kBlock), 0, s, src, nvec, total, E, R,
-                W, expert_offsets, expert_counts, dst);
+  const bool cache = (int64_t)total * 16 <= kCacheReuseBytes;
+  auto go = [&](auto kernel) {
+    return launch(kernel, dim3(grid), dim3(kBlock), 0, s, src, nvec, total, E, R, W,
+                  expert_offsets, expert_counts, dst);
+  };
+  if (bf16) return cache ? go(expert_scale_kernel<true, true>) : go(expert_scale_kernel<true, false>);
+  return cache ? go(expert_scale_kernel<false, true>) : go(expert_scale_kernel<false, false>);
 }
 
 }  // namespace moe

@@ -44,6 +44,14 @@ inline int64_t num_chunks(int64_t npicks, int E) {
   return (npicks + c - 1) / c;
 }
 
+// ----------------------------------------------------------- cache policy
+// The expert rows are written by one kernel and gathered by the combine right
+// after. While that buffer fits comfortably in the 256 MB Infinity Cache (at
+// most half of it) both sides go through the caches and the combine reads it
+// from there; beyond that both stream (non-temporal), which measured faster
+// for buffers of a few GB.
+constexpr int64_t kCacheReuseBytes = int64_t(128) << 20;
+
 // ------------------------------------------------------------ kernel timing
 // Optional per-thread timing events (benchmark hook; see
 // moe_set_timing_events): while armed, the i-th kernel launched (i < n) records
