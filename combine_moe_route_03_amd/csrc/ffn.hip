@@ -41,6 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kXCD = 8;
+constexpr int kGroupM = 1;  // m-tiles per rasterisation patch (2, 4, 8 measured no faster)
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
@@ -82,7 +83,7 @@ template <bool kGateUp, int BM, int BN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, const uint16_t* __restrict__ Bw, int64_t bstride,
-    int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles) {
+    int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int gm) {
   constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
   constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave per K step
   constexpr int kStage = (BM + BN) * kBK;    // elements of one A + B stage
@@ -95,11 +96,14 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int wm = wid >> 1, wn = wid & 1;
 
-  // ---- which tile. Tiles are numbered m-major (all n-tiles of m-tile 0, then
-  // of m-tile 1, ...) and each XCD takes one contiguous share of that order, so
-  // an XCD reads its share of the rows once and the weights of the few experts
-  // those rows belong to; blocks of one XCD share tiles through its L2.
-  // gridDim.x is a multiple of kXCD with at least ceil(tiles / kXCD) slots per XCD.
+  // ---- which tile. The m-tiles (every expert's rows in BM-row tiles, in
+  // expert order) are split into 8 contiguous shares, one per XCD, so an XCD
+  // reads its rows once and the weights of the few experts they belong to
+  // through its own L2. Inside a share, tiles go in patches of GM m-tiles:
+  // n-tile 0 of the patch's m-tiles, then n-tile 1, ...; the blocks resident
+  // on an XCD at one time then cover a GM x (32/GM) patch, re-using each B
+  // tile GM times and each A tile 32/GM times from L2.
+  // gridDim.x = 8 * (max m-tiles per XCD) * ntiles.
   const int xcd = blockIdx.x % kXCD, slot = blockIdx.x / kXCD;
   int ntile = 0;
   if (wid == 0) {
@@ -115,12 +119,18 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
       const int y = __shfl_up(incl, o);
       if (lane >= o) incl += y;
     }
-    const int total = __shfl(incl, kWave - 1) * ntiles;  // tiles that exist
-    const int share = (total + kXCD - 1) / kXCD;         // <= slots per XCD
-    const int logical = xcd * share + slot;
-    const bool live = slot < share && logical < total;
-    const int mtg = live ? logical / ntiles : -1;
-    ntile = live ? logical - mtg * ntiles : 0;
+    const int MT = __shfl(incl, kWave - 1);    // m-tiles that exist
+    const int mpx = (MT + kXCD - 1) / kXCD;    // m-tiles per XCD share
+    const int m_lo = xcd * mpx;
+    const int m_cnt = MT - m_lo < mpx ? (MT - m_lo > 0 ? MT - m_lo : 0) : mpx;
+    const bool live = slot < m_cnt * ntiles;
+    int mtg = -1;
+    if (live) {
+      const int grp = slot / (gm * ntiles), r = slot - grp * gm * ntiles;
+      const int gh = (m_cnt - grp * gm < gm) ? m_cnt - grp * gm : gm;  // m-tiles in this patch
+      ntile = r / gh;
+      mtg = m_lo + grp * gm + (r - ntile * gh);
+    }
     int base = incl - mine;
     if (live && mtg >= base && mtg < incl) {
       for (int e = e0; e < e1; ++e) {
@@ -307,20 +317,19 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, const in
                    void* out, hipStream_t s) {
   const int mtb = (int)((rows + BM - 1) / BM + E);  // each expert adds at most one partial tile
   auto grid_of = [&](int ntiles) {
-    const int64_t n = (int64_t)ntiles * mtb;
-    return (unsigned)((n + kXCD - 1) / kXCD * kXCD);
+    return (unsigned)(kXCD * ((mtb + kXCD - 1) / kXCD) * ntiles);
   };
   const int nt1 = I / (BN / 2);
   hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E,
                           static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
-                          static_cast<uint16_t*>(hbuf), (int64_t)I, nt1);
+                          static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, kGroupM);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
   return launch(ffn_gemm_kernel<false, BM, BN, OCC>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E,
                 static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
-                static_cast<uint16_t*>(out), (int64_t)H, nt2);
+                static_cast<uint16_t*>(out), (int64_t)H, nt2, kGroupM);
 }
 
 }  // namespace
