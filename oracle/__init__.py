@@ -74,6 +74,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_positions.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                        _i32p, _i32p, _i32p]
         L.oracle_dispatch_copy.argtypes = [_vp, ctypes.c_int64, _i32p, ctypes.c_int64, _vp]
+        L.oracle_expert_capacity.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_int64,
+                                             ctypes.c_int32]
+        L.oracle_expert_capacity.restype = ctypes.c_int32
+        L.oracle_dispatch_capacity.argtypes = [_vp, ctypes.c_int64, _i32p, ctypes.c_int64,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, _i32p, _i32p,
+                                               _i32p, _i32p, _i32p, _i32p, _i32p, _vp]
         L.oracle_expert_scale.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                           _i32p, _i32p, _vp]
         L.oracle_combine_f64.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
@@ -171,6 +178,34 @@ def dispatch(x: np.ndarray, idx: np.ndarray, E: int, R: int, W: int):
     send = dispatch_copy(x, row_token, nrows)
     return dict(expert_counts=ec, rank_counts=rc, expert_offsets=eo, rank_offsets=ro,
                 wave_offsets=wo, pos=pos, row_token=row_token, send_buf=send, nrows=nrows)
+
+
+def expert_capacity(k: int, f: float, T: int, E: int) -> int:
+    """Rows per expert for capacity factor f (eq. (3), rounded up)."""
+    return int(lib().oracle_expert_capacity(k, f, T, E))
+
+
+def dispatch_capacity(x: np.ndarray, idx: np.ndarray, E: int, R: int, W: int, cap: int):
+    """Capacity-factor dispatch outputs (buckets of exactly cap rows, zero padding)."""
+    x = np.ascontiguousarray(x)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    H = x.shape[1]
+    rows = E * cap
+    kept = np.empty(E, np.int32)
+    eo = np.empty(E, np.int32)
+    rc = np.empty(W * R, np.int32)
+    ro = np.empty(W * R, np.int32)
+    wo = np.empty(W + 1, np.int32)
+    pos = np.empty((T, k), np.int32)
+    rt = np.empty(max(rows, 1), np.int32)
+    send = np.empty((max(rows, 1), H), x.dtype)
+    lib().oracle_dispatch_capacity(x.ctypes.data, H * x.itemsize, _p(idx, _i32p), T, k, E, R, W,
+                                   cap, _p(kept, _i32p), _p(eo, _i32p), _p(rc, _i32p),
+                                   _p(ro, _i32p), _p(wo, _i32p), _p(pos, _i32p), _p(rt, _i32p),
+                                   send.ctypes.data)
+    return dict(kept_counts=kept, expert_offsets=eo, rank_counts=rc, rank_offsets=ro,
+                wave_offsets=wo, pos=pos, row_token=rt[:rows], send_buf=send[:rows], rows=rows)
 
 
 def expert_scale(send_buf: np.ndarray, expert_offsets: np.ndarray, expert_counts: np.ndarray):

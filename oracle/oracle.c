@@ -169,6 +169,61 @@ void oracle_dispatch_copy(const void* x, int64_t row_bytes,
            (size_t)row_bytes);
 }
 
+/* ---------------------------------------------------- capacity dispatch */
+
+int32_t oracle_expert_capacity(int32_t k, double f, int64_t T, int32_t E) {
+  if (!(f >= 0.0) || E <= 0) return -1;
+  double ec = ceil((double)k * f * (double)T / (double)E);
+  if (ec > 2147483647.0) return -1;
+  return (int32_t)ec;
+}
+
+void oracle_dispatch_capacity(const void* x, int64_t row_bytes, const int32_t* idx,
+                              int64_t T, int32_t k, int32_t E, int32_t R, int32_t W,
+                              int32_t cap, int32_t* kept_counts,
+                              int32_t* expert_offsets, int32_t* rank_counts,
+                              int32_t* rank_offsets, int32_t* wave_offsets,
+                              int32_t* pos, int32_t* row_token, void* send_buf) {
+  int32_t L = E / R;
+  int64_t rows = (int64_t)E * cap;
+  /* bucket starts: walk the buckets in (wave, rank, slot) order, cap rows each */
+  int32_t j = 0;
+  for (int32_t w = 0; w < W; ++w) {
+    wave_offsets[w] = j * cap;
+    for (int32_t r = 0; r < R; ++r) {
+      int32_t first = j, n = 0;
+      for (int32_t s = 0; s < L; ++s) {
+        int32_t e = r * L + s;
+        if (wave_of(e, L, W) != w) continue;
+        expert_offsets[e] = j * cap;
+        ++j;
+        ++n;
+      }
+      rank_offsets[w * R + r] = first * cap;
+      rank_counts[w * R + r] = n * cap;
+    }
+  }
+  wave_offsets[W] = (int32_t)rows;
+  /* padding everywhere first; kept rows overwrite it */
+  for (int64_t n = 0; n < rows; ++n) row_token[n] = -1;
+  memset(send_buf, 0, (size_t)(rows * row_bytes));
+  for (int32_t e = 0; e < E; ++e) kept_counts[e] = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t e = idx[t * k + i];
+      if (e < 0 || e >= E || kept_counts[e] >= cap) {
+        pos[t * k + i] = -1;
+        continue;
+      }
+      int32_t p = expert_offsets[e] + kept_counts[e]++;
+      pos[t * k + i] = p;
+      row_token[p] = (int32_t)t;
+      memcpy((char*)send_buf + (int64_t)p * row_bytes, (const char*)x + t * row_bytes,
+             (size_t)row_bytes);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------ expert */
 
 void oracle_expert_scale(const void* in, int32_t dtype, int64_t H, int32_t E,

@@ -65,6 +65,31 @@ void oracle_dispatch_copy(const void* x, int64_t row_bytes,
                           const int32_t* row_token, int64_t nrows,
                           void* send_buf);
 
+/* Expert capacity, MoE systems survey section 1.2 item 2), eq. (3): the rows
+ * one expert may take, k * f * T / E for capacity factor f, rounded up to a
+ * whole row (the equation is garbled in extraction; the fraction bar is read
+ * under T / E). Evaluated in double in the order ((k * f) * T) / E. Returns -1
+ * for f < 0 or a result that does not fit int32. */
+int32_t oracle_expert_capacity(int32_t k, double f, int64_t T, int32_t E);
+
+/* Capacity-factor dispatch (survey section 1.2 eq. (3) and EP flow step 2:
+ * samples beyond an expert's capacity are dropped, unused capacity is padded
+ * with zeros). Every expert bucket has exactly cap rows; bucket j of the
+ * (wave, rank, slot) order starts at row j * cap. An expert keeps its first
+ * cap picks in (token, pick) order; later picks are dropped (pos = -1), as are
+ * picks with ids outside [0, E). Outputs:
+ *   kept_counts[e] = min(c[e], cap); expert_offsets[e] = j(e) * cap;
+ *   rank_counts[w*R+r], rank_offsets[w*R+r], wave_offsets[W+1]: whole buckets
+ *   (padding included: it is part of what each destination receives);
+ *   pos[t][k]; row_token[E*cap] (-1 on padding rows); send_buf[E*cap][row]
+ *   (x rows, zero bytes on padding rows). */
+void oracle_dispatch_capacity(const void* x, int64_t row_bytes, const int32_t* idx,
+                              int64_t T, int32_t k, int32_t E, int32_t R, int32_t W,
+                              int32_t cap, int32_t* kept_counts,
+                              int32_t* expert_offsets, int32_t* rank_counts,
+                              int32_t* rank_offsets, int32_t* wave_offsets,
+                              int32_t* pos, int32_t* row_token, void* send_buf);
+
 /* Identity-scaled experts: out[n] = round_dtype((e(n) + 1) * in[n]) where
  * e(n) is the expert whose bucket holds row n. */
 void oracle_expert_scale(const void* in, int32_t dtype, int64_t H, int32_t E,
