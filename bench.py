@@ -78,6 +78,9 @@ def parse_args():
                     help="also time K steps replayed from one captured HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="separate route / dispatch_index / stats calls (7 kernels a step)")
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="capacity-factor dispatch (buckets of ceil(k*f*T/E) rows, overflow "
+                         "dropped, zero padding) instead of count-sized buckets")
     return ap.parse_args()
 
 
@@ -127,6 +130,17 @@ def stored_traffic(workload: str, kernel: str):
         kib = float(f["fetch_kib"]) * float(scale["fetch"]) + float(f["write_kib"]) * float(scale["write"])
         return int(round(kib * 1024))
     return None
+
+
+def capacity_bytes(wl, cap: int, kept: int) -> dict:
+    """The byte model with capacity-factor buckets: the copy writes every bucket
+    row (kept rows and zero padding); experts and combine touch the kept rows."""
+    T, H, E, k, b = wl.T, wl.H, wl.E, wl.k, wl.elem_bytes
+    out = algorithmic_bytes(wl)
+    out["dispatch_copy"] = T * H * b + E * cap * H * b + 4 * T * k
+    out["expert"] = 2 * kept * H * b
+    out["combine"] = kept * H * b + 8 * T * k + T * H * b
+    return out
 
 
 def ffn_flops(wl) -> int:
@@ -262,6 +276,33 @@ def main() -> int:
     if args.unfused:
         calls.append((L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream),
                       [("stats", "stats_kernel")]))
+    cap = kept = None
+    if args.capacity_factor is not None:
+        if swiglu:
+            print("--capacity-factor runs the identity-scaled experts only", file=sys.stderr)
+            return 2
+        cap = moe.expert_capacity(k, args.capacity_factor, T, E)
+        cbuf = moe.alloc_dispatch_capacity(shape, cap, dev)
+        ceo = torch.empty_like(cbuf["send_buf"])
+        rows = cbuf["rows"]
+        calls = [
+            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
+             [("route", "route_kernel")]),
+            (L.moe_dispatch_capacity, (
+                shp, cap, P(x), P(topk_idx), P(cbuf["send_buf"]), P(cbuf["kept_counts"]),
+                P(cbuf["expert_offsets"]), P(cbuf["rank_counts"]), P(cbuf["rank_offsets"]),
+                P(cbuf["wave_offsets"]), P(cbuf["pos"]), P(cbuf["row_token"]),
+                P(cbuf["workspace"]), cbuf["workspace"].numel(), stream),
+             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(capacity)"),
+              ("dispatch_copy", "copy_kernel"), ("dispatch_copy", "pad_kernel")]),
+            (L.moe_expert_scale_rows, (shp, rows, P(cbuf["send_buf"]), P(cbuf["expert_offsets"]),
+                                       P(cbuf["kept_counts"]), P(ceo), stream),
+             [("expert", "expert_scale_kernel")]),
+            (L.moe_combine_rows, (shp, rows, P(ceo), P(topk_w), P(cbuf["pos"]), P(y), stream),
+             [("combine", "combine_kernel")]),
+            (L.moe_stats, (P(cbuf["kept_counts"]), E, R, P(stats_raw), stream),
+             [("stats", "stats_kernel")]),
+        ]
     STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
     kernel_of = {st: "+".join(kn for c in calls for g, kn in c[2] if g == st) for st in STAGES_RUN}
 
@@ -322,6 +363,9 @@ def main() -> int:
     wall_instr = time.perf_counter() - t0
     stage_ms = stage_means(evs)
     nbytes = algorithmic_bytes(wl)
+    if cap is not None:
+        kept = int(cbuf["kept_counts"].sum().item())
+        nbytes = capacity_bytes(wl, cap, kept)
 
     graph_wall = None
     if args.graph:
@@ -447,6 +491,11 @@ def main() -> int:
     }
     if swiglu:
         result["config"]["I"] = wl.I
+    if cap is not None:
+        result["config"]["step"] = ("route+dispatch_capacity(count,place,copy,pad)"
+                                    "+expert+combine+stats")
+        result["config"].update(capacity_factor=args.capacity_factor, capacity=cap,
+                                kept_picks=kept, dropped_picks=T * k - kept)
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}

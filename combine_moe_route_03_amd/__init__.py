@@ -7,8 +7,9 @@ library must be built (``__graft_entry__.build()``); importing the functions
 without it raises, there is no fallback.
 
 Entry points mirror include/moe_route.h: ``route``, ``dispatch_index``,
-``route_index``, ``dispatch_copy``, ``dispatch``, ``expert_scale``,
-``expert_swiglu``, ``combine``, ``stats``.
+``route_index``, ``dispatch_copy``, ``dispatch``, ``dispatch_capacity``,
+``expert_scale``, ``expert_scale_rows``, ``expert_swiglu``, ``combine``,
+``combine_rows``, ``stats``.
 """
 from __future__ import annotations
 
@@ -56,6 +57,11 @@ SIGNATURES = {
     "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_expert_scale_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_expert_capacity": ([_i32, ctypes.c_double, _i32, _i32], ctypes.c_int32),
+    "moe_dispatch_capacity": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_swiglu_workspace_bytes": ([_shp, _i32], ctypes.c_size_t),
     "moe_expert_swiglu": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                           ctypes.c_int),
@@ -218,6 +224,65 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
         _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
         "moe_dispatch")
     return out
+
+
+# ------------------------------------------------------- capacity-factor path
+
+def expert_capacity(k: int, f: float, T: int, E: int) -> int:
+    """Rows per expert for capacity factor f (ceil(k*f*T/E)); -1 if invalid."""
+    return int(lib().moe_expert_capacity(k, f, T, E))
+
+
+def alloc_dispatch_capacity(shape: Shape, capacity: int, device) -> dict:
+    E, R, W, H, T, k = shape.E, shape.R, shape.W, shape.H, shape.T, shape.k
+    i32 = torch.int32
+    rows = E * capacity
+    return dict(
+        send_buf=_empty((rows, H), shape.dtype, device), kept_counts=_empty((E,), i32, device),
+        expert_offsets=_empty((E,), i32, device), rank_counts=_empty((W * R,), i32, device),
+        rank_offsets=_empty((W * R,), i32, device), wave_offsets=_empty((W + 1,), i32, device),
+        pos=_empty((T, k), i32, device), row_token=_empty((max(rows, 1),), i32, device),
+        workspace=_empty((max(dispatch_workspace_bytes(shape), 1),), torch.uint8, device),
+        rows=rows)
+
+
+def dispatch_capacity(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
+                      capacity: int, out: dict | None = None) -> dict:
+    """Capacity-factor dispatch: buckets of exactly `capacity` rows, overflow
+    dropped in token order, zero padding (four launches)."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    shape = Shape(T, H, E, k, R, W, x.dtype)
+    out = alloc_dispatch_capacity(shape, capacity, x.device) if out is None else out
+    sh = shape.c()
+    _check(lib().moe_dispatch_capacity(
+        ctypes.byref(sh), capacity, _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]),
+        _ptr(out["kept_counts"]), _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
+        _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]), _ptr(out["pos"]),
+        _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
+        "moe_dispatch_capacity")
+    return out
+
+
+def expert_scale_rows(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
+                      expert_counts: torch.Tensor, shape: Shape,
+                      expert_out: torch.Tensor | None = None) -> torch.Tensor:
+    expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
+    sh = shape.c()
+    _check(lib().moe_expert_scale_rows(ctypes.byref(sh), send_buf.shape[0], _ptr(send_buf),
+                                       _ptr(expert_offsets), _ptr(expert_counts),
+                                       _ptr(expert_out), _stream()), "moe_expert_scale_rows")
+    return expert_out
+
+
+def combine_rows(expert_out: torch.Tensor, topk_w: torch.Tensor, pos: torch.Tensor, shape: Shape,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    y = _empty((shape.T, shape.H), shape.dtype, expert_out.device) if y is None else y
+    sh = shape.c()
+    _check(lib().moe_combine_rows(ctypes.byref(sh), expert_out.shape[0], _ptr(expert_out),
+                                  _ptr(topk_w), _ptr(pos), _ptr(y), _stream()),
+           "moe_combine_rows")
+    return y
 
 
 # ----------------------------------------------------------- expert / combine

@@ -4,6 +4,8 @@
 #include "../../include/moe_route.h"
 #include "launch.h"
 
+#include <cmath>
+
 namespace {
 
 constexpr int64_t kIndexLimit = int64_t(1) << 31;  // flat 32-bit index spaces of the row kernels
@@ -167,7 +169,7 @@ int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_i
   return status_of(moe::launch_place_chunks(
       topk_idx, npicks, tpb * shape->k, (int)route_index_blocks(shape), shape->k, shape->E,
       shape->R, shape->W, hist, expert_counts, expert_offsets, rank_counts, rank_offsets,
-      wave_offsets, pos, row_token, stats, s));
+      wave_offsets, pos, row_token, stats, -1, s));
 }
 
 int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos, void* send_buf,
@@ -178,7 +180,8 @@ int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos,
   if (st != MOE_OK) return st;
   const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
   return status_of(
-      moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, send_buf, as_stream(stream)));
+      moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, int64_t(shape->T) * shape->k,
+                       send_buf, as_stream(stream)));
 }
 
 int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx, void* send_buf,
@@ -200,19 +203,28 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
   return moe_dispatch_copy(shape, x, pos, send_buf, stream);
 }
 
-int moe_expert_scale(const moe_shape* shape, const void* send_buf, const int32_t* expert_offsets,
-                     const int32_t* expert_counts, void* expert_out, moe_stream_t stream) {
+int moe_expert_scale_rows(const moe_shape* shape, int64_t rows, const void* send_buf,
+                          const int32_t* expert_offsets, const int32_t* expert_counts,
+                          void* expert_out, moe_stream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (rows < 0 || rows * (int64_t(shape->H) * elem_bytes(shape->dtype) / 16) >= kIndexLimit)
+    return MOE_ERR_ARG;
   if (!expert_offsets || !expert_counts) return MOE_ERR_ARG;
-  if (shape->T > 0 && (!send_buf || !expert_out)) return MOE_ERR_ARG;
+  if (rows > 0 && (!send_buf || !expert_out)) return MOE_ERR_ARG;
   if (!aligned(send_buf, 16) || !aligned(expert_out, 16) || !aligned(expert_offsets, 4) ||
       !aligned(expert_counts, 4))
     return MOE_ERR_ALIGN;
-  const int64_t rows = int64_t(shape->T) * shape->k;
   return status_of(moe::launch_expert_scale(send_buf, shape->dtype, rows, shape->H, shape->E,
                                             shape->R, shape->W, expert_offsets, expert_counts,
                                             expert_out, as_stream(stream)));
+}
+
+int moe_expert_scale(const moe_shape* shape, const void* send_buf, const int32_t* expert_offsets,
+                     const int32_t* expert_counts, void* expert_out, moe_stream_t stream) {
+  if (!shape) return MOE_ERR_ARG;
+  return moe_expert_scale_rows(shape, int64_t(shape->T) * shape->k, send_buf, expert_offsets,
+                               expert_counts, expert_out, stream);
 }
 
 size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I) {
@@ -248,15 +260,68 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
                                              workspace, expert_out, as_stream(stream)));
 }
 
-int moe_combine(const moe_shape* shape, const void* expert_out, const float* topk_w,
-                const int32_t* pos, void* y, moe_stream_t stream) {
+int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_out,
+                     const float* topk_w, const int32_t* pos, void* y, moe_stream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (rows < 0 || rows * (int64_t(shape->H) * elem_bytes(shape->dtype) / 16) >= kIndexLimit)
+    return MOE_ERR_ARG;
   if (shape->T > 0 && (!expert_out || !topk_w || !pos || !y)) return MOE_ERR_ARG;
   if (!aligned(expert_out, 16) || !aligned(y, 16) || !aligned(topk_w, 4) || !aligned(pos, 4))
     return MOE_ERR_ALIGN;
   return status_of(moe::launch_combine(expert_out, shape->dtype, topk_w, pos, shape->T, shape->k,
-                                       shape->H, y, as_stream(stream)));
+                                       shape->H, rows, y, as_stream(stream)));
+}
+
+int moe_combine(const moe_shape* shape, const void* expert_out, const float* topk_w,
+                const int32_t* pos, void* y, moe_stream_t stream) {
+  if (!shape) return MOE_ERR_ARG;
+  return moe_combine_rows(shape, int64_t(shape->T) * shape->k, expert_out, topk_w, pos, y,
+                          stream);
+}
+
+int32_t moe_expert_capacity(int32_t k, double f, int32_t T, int32_t E) {
+  if (k < 1 || T < 0 || E < 1 || !(f >= 0.0)) return -1;
+  const double ec = std::ceil(double(k) * f * double(T) / double(E));
+  return ec > 2147483647.0 ? -1 : int32_t(ec);
+}
+
+int moe_dispatch_capacity(const moe_shape* shape, int32_t capacity, const void* x,
+                          const int32_t* topk_idx, void* send_buf, int32_t* kept_counts,
+                          int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                          int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
+                          void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const int64_t nvec = int64_t(shape->H) * elem_bytes(shape->dtype) / 16;
+  const int64_t rows = int64_t(shape->E) * capacity;
+  if (capacity < 0 || rows * nvec >= kIndexLimit) return MOE_ERR_ARG;
+  if (!kept_counts || !expert_offsets || !rank_counts || !rank_offsets || !wave_offsets ||
+      !workspace)
+    return MOE_ERR_ARG;
+  if (shape->T > 0 && (!topk_idx || !pos || !x)) return MOE_ERR_ARG;
+  if (rows > 0 && (!send_buf || !row_token)) return MOE_ERR_ARG;
+  const void* ptrs[] = {topk_idx, kept_counts, expert_offsets, rank_counts, rank_offsets,
+                        wave_offsets, pos, workspace};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+  if (workspace_bytes_given < workspace_bytes(shape)) return MOE_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(row_token, 4)) return MOE_ERR_ALIGN;
+  const int64_t npicks = int64_t(shape->T) * shape->k;
+  hipStream_t s = as_stream(stream);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  st = status_of(moe::launch_count(topk_idx, npicks, shape->E, hist, s));
+  if (st != MOE_OK) return st;
+  st = status_of(moe::launch_place_chunks(
+      topk_idx, npicks, moe::chunk_picks(npicks, shape->E), (int)moe::num_chunks(npicks, shape->E),
+      shape->k, shape->E, shape->R, shape->W, hist, kept_counts, expert_offsets, rank_counts,
+      rank_offsets, wave_offsets, pos, row_token, nullptr, capacity, s));
+  if (st != MOE_OK) return st;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  st = status_of(moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, rows, send_buf, s));
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_pad(shape->E, shape->R, shape->W, capacity, kept_counts, row_bytes,
+                                   send_buf, row_token, s));
 }
 
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R, moe_stats_t* out,

@@ -98,12 +98,12 @@ hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int
 }  // namespace
 
 hipError_t launch_combine(const void* expert_out, int dtype, const float* w, const int32_t* pos,
-                          int T, int k, int64_t H, void* y, hipStream_t s) {
+                          int T, int k, int64_t H, int64_t eo_rows, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const bool bf16 = dtype == 1;
   const uint32_t nvec = (uint32_t)(H * (bf16 ? 2 : 4) / 16);
   const uint32_t total = (uint32_t)T * nvec;
-  const uint32_t nrows = (uint32_t)T * (uint32_t)k;
+  const uint32_t nrows = (uint32_t)eo_rows;
   if (k <= 2) return go<2>(expert_out, bf16, w, pos, k, nvec, total, nrows, y, s);
   if (k <= 4) return go<4>(expert_out, bf16, w, pos, k, nvec, total, nrows, y, s);
   if (k <= 8) return go<8>(expert_out, bf16, w, pos, k, nvec, total, nrows, y, s);

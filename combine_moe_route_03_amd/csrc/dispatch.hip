@@ -61,7 +61,10 @@ __global__ __launch_bounds__(kB) void place_kernel(
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
     int32_t* __restrict__ pos, int32_t* __restrict__ row_token, moe_stats_t* __restrict__ stats,
-    int sblock) {
+    int sblock, int cap) {
+  // cap >= 0: capacity-factor layout (every bucket exactly cap rows, an expert
+  // keeps its first cap picks in token order, later ones are dropped);
+  // cap < 0: buckets sized by the counts.
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
@@ -74,6 +77,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
   const int b = blockIdx.x;
   const int L = E / R, LW = L / W;
   const int ep = 1 << elog;        // E rounded up to a power of two
+  const int64_t rows = cap < 0 ? npicks : (int64_t)E * cap;  // rows of the send buffer
   const int nslice = kB >> elog;   // row slices of the hist matrix
   // This chunk's first batch of ids, loaded now so that its latency overlaps
   // the histogram read and the scans below.
@@ -125,9 +129,9 @@ __global__ __launch_bounds__(kB) void place_kernel(
     return;
   }
 
-  // 2. Exclusive scan of cnt over buckets in (wave, rank, slot) order; thread j
-  //    owns bucket j.
-  const int cj = (tid < E) ? cnt[bucket_expert(tid, R, L, LW)] : 0;
+  // 2. Exclusive scan of the bucket sizes in (wave, rank, slot) order; thread j
+  //    owns bucket j. With a capacity every bucket is cap rows long.
+  const int cj = (tid < E) ? (cap >= 0 ? cap : cnt[bucket_expert(tid, R, L, LW)]) : 0;
   int incl = cj;
   for (int o = 1; o < kWave; o <<= 1) {
     const int y = __shfl_up(incl, o);
@@ -146,19 +150,22 @@ __global__ __launch_bounds__(kB) void place_kernel(
 
   if (b == 0) {
     if (tid < E) {
-      expert_counts[tid] = cnt[tid];
+      expert_counts[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];  // rows kept
       expert_offsets[tid] = off[tid];
     }
     for (int q = tid; q < W * R; q += kB) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
       int s = 0;
-      for (int j = q * LW; j < q * LW + LW; ++j) s += cnt[bucket_expert(j, R, L, LW)];
+      for (int j = q * LW; j < q * LW + LW; ++j)
+        s += cap >= 0 ? cap : cnt[bucket_expert(j, R, L, LW)];
       rank_counts[q] = s;
       rank_offsets[q] = off[bucket_expert(q * LW, R, L, LW)];
     }
     for (int w = tid; w <= W; w += kB)
       wave_offsets[w] = (w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total;
   }
-  if (tid < E) run[tid] += off[tid];
+  // run[e]: picks of expert e before this chunk; with a capacity the rank
+  // inside the bucket decides between a row and a drop, so it stays relative.
+  if (tid < E && cap < 0) run[tid] += off[tid];
   __syncthreads();
 
   // 3. Stable ranks inside the chunk, 1024 picks per batch.
@@ -182,9 +189,10 @@ __global__ __launch_bounds__(kB) void place_kernel(
     if (valid) {
       int before = 0;
       for (int q = 0; q < wid; ++q) before += wcnt[q][e];
-      const int P = run[e] + before + rk;
+      const int rel = run[e] + before + rk;
+      const int P = cap < 0 ? rel : (rel < cap ? off[e] + rel : -1);
       pos[p] = P;
-      if ((uint64_t)P < (uint64_t)npicks) row_token[P] = (int32_t)(p / k);
+      if (P >= 0 && (int64_t)P < rows) row_token[P] = (int32_t)(p / k);
     } else if (p < p1) {
       pos[p] = -1;
     }
@@ -217,6 +225,21 @@ __global__ __launch_bounds__(kCopyBlock) void copy_kernel(const v4u* __restrict_
   }
 }
 
+// Zero padding of the capacity layout: block j fills bucket j's rows past the
+// kept ones with zero vectors and marks them row_token = -1.
+__global__ __launch_bounds__(kCopyBlock) void pad_kernel(int E, int R, int W, int cap,
+                                                         const int32_t* __restrict__ kept,
+                                                         uint32_t nvec, v4u* __restrict__ send,
+                                                         int32_t* __restrict__ row_token) {
+  const int j = blockIdx.x, L = E / R, LW = L / W;
+  const int e = bucket_expert(j, R, L, LW);
+  const int64_t r0 = (int64_t)j * cap + kept[e], r1 = (int64_t)(j + 1) * cap;
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += kCopyBlock) row_token[r] = -1;
+  const int64_t n = (r1 - r0) * nvec;
+  for (int64_t q = threadIdx.x; q < n; q += kCopyBlock)
+    send[r0 * nvec + q] = v4u{0u, 0u, 0u, 0u};
+}
+
 int ilog2_ceil(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -237,14 +260,14 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
                                int E, int R, int W, const int32_t* hist, int32_t* expert_counts,
                                int32_t* expert_offsets, int32_t* rank_counts,
                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
-                               int32_t* row_token, moe_stats_t* stats, hipStream_t s) {
+                               int32_t* row_token, moe_stats_t* stats, int cap, hipStream_t s) {
   // With no picks one block still runs to publish zero counts and offsets; the
   // statistics block, if any, comes after the placing blocks.
   const int sblock = nb == 0 ? 1 : nb;
   const unsigned grid = (unsigned)sblock + (stats != nullptr ? 1u : 0u);
   return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, chunk, nb, k, E,
                 ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
-                rank_offsets, wave_offsets, pos, row_token, stats, sblock);
+                rank_offsets, wave_offsets, pos, row_token, stats, sblock, cap);
 }
 
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
@@ -253,18 +276,25 @@ hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R,
                         int32_t* pos, int32_t* row_token, hipStream_t s) {
   return launch_place_chunks(idx, npicks, chunk_picks(npicks, E), (int)num_chunks(npicks, E), k,
                              E, R, W, hist, expert_counts, expert_offsets, rank_counts,
-                             rank_offsets, wave_offsets, pos, row_token, nullptr, s);
+                             rank_offsets, wave_offsets, pos, row_token, nullptr, -1, s);
 }
 
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
-                       void* send, hipStream_t s) {
+                       int64_t send_rows, void* send, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const uint32_t nvec = (uint32_t)(row_bytes / 16);
   const uint32_t total = (uint32_t)T * nvec;
-  const uint32_t nrows = (uint32_t)T * (uint32_t)k;
+  const uint32_t nrows = (uint32_t)send_rows;
   const unsigned grid = (unsigned)((total + kCopyBlock - 1) / kCopyBlock);
   return launch(copy_kernel, dim3(grid), dim3(kCopyBlock), 0, s, static_cast<const v4u*>(x), pos,
                 k, nvec, total, nrows, static_cast<v4u*>(send));
+}
+
+hipError_t launch_pad(int E, int R, int W, int cap, const int32_t* kept, int64_t row_bytes,
+                      void* send, int32_t* row_token, hipStream_t s) {
+  if (cap == 0) return hipSuccess;
+  return launch(pad_kernel, dim3((unsigned)E), dim3(kCopyBlock), 0, s, E, R, W, cap, kept,
+                (uint32_t)(row_bytes / 16), static_cast<v4u*>(send), row_token);
 }
 
 }  // namespace moe

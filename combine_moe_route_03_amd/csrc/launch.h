@@ -103,18 +103,22 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
                                int E, int R, int W, const int32_t* hist, int32_t* expert_counts,
                                int32_t* expert_offsets, int32_t* rank_counts,
                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
-                               int32_t* row_token, moe_stats_t* stats, hipStream_t s);
+                               int32_t* row_token, moe_stats_t* stats, int cap, hipStream_t s);
 
 // Row copies; row_bytes is a multiple of 16.
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
-                       void* send, hipStream_t s);
+                       int64_t send_rows, void* send, hipStream_t s);
+// Capacity layout: zero rows and row_token = -1 past each bucket's kept rows.
+hipError_t launch_pad(int E, int R, int W, int cap, const int32_t* kept, int64_t row_bytes,
+                      void* send, int32_t* row_token, hipStream_t s);
 
 hipError_t launch_expert_scale(const void* in, int dtype, int64_t rows, int64_t H, int E, int R,
                                int W, const int32_t* expert_offsets,
                                const int32_t* expert_counts, void* out, hipStream_t s);
 
+// expert_out has eo_rows rows; picks with pos outside [0, eo_rows) are skipped.
 hipError_t launch_combine(const void* expert_out, int dtype, const float* w, const int32_t* pos,
-                          int T, int k, int64_t H, void* y, hipStream_t s);
+                          int T, int k, int64_t H, int64_t eo_rows, void* y, hipStream_t s);
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s);
 

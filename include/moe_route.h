@@ -155,6 +155,37 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                  int32_t* row_token, void* workspace, size_t workspace_bytes,
                  moe_stream_t stream);
 
+/* Expert capacity (MoE systems survey section 1.2 item 2, eq. (3)): rows per
+ * expert for capacity factor f, ceil(k * f * T / E) evaluated in double in
+ * that order. Host-only, pure; -1 for k < 1, T < 0, E < 1, f < 0 (or NaN) or a
+ * result beyond int32. */
+int32_t moe_expert_capacity(int32_t k, double f, int32_t T, int32_t E);
+
+/* Capacity-factor dispatch (survey section 1.2 eq. (3) and section 1.1 EP flow
+ * step 2: samples beyond an expert's capacity are dropped, unused capacity is
+ * padded with zeros). Every bucket holds exactly `capacity` rows; bucket j of
+ * the (wave, rank, slot) order starts at row j * capacity; an expert keeps its
+ * first `capacity` picks in (token, pick) order and drops the rest (pos = -1),
+ * as it drops ids outside [0, E).
+ * send_buf       [E*capacity][H] out: kept rows, zero rows for padding.
+ * kept_counts    [E] out: min(c[e], capacity).
+ * expert_offsets [E] out: first row of expert e's bucket (= j * capacity).
+ * rank_counts, rank_offsets [W*R], wave_offsets [W+1] out: whole buckets
+ *                (padding is part of what each destination receives).
+ * pos [T][k] out; row_token [E*capacity] out (-1 on padding rows).
+ * workspace: moe_dispatch_workspace_bytes(shape) bytes.
+ * Four launches: count, place, copy, pad. Follow with moe_expert_scale_rows /
+ * moe_combine_rows with rows = E * capacity.
+ * Errors: MOE_ERR_ARG (capacity < 0, E*capacity rows beyond the index limits,
+ *         null pointers), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
+ *         MOE_ERR_DEVICE. */
+int moe_dispatch_capacity(const moe_shape* shape, int32_t capacity, const void* x,
+                          const int32_t* topk_idx, void* send_buf, int32_t* kept_counts,
+                          int32_t* expert_offsets, int32_t* rank_counts,
+                          int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                          int32_t* row_token, void* workspace, size_t workspace_bytes,
+                          moe_stream_t stream);
+
 /* Identity-scaled experts (the experts of the synthetic workloads):
  * expert_out[n][:] = round_dtype((e(n) + 1) * send_buf[n][:]) for every row n
  * inside some expert's bucket [expert_offsets[e], + expert_counts[e]); other
@@ -163,6 +194,12 @@ int moe_expert_scale(const moe_shape* shape, const void* send_buf,
                      const int32_t* expert_offsets,
                      const int32_t* expert_counts, void* expert_out,
                      moe_stream_t stream);
+
+/* moe_expert_scale over a send buffer of `rows` rows (the capacity layout has
+ * E*capacity rows instead of T*k). */
+int moe_expert_scale_rows(const moe_shape* shape, int64_t rows, const void* send_buf,
+                          const int32_t* expert_offsets, const int32_t* expert_counts,
+                          void* expert_out, moe_stream_t stream);
 
 /* Bytes of device workspace moe_expert_swiglu needs (the bf16 intermediate,
  * T*k x I); 0 for an invalid shape or I. Host-only, pure. */
@@ -200,6 +237,12 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
 int moe_combine(const moe_shape* shape, const void* expert_out,
                 const float* topk_w, const int32_t* pos, void* y,
                 moe_stream_t stream);
+
+/* moe_combine over an expert-row buffer of `rows` rows (E*capacity for the
+ * capacity layout): picks with pos outside [0, rows) contribute nothing. */
+int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_out,
+                     const float* topk_w, const int32_t* pos, void* y,
+                     moe_stream_t stream);
 
 /* Skew statistics of S from expert_counts [E] (DODOCO summary, "metrics"):
  * per-expert max/mean and the Gini coefficient

@@ -147,3 +147,21 @@ def test_workspace_covers_fused_histograms():
         ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
         cap = min(512, 65536 // (1 << (E - 1).bit_length()))
         assert E * 4 <= ws <= cap * E * 4 + 255
+
+
+def test_capacity_helpers_and_validation():
+    import oracle
+    L = moe.lib()
+    for k, f, T, E in ((2, 1.25, 256, 8), (6, 1.0, 4096, 64), (1, 1.1, 10, 3), (8, 0.0, 99, 16),
+                       (2, 1.1, 100, 4), (8, 1.25, 16384, 256)):
+        assert L.moe_expert_capacity(k, f, T, E) == oracle.expert_capacity(k, f, T, E)
+    assert L.moe_expert_capacity(2, -1.0, 10, 4) == -1
+    assert L.moe_expert_capacity(2, float("nan"), 10, 4) == -1
+    sh = _shape(T=64, E=8, k=2, R=4)
+    ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
+    args = [FAKE] * 10  # x .. row_token
+    assert L.moe_dispatch_capacity(ctypes.byref(sh), -1, *args, FAKE, ws, None) == ARG
+    assert L.moe_dispatch_capacity(ctypes.byref(sh), 1 << 30, *args, FAKE, ws, None) == ARG
+    assert L.moe_dispatch_capacity(ctypes.byref(sh), 16, *args, FAKE, ws - 1, None) == WORKSPACE
+    assert L.moe_combine_rows(ctypes.byref(sh), -1, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    assert L.moe_expert_scale_rows(ctypes.byref(sh), -1, FAKE, FAKE, FAKE, FAKE, None) == ARG
