@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_expert_swiglu_rows.argtypes = [_u16p, _i32p, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, _u16p, _u16p, _f64p, _u16p]
         L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
+        L.oracle_dirichlet_alpha.argtypes = [_i32p, ctypes.c_int32]
+        L.oracle_dirichlet_alpha.restype = ctypes.c_double
         L.oracle_gini_i64.argtypes = [_i64p, ctypes.c_int32]
         L.oracle_gini_i64.restype = ctypes.c_double
         L.oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -307,3 +309,9 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 def as_f64(a: np.ndarray) -> np.ndarray:
     return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def dirichlet_alpha(counts: np.ndarray) -> float:
+    """Maximum-likelihood symmetric Dirichlet alpha of an expert count vector."""
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    return float(lib().oracle_dirichlet_alpha(_p(c, _i32p), c.shape[0]))

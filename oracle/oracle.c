@@ -340,6 +340,31 @@ double oracle_gini_i64(const int64_t* v, int32_t n) {
   return (double)num / (double)(2 * (int64_t)n * sum);
 }
 
+/* L'(a) for the symmetric Dirichlet-multinomial, as plain finite sums. */
+static double dm_score(const int32_t* counts, int32_t E, int64_t N, double a) {
+  double s = 0.0;
+  for (int32_t e = 0; e < E; ++e)
+    for (int32_t j = 0; j < counts[e]; ++j) s += 1.0 / (a + (double)j);
+  double t = 0.0;
+  for (int64_t j = 0; j < N; ++j) t += 1.0 / ((double)E * a + (double)j);
+  return s - (double)E * t;
+}
+
+double oracle_dirichlet_alpha(const int32_t* counts, int32_t E) {
+  int64_t N = 0;
+  for (int32_t e = 0; e < E; ++e) N += counts[e];
+  if (E < 2 || N == 0) return NAN;
+  double lo = log(1e-8), hi = log(1e8);
+  if (dm_score(counts, E, N, exp(hi)) > 0.0) return INFINITY;
+  if (dm_score(counts, E, N, exp(lo)) < 0.0) return 0.0;
+  for (int it = 0; it < 200 && hi - lo > 1e-15; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (dm_score(counts, E, N, exp(mid)) > 0.0) lo = mid;
+    else hi = mid;
+  }
+  return exp(0.5 * (lo + hi));
+}
+
 void oracle_stats(const int32_t* expert_counts, int32_t E, int32_t R,
                   oracle_stats_t* out) {
   int32_t L = E / R;
