@@ -354,7 +354,7 @@ double oracle_dirichlet_alpha(const int32_t* counts, int32_t E) {
   int64_t N = 0;
   for (int32_t e = 0; e < E; ++e) N += counts[e];
   if (E < 2 || N == 0) return NAN;
-  double lo = log(1e-8), hi = log(1e8);
+  double lo = log(1e-8), hi = log(1e6);
   if (dm_score(counts, E, N, exp(hi)) > 0.0) return INFINITY;
   if (dm_score(counts, E, N, exp(lo)) < 0.0) return 0.0;
   for (int it = 0; it < 200 && hi - lo > 1e-15; ++it) {

@@ -159,9 +159,10 @@ void oracle_stats(const int32_t* expert_counts, int32_t E, int32_t R,
  *   L(a) = lnG(E a) - lnG(N + E a) + sum_e [lnG(c_e + a) - lnG(a)],
  * whose derivative for integer counts is the finite sum
  *   L'(a) = sum_e sum_{j < c_e} 1 / (a + j) - E sum_{j < N} 1 / (E a + j).
- * The root of L' is found by bisecting its sign on ln a over [1e-8, 1e8].
- * Returns +inf when L' > 0 at 1e8 (counts as even as multinomial sampling or
- * more), 0 when L' < 0 at 1e-8, NaN for E < 2 or N = 0. */
+ * The root of L' is found by bisecting its sign on ln a over [1e-8, 1e6].
+ * Returns +inf when L' > 0 at 1e6 (counts as even as multinomial sampling, or
+ * so close that the score's sign beyond 1e6 is below double precision in a
+ * digamma evaluation), 0 when L' < 0 at 1e-8, NaN for E < 2 or N = 0. */
 double oracle_dirichlet_alpha(const int32_t* counts, int32_t E);
 
 /* Gini of n non-negative integers: sum_a sum_b |v_a - v_b| / (2 n sum v). */
