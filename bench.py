@@ -418,6 +418,20 @@ def main() -> int:
         cold_ms = stage_means(cevs)
         del flush
 
+    # Fitted symmetric Dirichlet alpha of this step's counts: a summary of S
+    # computed on demand (its own launch), timed apart from the step.
+    counts_t = cbuf["kept_counts"] if cap is not None else buf["expert_counts"]
+    alpha_t = torch.empty((1,), dtype=torch.float64, device=dev)
+    moe.dirichlet_alpha_device(counts_t, alpha_t)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(20):
+        moe.dirichlet_alpha_device(counts_t, alpha_t)
+    eb.record()
+    torch.cuda.synchronize()
+    alpha_fit = {"value": float(alpha_t.item()), "us": round(ea.elapsed_time(eb) * 1e3 / 20, 2),
+                 "kernel": "dirichlet_alpha_kernel", "in_step": False}
+
     def gbs(name, ms):
         return nbytes[name] / (ms * 1e-3) / 1e9
 
@@ -488,6 +502,7 @@ def main() -> int:
                         "events recorded by the library's extended launches (instrumented loop "
                         f"of {K} steps, {wall_instr * 1e3 / K:.4f} ms/step wall)",
         "plain_copy_GBs": round(copy_gbs, 1),
+        "dirichlet_alpha": alpha_fit,
     }
     if swiglu:
         result["config"]["I"] = wl.I

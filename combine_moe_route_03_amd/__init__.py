@@ -67,6 +67,7 @@ SIGNATURES = {
                           ctypes.c_int),
     "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "moe_dirichlet_alpha": ([_vp, _i32, _vp, _vp], ctypes.c_int),
     "moe_set_timing_events": ([_vp, _vp, _i32], ctypes.c_int),
     "moe_timed_launches": ([], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -348,3 +349,16 @@ def stats_to_dict(raw: torch.Tensor) -> dict:
 def stats(expert_counts: torch.Tensor, R: int) -> dict:
     """Statistics as a host dict (synchronises with the stream)."""
     return stats_to_dict(stats_device(expert_counts, R))
+
+
+def dirichlet_alpha_device(expert_counts: torch.Tensor, out: torch.Tensor | None = None):
+    """Enqueue the alpha fit; returns the device float64 tensor (one element)."""
+    out = _empty((1,), torch.float64, expert_counts.device) if out is None else out
+    _check(lib().moe_dirichlet_alpha(_ptr(expert_counts), expert_counts.numel(), _ptr(out),
+                                     _stream()), "moe_dirichlet_alpha")
+    return out
+
+
+def dirichlet_alpha(expert_counts: torch.Tensor) -> float:
+    """Fitted symmetric Dirichlet alpha of the counts (synchronises)."""
+    return float(dirichlet_alpha_device(expert_counts).item())

@@ -324,6 +324,13 @@ int moe_dispatch_capacity(const moe_shape* shape, int32_t capacity, const void* 
                                    send_buf, row_token, s));
 }
 
+int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_out,
+                        moe_stream_t stream) {
+  if (!expert_counts || !alpha_out || E < 1 || E > 1024) return MOE_ERR_ARG;
+  if (!aligned(expert_counts, 4) || !aligned(alpha_out, 8)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_dirichlet_alpha(expert_counts, E, alpha_out, as_stream(stream)));
+}
+
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R, moe_stats_t* out,
               moe_stream_t stream) {
   if (!expert_counts || !out) return MOE_ERR_ARG;

@@ -122,6 +122,9 @@ hipError_t launch_combine(const void* expert_out, int dtype, const float* w, con
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s);
 
+// Fitted symmetric Dirichlet alpha of E <= 1024 counts into one device double.
+hipError_t launch_dirichlet_alpha(const int32_t* counts, int E, double* out, hipStream_t s);
+
 // Grouped SwiGLU FFN (bf16): gate/up GEMM with fused SiLU*up into hbuf
 // [rows][I], then the down GEMM into out [rows][H]. Needs I % 64 == 0 and
 // H % 128 == 0.

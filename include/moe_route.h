@@ -254,6 +254,19 @@ int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_ou
 int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
               moe_stats_t* out, moe_stream_t stream);
 
+/* Fitted symmetric Dirichlet alpha of the expert counts (DODOCO summary,
+ * "metrics": the third scalar summary of S, resolving near-uniform routings
+ * where the Gini coefficient compresses). Reading: the maximum-likelihood
+ * alpha of a Dirichlet-multinomial with E equal concentrations, i.e. the root
+ * of sum_{c_e > 0} [psi(c_e + a) - psi(a)] - E [psi(N + E a) - psi(E a)],
+ * searched on [1e-8, 1e6]: +inf when the score is still positive at 1e6 (as
+ * even as multinomial sampling), 0 when negative at 1e-8, NaN for E < 2 or no
+ * picks; otherwise to ~1e-12 relative. One block; writes one device double.
+ * Errors: MOE_ERR_ARG (null pointer, E outside [1, 1024]), MOE_ERR_ALIGN
+ *         (alpha_out not 8-byte aligned), MOE_ERR_DEVICE. */
+int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_out,
+                        moe_stream_t stream);
+
 /* Kernel timing hook for benchmarks (not a step of the path). After
  * moe_set_timing_events(starts, stops, n), the kernels this library launches
  * from the calling thread use AMD's extended launch: the i-th one (i < n, at

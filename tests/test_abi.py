@@ -165,3 +165,11 @@ def test_capacity_helpers_and_validation():
     assert L.moe_dispatch_capacity(ctypes.byref(sh), 16, *args, FAKE, ws - 1, None) == WORKSPACE
     assert L.moe_combine_rows(ctypes.byref(sh), -1, FAKE, FAKE, FAKE, FAKE, None) == ARG
     assert L.moe_expert_scale_rows(ctypes.byref(sh), -1, FAKE, FAKE, FAKE, FAKE, None) == ARG
+
+
+def test_dirichlet_alpha_validation():
+    L = moe.lib()
+    assert L.moe_dirichlet_alpha(None, 8, FAKE, None) == ARG
+    assert L.moe_dirichlet_alpha(FAKE, 0, FAKE, None) == ARG
+    assert L.moe_dirichlet_alpha(FAKE, 1025, FAKE, None) == ARG
+    assert L.moe_dirichlet_alpha(FAKE, 8, ctypes.c_void_p((1 << 20) + 4), None) == ALIGN
