@@ -94,6 +94,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_expert_swiglu_rows.argtypes = [_u16p, _i32p, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, _u16p, _u16p, _f64p, _u16p]
         L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
+        _d = ctypes.c_double
+        L.oracle_wave_time.argtypes = [_d, _d, _d, _d]
+        L.oracle_wave_time.restype = _d
+        L.oracle_optimal_waves.argtypes = [_d, _d, _d]
+        L.oracle_optimal_waves.restype = _d
+        L.oracle_plan_waves.argtypes = [_d, _d, _d, ctypes.c_int32]
+        L.oracle_plan_waves.restype = ctypes.c_int32
+        L.oracle_link_p95.argtypes = [_d, _d, ctypes.c_int32]
+        L.oracle_link_p95.restype = _d
         L.oracle_dirichlet_alpha.argtypes = [_i32p, ctypes.c_int32]
         L.oracle_dirichlet_alpha.restype = ctypes.c_double
         L.oracle_gini_i64.argtypes = [_i64p, ctypes.c_int32]
@@ -315,3 +324,19 @@ def dirichlet_alpha(counts: np.ndarray) -> float:
     """Maximum-likelihood symmetric Dirichlet alpha of an expert count vector."""
     c = np.ascontiguousarray(counts, dtype=np.int32)
     return float(lib().oracle_dirichlet_alpha(_p(c, _i32p), c.shape[0]))
+
+
+def wave_time(M: float, a: float, b: float, W: float) -> float:
+    return float(lib().oracle_wave_time(M, a, b, W))
+
+
+def optimal_waves(M: float, a: float, b: float) -> float:
+    return float(lib().oracle_optimal_waves(M, a, b))
+
+
+def plan_waves(M: float, a: float, b: float, L: int) -> int:
+    return int(lib().oracle_plan_waves(M, a, b, L))
+
+
+def link_p95(m_avg: float, B: float, n: int) -> float:
+    return float(lib().oracle_link_p95(m_avg, B, n))

@@ -365,6 +365,31 @@ double oracle_dirichlet_alpha(const int32_t* counts, int32_t E) {
   return exp(0.5 * (lo + hi));
 }
 
+double oracle_wave_time(double M, double a, double b, double W) {
+  return W * a + M / b + M / (W * b);
+}
+
+double oracle_optimal_waves(double M, double a, double b) { return sqrt(M / (a * b)); }
+
+int32_t oracle_plan_waves(double M, double a, double b, int32_t L) {
+  int32_t best = 1;
+  double tbest = oracle_wave_time(M, a, b, 1.0);
+  for (int32_t W = 2; W <= L; ++W) {
+    if (L % W != 0) continue;
+    double t = oracle_wave_time(M, a, b, (double)W);
+    if (t < tbest) {
+      tbest = t;
+      best = W;
+    }
+  }
+  return best;
+}
+
+double oracle_link_p95(double m_avg, double B, int32_t n) {
+  double p = 1.0 / (double)n;
+  return m_avg * (1.0 + 1.645 * sqrt(1.0 / (B * p)));
+}
+
 void oracle_stats(const int32_t* expert_counts, int32_t E, int32_t R,
                   oracle_stats_t* out) {
   int32_t L = E / R;

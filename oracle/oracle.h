@@ -165,6 +165,25 @@ void oracle_stats(const int32_t* expert_counts, int32_t E, int32_t R,
  * digamma evaluation), 0 when L' < 0 at 1e-8, NaN for E < 2 or N = 0. */
 double oracle_dirichlet_alpha(const int32_t* counts, int32_t E);
 
+/* Wave-scheduled exchange model (irregular AllToAll page, "optimal wave
+ * count"): end-to-end time of W waves, T(W) = W a + M / b + M / (W b), with a
+ * the per-wave start latency (s), b the link bandwidth (bytes/s), M the bytes
+ * one link carries. */
+double oracle_wave_time(double M, double a, double b, double W);
+
+/* The minimiser of T over real W > 0: sqrt(M / (a b)) (same passage). */
+double oracle_optimal_waves(double M, double a, double b);
+
+/* The layout needs L mod W = 0: the divisor W of L with the smallest T(W)
+ * (ties to the smaller W), found by trying every W = 1..L. */
+int32_t oracle_plan_waves(double M, double a, double b, int32_t L);
+
+/* 95th-percentile per-link volume under the normal approximation of the
+ * multinomial (irregular AllToAll page, "long-tail latency"):
+ * m_p95 = m_avg (1 + 1.645 sqrt(1 / (B p))), p = 1 / n for n destinations,
+ * B tokens. The page notes the approximation fails for B p < 10. */
+double oracle_link_p95(double m_avg, double B, int32_t n);
+
 /* Gini of n non-negative integers: sum_a sum_b |v_a - v_b| / (2 n sum v). */
 double oracle_gini_i64(const int64_t* v, int32_t n);
 
