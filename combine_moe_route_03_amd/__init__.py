@@ -59,6 +59,10 @@ SIGNATURES = {
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_scale_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_capacity": ([_i32, ctypes.c_double, _i32, _i32], ctypes.c_int32),
+    "moe_wave_time": ([ctypes.c_double, ctypes.c_double, ctypes.c_double, _i32], ctypes.c_double),
+    "moe_plan_waves": ([ctypes.c_double, ctypes.c_double, ctypes.c_double, _i32,
+                        ctypes.POINTER(ctypes.c_double)], ctypes.c_int32),
+    "moe_link_p95": ([ctypes.c_double, ctypes.c_double, _i32], ctypes.c_double),
     "moe_dispatch_capacity": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -232,6 +236,22 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
 def expert_capacity(k: int, f: float, T: int, E: int) -> int:
     """Rows per expert for capacity factor f (ceil(k*f*T/E)); -1 if invalid."""
     return int(lib().moe_expert_capacity(k, f, T, E))
+
+
+def wave_time(message_bytes: float, alpha_s: float, beta: float, W: int) -> float:
+    """T(W) = W alpha + M/beta + M/(W beta) of the wave-scheduled exchange."""
+    return float(lib().moe_wave_time(message_bytes, alpha_s, beta, W))
+
+
+def plan_waves(message_bytes: float, alpha_s: float, beta: float, L: int):
+    """(W, T(W)): the divisor of L with the smallest modelled exchange time."""
+    t = ctypes.c_double()
+    W = int(lib().moe_plan_waves(message_bytes, alpha_s, beta, L, ctypes.byref(t)))
+    return W, t.value
+
+
+def link_p95(mean_bytes: float, tokens: float, destinations: int) -> float:
+    return float(lib().moe_link_p95(mean_bytes, tokens, destinations))
 
 
 def alloc_dispatch_capacity(shape: Shape, capacity: int, device) -> dict:

@@ -280,6 +280,38 @@ int moe_combine(const moe_shape* shape, const void* expert_out, const float* top
                           stream);
 }
 
+double moe_wave_time(double message_bytes, double alpha_s, double beta_bytes_per_s, int32_t W) {
+  if (W < 1 || !(alpha_s >= 0.0) || !(beta_bytes_per_s > 0.0) || !(message_bytes >= 0.0))
+    return -1.0;
+  return W * alpha_s + message_bytes / beta_bytes_per_s + message_bytes / (W * beta_bytes_per_s);
+}
+
+int32_t moe_plan_waves(double message_bytes, double alpha_s, double beta_bytes_per_s, int32_t L,
+                       double* time_out) {
+  if (L < 1 || moe_wave_time(message_bytes, alpha_s, beta_bytes_per_s, 1) < 0.0) return -1;
+  // T(W) is convex in W with its real minimum at sqrt(M / (alpha beta)); the
+  // layout needs W | L, so the best feasible W is a divisor of L on either side.
+  int32_t best = 1;
+  double tbest = moe_wave_time(message_bytes, alpha_s, beta_bytes_per_s, 1);
+  for (int32_t d = 1; (int64_t)d * d <= L; ++d) {
+    if (L % d != 0) continue;
+    for (int32_t W : {d, L / d}) {
+      const double t = moe_wave_time(message_bytes, alpha_s, beta_bytes_per_s, W);
+      if (t < tbest || (t == tbest && W < best)) {
+        tbest = t;
+        best = W;
+      }
+    }
+  }
+  if (time_out) *time_out = tbest;
+  return best;
+}
+
+double moe_link_p95(double mean_bytes, double tokens, int32_t destinations) {
+  if (destinations < 1 || !(tokens > 0.0) || !(mean_bytes >= 0.0)) return -1.0;
+  return mean_bytes * (1.0 + 1.645 * std::sqrt(destinations / tokens));
+}
+
 int32_t moe_expert_capacity(int32_t k, double f, int32_t T, int32_t E) {
   if (k < 1 || T < 0 || E < 1 || !(f >= 0.0)) return -1;
   const double ec = std::ceil(double(k) * f * double(T) / double(E));

@@ -161,6 +161,29 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  * result beyond int32. */
 int32_t moe_expert_capacity(int32_t k, double f, int32_t T, int32_t E);
 
+/* Wave-scheduled exchange model (irregular AllToAll page, "optimal wave
+ * count"; host-only, pure): the end-to-end time of W expert waves
+ *   T(W) = W alpha + M / beta + M / (W beta)
+ * with alpha the start latency of one wave (s), beta one link's bandwidth
+ * (bytes/s) and M the bytes the most loaded link carries. -1 for W < 1,
+ * alpha < 0, beta <= 0 or M < 0. */
+double moe_wave_time(double message_bytes, double alpha_s, double beta_bytes_per_s, int32_t W);
+
+/* The wave count for this layout: the divisor W of L (the local experts per
+ * rank; waves split them, so L mod W = 0) with the smallest T(W), ties to the
+ * smaller W (the real optimum is sqrt(M / (alpha beta)); the page's NVLink 5.0
+ * example, 16 MB at 1 us and 50 GB/s, gives about 18). Writes T(W) to
+ * *time_out when non-NULL. -1 for L < 1 or invalid model parameters. */
+int32_t moe_plan_waves(double message_bytes, double alpha_s, double beta_bytes_per_s, int32_t L,
+                       double* time_out);
+
+/* 95th-percentile bytes on one link when `tokens` tokens pick among
+ * `destinations` equally likely destinations (irregular AllToAll page,
+ * "long-tail latency"; normal approximation of the multinomial, valid for
+ * tokens / destinations >= 10): mean (1 + 1.645 sqrt(destinations / tokens)).
+ * -1 for destinations < 1, tokens <= 0 or mean < 0. */
+double moe_link_p95(double mean_bytes, double tokens, int32_t destinations);
+
 /* Capacity-factor dispatch (survey section 1.2 eq. (3) and section 1.1 EP flow
  * step 2: samples beyond an expert's capacity are dropped, unused capacity is
  * padded with zeros). Every bucket holds exactly `capacity` rows; bucket j of

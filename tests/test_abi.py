@@ -19,7 +19,7 @@ OK, ARG, ALIGN, WORKSPACE, UNSUPPORTED, DEVICE = 0, -1, -2, -3, -4, -5
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_lists_the_expected_entry_points():
@@ -173,3 +173,20 @@ def test_dirichlet_alpha_validation():
     assert L.moe_dirichlet_alpha(FAKE, 0, FAKE, None) == ARG
     assert L.moe_dirichlet_alpha(FAKE, 1025, FAKE, None) == ARG
     assert L.moe_dirichlet_alpha(FAKE, 8, ctypes.c_void_p((1 << 20) + 4), None) == ALIGN
+
+
+def test_wave_planner_and_p95_match_the_oracle():
+    # host-only planning functions of the library against the oracle's models
+    import oracle
+    for M, a, b in ((16e6, 1e-6, 50e9), (2e9, 2e-6, 153e9), (1e5, 5e-6, 10e9), (0.0, 1e-6, 1e9)):
+        for W in (1, 3, 8, 18):
+            assert abs(moe.wave_time(M, a, b, W) - oracle.wave_time(M, a, b, W)) <= 1e-15 * (
+                oracle.wave_time(M, a, b, W) + 1)
+        for L in (1, 8, 12, 18, 32, 64, 1024):
+            W, t = moe.plan_waves(M, a, b, L)
+            assert W == oracle.plan_waves(M, a, b, L)
+            assert t == moe.wave_time(M, a, b, W)
+    for m, B, n in ((100.0, 4096, 8), (1e6, 16384, 32), (5.0, 32, 16)):
+        assert abs(moe.link_p95(m, B, n) - oracle.link_p95(m, B, n)) <= 1e-12 * oracle.link_p95(m, B, n)
+    assert moe.plan_waves(1.0, 1e-6, 0.0, 8)[0] == -1 and moe.wave_time(1.0, 1e-6, 1e9, 0) == -1.0
+    assert moe.link_p95(1.0, 0.0, 4) == -1.0
