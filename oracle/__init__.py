@@ -340,3 +340,113 @@ def plan_waves(M: float, a: float, b: float, L: int) -> int:
 
 def link_p95(m_avg: float, B: float, n: int) -> float:
     return float(lib().oracle_link_p95(m_avg, B, n))
+
+
+# ------------------------------------------ virtual-source exchange (one GPU)
+#
+# The expert-parallel exchange of R ranks emulated on one device (MoE systems
+# survey, crad.ict.ac.cn, section 1.1, EP flow steps 2-4; irregular AllToAll
+# page, "sources of irregular a2a": the per-pair send counts of an Alltoallv).
+# The T tokens split into R equal source shards; source s dispatches its own
+# tokens exactly as a single rank does; destination d owns experts
+# d*L .. d*L+L-1 (L = E/R); with W waves each (source, wave, destination) pair is
+# one message. All tables are in rows; offsets are absolute rows of the
+# concatenated buffers.
+
+
+def vsrc_exchange(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, R: int, W: int = 1):
+    """Every table and buffer of the emulated exchange, as a dict:
+
+    send       rows of all sources, source s at rows [s*Ts*k, (s+1)*Ts*k), each in
+               the one-rank dispatch layout of its own tokens (buckets in (wave,
+               destination, slot) order, token order inside a bucket);
+    src_counts [R][E]: picks of expert e made by source s's tokens;
+    send_counts / send_offsets [R][W][R] (source, wave, destination): the
+               Alltoallv send side;
+    recv_counts / recv_offsets [R][W][R] (destination, wave, source): the receive
+               side; recv is ordered by destination, then wave, then source, and
+               holds the message of that triple unchanged;
+    grouped    each destination's rows regrouped by local expert, then source
+               (so, over all destinations, rows in expert order and token order
+               inside an expert); expert_counts / expert_offsets index it;
+    expert_out (e+1)-scaled rows of grouped;
+    back_recv, back_send: expert rows carried back (ungroup, reverse exchange);
+    pos [T][k]: the send row of each pick; y: fp32 fma-chain combine."""
+    T, k = idx.shape
+    if R < 1 or E % R or T % R or (E // R) % W:
+        raise ValueError("need R | E, R | T and W | E/R")
+    L, Ts, H = E // R, T // R, x.shape[1]
+    LW = L // W
+    rows = T * k
+    send = np.zeros((rows, H), x.dtype)
+    pos = np.full((T, k), -1, np.int32)
+    src_counts = np.zeros((R, E), np.int32)
+    send_counts = np.zeros((R, W, R), np.int64)
+    send_offsets = np.zeros((R, W, R), np.int64)
+    for s in range(R):
+        sl = slice(s * Ts, (s + 1) * Ts)
+        d_s = dispatch(x[sl], idx[sl], E, R, W)
+        base = s * Ts * k
+        src_counts[s] = d_s["expert_counts"]
+        send[base:base + d_s["nrows"]] = d_s["send_buf"]
+        pos[sl] = np.where(d_s["pos"] >= 0, d_s["pos"] + base, -1)
+        send_counts[s] = d_s["rank_counts"].reshape(W, R)
+        send_offsets[s] = d_s["rank_offsets"].reshape(W, R) + base
+
+    # the Alltoallv: destination d, wave w, source s in that order
+    recv_counts = send_counts.transpose(2, 1, 0).copy()
+    recv_offsets = np.zeros_like(recv_counts)
+    recv = np.zeros_like(send)
+    r = 0
+    for d in range(R):
+        for wv in range(W):
+            for s in range(R):
+                c = recv_counts[d, wv, s]
+                recv_offsets[d, wv, s] = r
+                a = send_offsets[s, wv, d]
+                recv[r:r + c] = send[a:a + c]
+                r += c
+
+    # receive-side regroup. Source s's message (d, w) holds slots j of wave w
+    # in slot order; the regrouped rows of destination d run over (slot, source).
+    expert_counts = src_counts.sum(axis=0).astype(np.int64)
+    expert_offsets = np.concatenate([[0], np.cumsum(expert_counts)[:-1]]).astype(np.int64)
+    grp_start = np.zeros((E, R), np.int64)
+    recv_sub = np.zeros((E, R), np.int64)
+    for e in range(E):
+        d, j = divmod(e, L)
+        wv = j // LW
+        for s in range(R):
+            grp_start[e, s] = expert_offsets[e] + src_counts[:s, e].sum()
+            recv_sub[e, s] = recv_offsets[d, wv, s] + src_counts[s, d * L + wv * LW:e].sum()
+    grouped = np.zeros_like(send)
+    for e in range(E):
+        for s in range(R):
+            c = src_counts[s, e]
+            grouped[grp_start[e, s]:grp_start[e, s] + c] = recv[recv_sub[e, s]:recv_sub[e, s] + c]
+
+    expert_out = expert_scale(grouped, expert_offsets.astype(np.int32),
+                              expert_counts.astype(np.int32))
+
+    # combine direction: ungroup, reverse exchange, combine at the source
+    back_recv = np.zeros_like(send)
+    for e in range(E):
+        for s in range(R):
+            c = src_counts[s, e]
+            back_recv[recv_sub[e, s]:recv_sub[e, s] + c] = \
+                expert_out[grp_start[e, s]:grp_start[e, s] + c]
+    back_send = np.zeros_like(send)
+    for d in range(R):
+        for wv in range(W):
+            for s in range(R):
+                c = recv_counts[d, wv, s]
+                a, b = send_offsets[s, wv, d], recv_offsets[d, wv, s]
+                back_send[a:a + c] = back_recv[b:b + c]
+    y = combine_f32fma(back_send, np.asarray(w, np.float32), pos, T)
+    i32 = lambda a: np.asarray(a, np.int32)
+    return dict(send=send, pos=pos, src_counts=src_counts, send_counts=i32(send_counts),
+                send_offsets=i32(send_offsets), recv_counts=i32(recv_counts),
+                recv_offsets=i32(recv_offsets), recv=recv, expert_counts=i32(expert_counts),
+                expert_offsets=i32(expert_offsets), grp_start=i32(grp_start),
+                recv_sub=i32(recv_sub), grouped=grouped, expert_out=expert_out,
+                back_recv=back_recv, back_send=back_send, y=y)
