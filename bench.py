@@ -20,6 +20,11 @@ the launch stream), so a stage's time is its kernels' execution time. The
 dominant kernel's algorithmic bytes (or flops) over its average duration is
 `roofline`. A third loop repeats the instrumented steps after evicting the
 256 MB Infinity Cache (a 512 MiB scratch write) for cold-cache stage times.
+
+--vsrc runs the exchange of R ranks emulated on the one device instead: every
+source shard's dispatch and the count exchange, the block-transpose all-to-all,
+the receive-side regroup, the experts on the regrouped rows, then ungroup,
+reverse all-to-all and combine at the sources (15 kernels a step).
 """
 from __future__ import annotations
 
@@ -38,7 +43,8 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-STAGES = ("route", "dispatch_index", "dispatch_copy", "expert", "combine", "stats")
+STAGES = ("route", "dispatch_index", "dispatch_copy", "exchange", "regroup", "expert", "combine",
+          "stats")
 
 
 class HipEvents:
@@ -78,6 +84,8 @@ def parse_args():
                     help="also time K steps replayed from one captured HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="separate route / dispatch_index / stats calls (7 kernels a step)")
+    ap.add_argument("--vsrc", action="store_true",
+                    help="the expert-parallel exchange of R virtual source ranks on one device")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="capacity-factor dispatch (buckets of ceil(k*f*T/E) rows, overflow "
                          "dropped, zero padding) instead of count-sized buckets")
@@ -143,17 +151,40 @@ def capacity_bytes(wl, cap: int, kept: int) -> dict:
     return out
 
 
+def vsrc_bytes(wl, nrows: int) -> dict:
+    """The byte model of the emulated exchange: each exchange and regroup
+    launch reads and writes every sent row once (two launches each a step)."""
+    H, b = wl.H, wl.elem_bytes
+    out = algorithmic_bytes(wl)
+    out["exchange"] = 2 * 2 * nrows * H * b
+    out["regroup"] = 2 * 2 * nrows * H * b
+    return out
+
+
 def ffn_flops(wl) -> int:
     return 6 * wl.T * wl.k * wl.H * wl.I  # gate/up (2*2I*H) + down (2*H*I) per row
 
 
-def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None) -> dict:
+def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) -> dict:
     """The oracle, as it stands, timed on the host (single thread)."""
     import numpy as np
 
     import oracle
 
-    if ffn_weights is None:
+    if vsrc:
+        passes, t_used = 0, 0.0
+        while passes < 2 or t_used < seconds:
+            t0 = time.perf_counter()
+            idx, w = oracle.route(logits, wl.k)
+            v = oracle.vsrc_exchange(x, idx, w, wl.E, wl.R, wl.W)
+            oracle.stats(v["expert_counts"], wl.R)
+            t_used += time.perf_counter() - t0
+            passes += 1
+        tokens = wl.T * passes
+        sample = (f"{passes} full passes of the {wl.name} workload (T={wl.T}) through the oracle "
+                  f"(C steps, numpy block moves): route, per-source dispatch, exchange, regroup, "
+                  f"expert, ungroup, exchange back, combine, stats")
+    elif ffn_weights is None:
         passes, t_used = 0, 0.0
         while passes < 2 or t_used < seconds:
             t0 = time.perf_counter()
@@ -303,8 +334,50 @@ def main() -> int:
             (L.moe_stats, (P(cbuf["kept_counts"]), E, R, P(stats_raw), stream),
              [("stats", "stats_kernel")]),
         ]
+    if args.vsrc:
+        if swiglu or cap is not None:
+            print("--vsrc runs the identity-scaled experts without a capacity", file=sys.stderr)
+            return 2
+        vb = moe.alloc_vsrc(shape, dev)
+        veo = torch.empty_like(vb["send_buf"])
+        vback_recv = torch.empty_like(vb["recv_buf"])
+        vback_send = torch.empty_like(vb["send_buf"])
+        # the regrouped rows are in plain expert order: the bucket order of W = 1
+        sh1 = moe.Shape(T, H, E, k, R, 1, tdt).c()
+        shp1 = ctypes.byref(sh1)
+        vws = (P(vb["workspace"]), vb["workspace"].numel())
+        ex_tabs = (P(vb["send_offsets"]), P(vb["recv_counts"]), P(vb["recv_offsets"]))
+        rg_tabs = (P(vb["src_counts"]), P(vb["recv_offsets"]), P(vb["expert_offsets"]))
+        calls = [
+            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
+             [("route", "route_kernel")]),
+            (L.moe_vsrc_dispatch, (
+                shp, P(x), P(topk_idx), P(vb["send_buf"]), P(vb["src_counts"]),
+                P(vb["send_counts"]), P(vb["send_offsets"]), P(vb["recv_counts"]),
+                P(vb["recv_offsets"]), P(vb["expert_counts"]), P(vb["expert_offsets"]),
+                P(vb["pos"]), *vws, stream),
+             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(sources)"),
+              ("dispatch_index", "vsrc_plan_kernel"), ("dispatch_copy", "copy_kernel")]),
+            (L.moe_vsrc_exchange, (shp, 0, P(vb["send_buf"]), P(vb["recv_buf"]), *ex_tabs, stream),
+             [("exchange", "segcopy_kernel<exchange>")]),
+            (L.moe_vsrc_regroup, (shp, 0, P(vb["recv_buf"]), P(vb["grouped"]), *rg_tabs, *vws,
+                                  stream),
+             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
+            (L.moe_expert_scale_rows, (shp1, T * k, P(vb["grouped"]), P(vb["expert_offsets"]),
+                                       P(vb["expert_counts"]), P(veo), stream),
+             [("expert", "expert_scale_kernel")]),
+            (L.moe_vsrc_regroup, (shp, 1, P(veo), P(vback_recv), *rg_tabs, *vws, stream),
+             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
+            (L.moe_vsrc_exchange, (shp, 1, P(vback_recv), P(vback_send), *ex_tabs, stream),
+             [("exchange", "segcopy_kernel<exchange>")]),
+            (L.moe_combine, (shp, P(vback_send), P(topk_w), P(vb["pos"]), P(y), stream),
+             [("combine", "combine_kernel")]),
+            (L.moe_stats, (P(vb["expert_counts"]), E, R, P(stats_raw), stream),
+             [("stats", "stats_kernel")]),
+        ]
     STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
-    kernel_of = {st: "+".join(kn for c in calls for g, kn in c[2] if g == st) for st in STAGES_RUN}
+    kernel_of = {st: "+".join(dict.fromkeys(kn for c in calls for g, kn in c[2] if g == st))
+                 for st in STAGES_RUN}
 
     hipev = HipEvents()
     set_events = L.moe_set_timing_events
@@ -330,13 +403,22 @@ def main() -> int:
             return (ctypes.c_void_p * NPAIR)(*[hipev.create() for _ in range(NPAIR)])
         return [[(arr(), arr()) for _ in calls] for _ in range(n)]
 
+    kernel_ms = {}
+
     def stage_means(evs):
-        """Per stage: summed execution time of its kernels, averaged over steps."""
+        """Per stage: summed execution time of its kernels, averaged over steps
+        (and each kernel's mean time per launch into kernel_ms)."""
         tot = {st: 0.0 for st in STAGES_RUN}
+        per, n = {}, {}
         for e in evs:
             for i, (_, _, kernels) in enumerate(calls):
-                for j, (st, _) in enumerate(kernels):
-                    tot[st] += hipev.ms(e[i][0][j], e[i][1][j])
+                for j, (st, kn) in enumerate(kernels):
+                    t = hipev.ms(e[i][0][j], e[i][1][j])
+                    tot[st] += t
+                    per[kn] = per.get(kn, 0.0) + t
+                    n[kn] = n.get(kn, 0) + 1
+        kernel_ms.clear()
+        kernel_ms.update({kn: per[kn] / n[kn] for kn in per})
         return {st: v / len(evs) for st, v in tot.items()}
 
     for _ in range(args.warmup):
@@ -362,10 +444,13 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t0
     stage_ms = stage_means(evs)
+    kernel_us = {kn: round(v * 1e3, 2) for kn, v in kernel_ms.items()}
     nbytes = algorithmic_bytes(wl)
     if cap is not None:
         kept = int(cbuf["kept_counts"].sum().item())
         nbytes = capacity_bytes(wl, cap, kept)
+    if args.vsrc:
+        nbytes = vsrc_bytes(wl, int(vb["expert_counts"].sum().item()))
 
     graph_wall = None
     if args.graph:
@@ -420,7 +505,8 @@ def main() -> int:
 
     # Fitted symmetric Dirichlet alpha of this step's counts: a summary of S
     # computed on demand (its own launch), timed apart from the step.
-    counts_t = cbuf["kept_counts"] if cap is not None else buf["expert_counts"]
+    counts_t = (cbuf["kept_counts"] if cap is not None
+                else vb["expert_counts"] if args.vsrc else buf["expert_counts"])
     alpha_t = torch.empty((1,), dtype=torch.float64, device=dev)
     moe.dirichlet_alpha_device(counts_t, alpha_t)
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -449,7 +535,8 @@ def main() -> int:
         return rep
 
     # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
-    single = [n for n in ("route", "dispatch_copy", "expert", "combine", "stats")
+    single = [n for n in ("route", "dispatch_copy", "exchange", "regroup", "expert", "combine",
+                          "stats")
               if n in STAGES_RUN and not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
@@ -466,6 +553,8 @@ def main() -> int:
                     "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
 
     dc_keys = ("dispatch_index", "dispatch_copy", "combine")
+    if args.vsrc:
+        dc_keys = ("dispatch_index", "dispatch_copy", "exchange", "regroup", "combine")
     dc_ms = sum(stage_ms[n] for n in dc_keys)
     dc_bytes = sum(nbytes[n] for n in dc_keys)
     result = {
@@ -498,6 +587,7 @@ def main() -> int:
         },
         "roofline": roofline,
         "stages": stage_report(stage_ms),
+        "kernel_us_per_launch": kernel_us,
         "stage_timing": "sum of the execution times of each stage's kernels, from start/stop "
                         "events recorded by the library's extended launches (instrumented loop "
                         f"of {K} steps, {wall_instr * 1e3 / K:.4f} ms/step wall)",
@@ -511,6 +601,9 @@ def main() -> int:
                                     "+expert+combine+stats")
         result["config"].update(capacity_factor=args.capacity_factor, capacity=cap,
                                 kept_picks=kept, dropped_picks=T * k - kept)
+    if args.vsrc:
+        result["config"]["step"] = ("route+vsrc_dispatch(count,place,plan,copy)+exchange"
+                                    "+regroup+expert+ungroup+exchange back+combine+stats")
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}
@@ -524,7 +617,8 @@ def main() -> int:
                                  "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9
                                                         / HBM_PEAK_GBS, 4)}}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, logits_np, x_np, args.cpu_seconds, ffn_np)
+        result["cpu_baseline"] = cpu_baseline(wl, logits_np, x_np, args.cpu_seconds, ffn_np,
+                                              vsrc=args.vsrc)
     print(json.dumps(result), flush=True)
     return 0
 

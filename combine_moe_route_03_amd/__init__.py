@@ -66,6 +66,12 @@ SIGNATURES = {
     "moe_dispatch_capacity": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
+    "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_vsrc_exchange": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_vsrc_regroup": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                         ctypes.c_int),
     "moe_expert_swiglu_workspace_bytes": ([_shp, _i32], ctypes.c_size_t),
     "moe_expert_swiglu": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                           ctypes.c_int),
@@ -283,6 +289,63 @@ def dispatch_capacity(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W
         _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
         "moe_dispatch_capacity")
     return out
+
+
+# ------------------------------------------------ virtual-source exchange
+
+def vsrc_workspace_bytes(shape: Shape) -> int:
+    return int(lib().moe_vsrc_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def alloc_vsrc(shape: Shape, device) -> dict:
+    """Buffers of the emulated exchange: three row buffers of T*k rows (send,
+    recv, grouped) and the count tables."""
+    E, R, W, H, T, k = shape.E, shape.R, shape.W, shape.H, shape.T, shape.k
+    i32 = torch.int32
+    rows = T * k
+    return dict(
+        send_buf=_empty((rows, H), shape.dtype, device), recv_buf=_empty((rows, H), shape.dtype, device),
+        grouped=_empty((rows, H), shape.dtype, device), src_counts=_empty((R, E), i32, device),
+        send_counts=_empty((R, W, R), i32, device), send_offsets=_empty((R, W, R), i32, device),
+        recv_counts=_empty((R, W, R), i32, device), recv_offsets=_empty((R, W, R), i32, device),
+        expert_counts=_empty((E,), i32, device), expert_offsets=_empty((E,), i32, device),
+        pos=_empty((T, k), i32, device),
+        workspace=_empty((max(vsrc_workspace_bytes(shape), 1),), torch.uint8, device), rows=rows)
+
+
+def vsrc_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, shape: Shape, out: dict) -> dict:
+    """Every source shard's dispatch into out["send_buf"] plus the count
+    exchange tables (four launches)."""
+    sh = shape.c()
+    _check(lib().moe_vsrc_dispatch(
+        ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]), _ptr(out["src_counts"]),
+        _ptr(out["send_counts"]), _ptr(out["send_offsets"]), _ptr(out["recv_counts"]),
+        _ptr(out["recv_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["pos"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
+        "moe_vsrc_dispatch")
+    return out
+
+
+def vsrc_exchange(src: torch.Tensor, dst: torch.Tensor, shape: Shape, out: dict,
+                  direction: int = 0) -> torch.Tensor:
+    """The all-to-all as a block transpose: send -> recv (direction 0) or
+    recv -> send (direction 1), with the tables in `out`."""
+    sh = shape.c()
+    _check(lib().moe_vsrc_exchange(
+        ctypes.byref(sh), direction, _ptr(src), _ptr(dst), _ptr(out["send_offsets"]),
+        _ptr(out["recv_counts"]), _ptr(out["recv_offsets"]), _stream()), "moe_vsrc_exchange")
+    return dst
+
+
+def vsrc_regroup(src: torch.Tensor, dst: torch.Tensor, shape: Shape, out: dict,
+                 direction: int = 0) -> torch.Tensor:
+    """Receive-side regroup: recv -> grouped (direction 0) or back (1)."""
+    sh = shape.c()
+    _check(lib().moe_vsrc_regroup(
+        ctypes.byref(sh), direction, _ptr(src), _ptr(dst), _ptr(out["src_counts"]),
+        _ptr(out["recv_offsets"]), _ptr(out["expert_offsets"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream()), "moe_vsrc_regroup")
+    return dst
 
 
 def expert_scale_rows(send_buf: torch.Tensor, expert_offsets: torch.Tensor,

@@ -73,6 +73,34 @@ int check_copy_args(const moe_shape* sh, const void* x, const int32_t* pos, void
   return MOE_OK;
 }
 
+// Virtual-source exchange: equal source shards.
+int check_vsrc_shape(const moe_shape* sh) {
+  const int st = check_shape(sh);
+  if (st != MOE_OK) return st;
+  if (sh->T % sh->R != 0) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// Per-source hist rows, per-source expert offsets and wave offsets (dispatch),
+// or the 3 * E * R segment table (regroup).
+size_t vsrc_workspace_bytes(const moe_shape* sh) {
+  int64_t chunk;
+  int spc;
+  moe::source_chunks(int64_t(sh->T / sh->R) * sh->k, sh->E, chunk, spc);
+  const int64_t R = sh->R, E = sh->E;
+  const int64_t disp = (R * spc * E + R * E + R * (sh->W + 1)) * 4;
+  const int64_t regroup = 3 * E * R * 4;
+  const int64_t bytes = disp > regroup ? disp : regroup;
+  return size_t((bytes + 255) / 256 * 256);
+}
+
+int check_vsrc_move(const moe_shape* sh, int32_t direction, const void* in, const void* out) {
+  if (direction != 0 && direction != 1) return MOE_ERR_ARG;
+  if (sh->T > 0 && (!in || !out)) return MOE_ERR_ARG;
+  if (!aligned(in, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -369,6 +397,90 @@ int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R, moe_stats_t* o
   if (E < 1 || E > 1024 || R < 1 || E % R != 0) return MOE_ERR_ARG;
   if (!aligned(expert_counts, 4) || !aligned(out, 8)) return MOE_ERR_ALIGN;
   return status_of(moe::launch_stats(expert_counts, E, R, out, as_stream(stream)));
+}
+
+// ------------------------------------------------ virtual-source exchange
+
+size_t moe_vsrc_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return vsrc_workspace_bytes(shape);
+}
+
+int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                      void* send_buf, int32_t* src_counts, int32_t* send_counts,
+                      int32_t* send_offsets, int32_t* recv_counts, int32_t* recv_offsets,
+                      int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_vsrc_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!src_counts || !send_counts || !send_offsets || !recv_counts || !recv_offsets ||
+      !expert_counts || !expert_offsets || !workspace)
+    return MOE_ERR_ARG;
+  if (shape->T > 0 && (!topk_idx || !pos)) return MOE_ERR_ARG;
+  const void* p4[] = {topk_idx, src_counts, send_counts, send_offsets, recv_counts,
+                      recv_offsets, expert_counts, expert_offsets, pos, workspace};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+  st = check_copy_args(shape, x, pos, send_buf);
+  if (st != MOE_OK) return st;
+  if (workspace_bytes_given < vsrc_workspace_bytes(shape)) return MOE_ERR_WORKSPACE;
+  const int R = shape->R, W = shape->W, E = shape->E, k = shape->k;
+  const int64_t src_picks = int64_t(shape->T / R) * k;
+  int64_t chunk;
+  int spc;
+  moe::source_chunks(src_picks, E, chunk, spc);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* src_offsets = hist + int64_t(R) * spc * E;
+  int32_t* wave_offsets = src_offsets + int64_t(R) * E;
+  hipStream_t s = as_stream(stream);
+  st = status_of(moe::launch_count_sources(topk_idx, R, src_picks, E, hist, s));
+  if (st != MOE_OK) return st;
+  st = status_of(moe::launch_place_sources(topk_idx, R, src_picks, k, E, R, W, hist, src_counts,
+                                           src_offsets, send_counts, send_offsets, wave_offsets,
+                                           pos, s));
+  if (st != MOE_OK) return st;
+  st = status_of(moe::launch_vsrc_plan(R, W, E, src_counts, send_counts, recv_counts,
+                                       recv_offsets, expert_counts, expert_offsets, s));
+  if (st != MOE_OK) return st;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_copy(x, pos, shape->T, k, row_bytes, int64_t(shape->T) * k,
+                                    send_buf, s));
+}
+
+int moe_vsrc_exchange(const moe_shape* shape, int32_t direction, const void* in, void* out,
+                      const int32_t* send_offsets, const int32_t* recv_counts,
+                      const int32_t* recv_offsets, moe_stream_t stream) {
+  int st = check_vsrc_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_vsrc_move(shape, direction, in, out);
+  if (st != MOE_OK) return st;
+  if (!send_offsets || !recv_counts || !recv_offsets) return MOE_ERR_ARG;
+  if (!aligned(send_offsets, 4) || !aligned(recv_counts, 4) || !aligned(recv_offsets, 4))
+    return MOE_ERR_ALIGN;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_vsrc_exchange(in, out, row_bytes, int64_t(shape->T) * shape->k,
+                                             shape->R, shape->W, send_offsets, recv_counts,
+                                             recv_offsets, direction == 1, as_stream(stream)));
+}
+
+int moe_vsrc_regroup(const moe_shape* shape, int32_t direction, const void* in, void* out,
+                     const int32_t* src_counts, const int32_t* recv_offsets,
+                     const int32_t* expert_offsets, void* workspace,
+                     size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_vsrc_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_vsrc_move(shape, direction, in, out);
+  if (st != MOE_OK) return st;
+  if (!src_counts || !recv_offsets || !expert_offsets || !workspace) return MOE_ERR_ARG;
+  if (!aligned(src_counts, 4) || !aligned(recv_offsets, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(workspace, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_given < vsrc_workspace_bytes(shape)) return MOE_ERR_WORKSPACE;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_vsrc_regroup(
+      in, out, row_bytes, int64_t(shape->T) * shape->k, shape->E, shape->R, shape->W, src_counts,
+      recv_offsets, expert_offsets, static_cast<int32_t*>(workspace), direction == 1,
+      as_stream(stream)));
 }
 
 }  // extern "C"

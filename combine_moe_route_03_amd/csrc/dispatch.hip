@@ -20,6 +20,12 @@
 //                 prefetched while the current one is placed.
 //   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
 //                 k stores.
+//
+// Source shards: count and place also run over nsrc equal shards of the picks
+// at once (the virtual source ranks of the emulated exchange). Shard s owns
+// spc consecutive chunks and hist rows, its own buckets at rows
+// [s*src_picks, (s+1)*src_picks), and its own slice of every count and offset
+// output; with one shard this is the plain single-rank dispatch.
 #include "block_stats.h"
 #include "device.h"
 #include "launch.h"
@@ -31,15 +37,27 @@ constexpr int kB = kIndexBlock;  // 1024 threads, 16 waves
 constexpr int kWaves = kB / kWave;
 constexpr int kMaxE = 1024;
 
-__global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ idx,
-                                                   int64_t npicks, int64_t chunk, int E,
-                                                   int32_t* __restrict__ hist) {
+// Picks [p0, p1) of block b: chunk b - src*spc of shard src.
+__device__ __forceinline__ void chunk_range(int b, int spc, int nsrc, int64_t chunk,
+                                            int64_t src_picks, int& src, int64_t& p0,
+                                            int64_t& p1) {
+  src = spc > 0 ? b / spc : 0;
+  if (src > nsrc - 1) src = nsrc - 1;
+  const int64_t end = (int64_t)(src + 1) * src_picks;
+  p0 = (int64_t)src * src_picks + (int64_t)(b - src * spc) * chunk;
+  p1 = p0 + chunk < end ? p0 + chunk : end;
+}
+
+__global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ idx, int nsrc,
+                                                   int spc, int64_t src_picks, int64_t chunk,
+                                                   int E, int32_t* __restrict__ hist) {
   __shared__ int32_t h[kMaxE];
   const int tid = threadIdx.x;
   if (tid < E) h[tid] = 0;
   __syncthreads();
-  const int64_t p0 = (int64_t)blockIdx.x * chunk;
-  const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
+  int src;
+  int64_t p0, p1;
+  chunk_range(blockIdx.x, spc, nsrc, chunk, src_picks, src, p0, p1);
   for (int64_t base = p0; base < p1; base += 4 * kB) {
     int ev[4];
 #pragma unroll
@@ -56,15 +74,16 @@ __global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ i
 }
 
 __global__ __launch_bounds__(kB) void place_kernel(
-    const int32_t* __restrict__ idx, int64_t npicks, int64_t chunk, int nb, int k, int E,
-    int elog, int R, int W, const int32_t* __restrict__ hist, int32_t* __restrict__ expert_counts,
+    const int32_t* __restrict__ idx, int64_t npicks, int nsrc, int spc, int64_t src_picks,
+    int64_t chunk, int k, int E, int elog, int R, int W, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ wave_offsets,
     int32_t* __restrict__ pos, int32_t* __restrict__ row_token, moe_stats_t* __restrict__ stats,
     int sblock, int cap) {
   // cap >= 0: capacity-factor layout (every bucket exactly cap rows, an expert
   // keeps its first cap picks in token order, later ones are dropped);
-  // cap < 0: buckets sized by the counts.
+  // cap < 0: buckets sized by the counts. Capacity runs with one shard only.
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
@@ -79,10 +98,14 @@ __global__ __launch_bounds__(kB) void place_kernel(
   const int ep = 1 << elog;        // E rounded up to a power of two
   const int64_t rows = cap < 0 ? npicks : (int64_t)E * cap;  // rows of the send buffer
   const int nslice = kB >> elog;   // row slices of the hist matrix
+  // This block's shard: hist rows [h0, h1), rows from base, outputs at slice src.
+  int src;
+  int64_t p0, p1;
+  chunk_range(b, spc, nsrc, chunk, src_picks, src, p0, p1);
+  const int h0 = src * spc, h1 = h0 + spc;
+  const int64_t base = (int64_t)src * src_picks;
   // This chunk's first batch of ids, loaded now so that its latency overlaps
   // the histogram read and the scans below.
-  const int64_t p0 = (int64_t)b * chunk;
-  const int64_t p1 = (p0 + chunk < npicks) ? p0 + chunk : npicks;
   int e_next = (p0 + tid < p1) ? idx[p0 + tid] : -1;
 
   if (tid < E) {
@@ -90,18 +113,19 @@ __global__ __launch_bounds__(kB) void place_kernel(
     for (int q = 0; q < kWaves; ++q) wcnt[q][tid] = 0;
   }
 
-  // 1. Picks of each expert in earlier chunks and in all chunks. Thread
-  //    (s, e) = (tid >> elog, tid & (ep-1)) sums rows s, s+nslice, ...
+  // 1. Picks of each expert in the shard's earlier chunks and in all its
+  //    chunks. Thread (s, e) = (tid >> elog, tid & (ep-1)) sums rows h0+s,
+  //    h0+s+nslice, ...
   {
     const int e = tid & (ep - 1), s = tid >> elog;
     int pre = 0, all = 0;
     if (e < E) {
-      for (int r0 = s; r0 < nb; r0 += 4 * nslice) {
+      for (int r0 = h0 + s; r0 < h1; r0 += 4 * nslice) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = r0 + u * nslice;
-          v[u] = (r < nb) ? hist[(int64_t)r * E + e] : 0;
+          v[u] = (r < h1) ? hist[(int64_t)r * E + e] : 0;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -148,24 +172,29 @@ __global__ __launch_bounds__(kB) void place_kernel(
   if (tid < E) off[bucket_expert(tid, R, L, LW)] = excl;
   __syncthreads();
 
-  if (b == 0) {
+  if (b == h0) {  // the shard's first block publishes its counts and offsets
+    int32_t* ec = expert_counts + (int64_t)src * E;
+    int32_t* eo = expert_offsets + (int64_t)src * E;
+    int32_t* rc = rank_counts + (int64_t)src * W * R;
+    int32_t* ro = rank_offsets + (int64_t)src * W * R;
+    int32_t* wo = wave_offsets + (int64_t)src * (W + 1);
     if (tid < E) {
-      expert_counts[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];  // rows kept
-      expert_offsets[tid] = off[tid];
+      ec[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];  // rows kept
+      eo[tid] = (int32_t)(base + off[tid]);
     }
     for (int q = tid; q < W * R; q += kB) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
       int s = 0;
       for (int j = q * LW; j < q * LW + LW; ++j)
         s += cap >= 0 ? cap : cnt[bucket_expert(j, R, L, LW)];
-      rank_counts[q] = s;
-      rank_offsets[q] = off[bucket_expert(q * LW, R, L, LW)];
+      rc[q] = s;
+      ro[q] = (int32_t)(base + off[bucket_expert(q * LW, R, L, LW)]);
     }
     for (int w = tid; w <= W; w += kB)
-      wave_offsets[w] = (w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total;
+      wo[w] = (int32_t)(base + ((w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total));
   }
   // run[e]: picks of expert e before this chunk; with a capacity the rank
   // inside the bucket decides between a row and a drop, so it stays relative.
-  if (tid < E && cap < 0) run[tid] += off[tid];
+  if (tid < E && cap < 0) run[tid] += (int32_t)base + off[tid];
   __syncthreads();
 
   // 3. Stable ranks inside the chunk, 1024 picks per batch.
@@ -192,7 +221,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
       const int rel = run[e] + before + rk;
       const int P = cap < 0 ? rel : (rel < cap ? off[e] + rel : -1);
       pos[p] = P;
-      if (P >= 0 && (int64_t)P < rows) row_token[P] = (int32_t)(p / k);
+      if (row_token && P >= 0 && (int64_t)P < rows) row_token[P] = (int32_t)(p / k);
     } else if (p < p1) {
       pos[p] = -1;
     }
@@ -252,7 +281,7 @@ hipError_t launch_count(const int32_t* idx, int64_t npicks, int E, int32_t* hist
                         hipStream_t s) {
   const int64_t nb = num_chunks(npicks, E);
   if (nb == 0) return hipSuccess;
-  return launch(count_kernel, dim3((unsigned)nb), dim3(kB), 0, s, idx, npicks,
+  return launch(count_kernel, dim3((unsigned)nb), dim3(kB), 0, s, idx, 1, (int)nb, npicks,
                 chunk_picks(npicks, E), E, hist);
 }
 
@@ -265,8 +294,8 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
   // statistics block, if any, comes after the placing blocks.
   const int sblock = nb == 0 ? 1 : nb;
   const unsigned grid = (unsigned)sblock + (stats != nullptr ? 1u : 0u);
-  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, chunk, nb, k, E,
-                ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
+  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, 1, nb, npicks, chunk, k,
+                E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
                 rank_offsets, wave_offsets, pos, row_token, stats, sblock, cap);
 }
 
@@ -295,6 +324,36 @@ hipError_t launch_pad(int E, int R, int W, int cap, const int32_t* kept, int64_t
   if (cap == 0) return hipSuccess;
   return launch(pad_kernel, dim3((unsigned)E), dim3(kCopyBlock), 0, s, E, R, W, cap, kept,
                 (uint32_t)(row_bytes / 16), static_cast<v4u*>(send), row_token);
+}
+
+// Source shards: nsrc shards of src_picks picks, spc chunks each (spc >= 1).
+void source_chunks(int64_t src_picks, int E, int64_t& chunk, int& spc) {
+  const int64_t n = num_chunks(src_picks, E);
+  spc = n < 1 ? 1 : (int)n;
+  chunk = chunk_picks(src_picks, E);
+}
+
+hipError_t launch_count_sources(const int32_t* idx, int nsrc, int64_t src_picks, int E,
+                                int32_t* hist, hipStream_t s) {
+  int64_t chunk;
+  int spc;
+  source_chunks(src_picks, E, chunk, spc);
+  return launch(count_kernel, dim3((unsigned)(nsrc * spc)), dim3(kB), 0, s, idx, nsrc, spc,
+                src_picks, chunk, E, hist);
+}
+
+hipError_t launch_place_sources(const int32_t* idx, int nsrc, int64_t src_picks, int k, int E,
+                                int R, int W, const int32_t* hist, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* rank_counts,
+                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                                hipStream_t s) {
+  int64_t chunk;
+  int spc;
+  source_chunks(src_picks, E, chunk, spc);
+  return launch(place_kernel, dim3((unsigned)(nsrc * spc)), dim3(kB), 0, s, idx,
+                (int64_t)nsrc * src_picks, nsrc, spc, src_picks, chunk, k, E, ilog2_ceil(E), R, W,
+                hist, expert_counts, expert_offsets, rank_counts, rank_offsets, wave_offsets, pos,
+                (int32_t*)nullptr, (moe_stats_t*)nullptr, -1, -1);
 }
 
 }  // namespace moe

@@ -122,6 +122,35 @@ hipError_t launch_combine(const void* expert_out, int dtype, const float* w, con
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s);
 
+// Virtual source shards (the emulated exchange): nsrc shards of src_picks
+// picks; hist holds nsrc * source_chunks rows of E. Each shard's counts and
+// offsets go to its own slice ([nsrc][E], [nsrc][W*R], [nsrc][W+1]); positions
+// are absolute rows with shard s at [s*src_picks, (s+1)*src_picks).
+void source_chunks(int64_t src_picks, int E, int64_t& chunk, int& spc);
+hipError_t launch_count_sources(const int32_t* idx, int nsrc, int64_t src_picks, int E,
+                                int32_t* hist, hipStream_t s);
+hipError_t launch_place_sources(const int32_t* idx, int nsrc, int64_t src_picks, int k, int E,
+                                int R, int W, const int32_t* hist, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* rank_counts,
+                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                                hipStream_t s);
+// Receive side of the exchange and the grouped expert layout from the
+// per-source counts ([R][E]) and send counts ([R][W][R]).
+hipError_t launch_vsrc_plan(int R, int W, int E, const int32_t* src_counts,
+                            const int32_t* send_counts, int32_t* recv_counts,
+                            int32_t* recv_offsets, int32_t* expert_counts,
+                            int32_t* expert_offsets, hipStream_t s);
+// Block transpose send -> recv (back: recv -> send); rows = buffer rows.
+hipError_t launch_vsrc_exchange(const void* in, void* out, int64_t row_bytes, int64_t rows, int R,
+                                int W, const int32_t* send_offsets, const int32_t* recv_counts,
+                                const int32_t* recv_offsets, bool back, hipStream_t s);
+// Receive-side regroup recv -> grouped (back: grouped -> recv); tables holds
+// 3 * E * R int32.
+hipError_t launch_vsrc_regroup(const void* in, void* out, int64_t row_bytes, int64_t rows, int E,
+                               int R, int W, const int32_t* src_counts,
+                               const int32_t* recv_offsets, const int32_t* expert_offsets,
+                               int32_t* tables, bool back, hipStream_t s);
+
 // Fitted symmetric Dirichlet alpha of E <= 1024 counts into one device double.
 hipError_t launch_dirichlet_alpha(const int32_t* counts, int E, double* out, hipStream_t s);
 

@@ -212,7 +212,10 @@ int moe_dispatch_capacity(const moe_shape* shape, int32_t capacity, const void* 
 /* Identity-scaled experts (the experts of the synthetic workloads):
  * expert_out[n][:] = round_dtype((e(n) + 1) * send_buf[n][:]) for every row n
  * inside some expert's bucket [expert_offsets[e], + expert_counts[e]); other
- * rows are untouched. Rounding is to nearest, ties to even. */
+ * rows are untouched. Rounding is to nearest, ties to even. The buckets must
+ * lie in the (wave, rank, slot) order of the shape's R and W, as every dispatch
+ * entry writes them; plain expert order (moe_vsrc_regroup's grouped layout) is
+ * that order with W = 1. */
 int moe_expert_scale(const moe_shape* shape, const void* send_buf,
                      const int32_t* expert_offsets,
                      const int32_t* expert_counts, void* expert_out,
@@ -289,6 +292,76 @@ int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
  *         (alpha_out not 8-byte aligned), MOE_ERR_DEVICE. */
 int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_out,
                         moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Virtual-source exchange: the expert-parallel exchange of R ranks emulated on
+ * one device (MoE systems survey, crad.ict.ac.cn, section 1.1, EP flow steps
+ * 2-4; irregular AllToAll page, "sources of irregular a2a": every (source,
+ * destination) pair has its own row count, possibly 0, as an Alltoallv takes
+ * them). The T tokens split into R equal source shards (T % R == 0): source s
+ * holds tokens [s*T/R, (s+1)*T/R). Destination d owns experts d*L .. d*L+L-1,
+ * L = E/R; with W waves each (source, wave, destination) triple is one
+ * message. All counts and offsets are in rows; offsets are absolute rows of the
+ * concatenated buffers below, so a real Alltoallv of rank s would take the
+ * rows of its own slice, relative to its own first row. Buffers hold T*k rows
+ * of H elements (row layout as in moe_dispatch):
+ *   send     source s at rows [s*T/R*k, (s+1)*T/R*k) in the single-rank
+ *            dispatch layout of its own tokens (buckets in (wave, destination,
+ *            slot) order, token order inside a bucket); rows of dropped ids
+ *            (outside [0, E)) stay unused at the end of the source's range.
+ *   recv     the (destination, wave, source) messages back to back.
+ *   grouped  each destination's rows by local expert, then source, i.e. over
+ *            all destinations expert order and token order inside an expert.
+ * Rows past the last message or segment are left as they are.
+ * One call of each direction at a time per buffer set; all on `stream`. */
+
+/* Workspace bytes of moe_vsrc_dispatch and moe_vsrc_regroup for this shape
+ * (0 if the shape is invalid). */
+size_t moe_vsrc_workspace_bytes(const moe_shape* shape);
+
+/* Every source's dispatch at once plus the count exchange (one-rank dispatch
+ * of each shard, then the receive side's tables).
+ * x [T][H] in; topk_idx [T][k] in; send_buf [T*k][H] out.
+ * src_counts   [R][E] out: picks of expert e among source s's tokens.
+ * send_counts  [R][W][R] out: rows source s sends in wave w to destination d.
+ * send_offsets [R][W][R] out: first send row of that message.
+ * recv_counts  [R][W][R] out: rows destination d receives in wave w from
+ *              source s (= send_counts transposed).
+ * recv_offsets [R][W][R] out: first recv row of that message.
+ * expert_counts, expert_offsets [E] out: the grouped layout, buckets in
+ *              expert order (for moe_vsrc_regroup, moe_expert_swiglu, and
+ *              moe_expert_scale_rows with a shape of W = 1).
+ * pos [T][k] out: send row of each pick, -1 for dropped ids (combine input).
+ * Four launches: count, place (per shard), plan, copy. All pointers DEVICE.
+ * Errors: MOE_ERR_ARG (T % R != 0, shape outside the limits, null pointers),
+ *         MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
+int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                      void* send_buf, int32_t* src_counts, int32_t* send_counts,
+                      int32_t* send_offsets, int32_t* recv_counts, int32_t* recv_offsets,
+                      int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* The all-to-all as a block transpose of whole messages. direction 0
+ * (dispatch): in = send layout, out = recv layout; direction 1 (combine): in =
+ * recv layout, out = send layout (the reverse exchange of the expert rows).
+ * send_offsets, recv_counts, recv_offsets as written by moe_vsrc_dispatch;
+ * entries that do not describe rows inside the buffers are skipped. One launch.
+ * Errors: MOE_ERR_ARG (direction not 0/1, null pointers, shape), MOE_ERR_ALIGN
+ *         (buffers not 16-byte aligned), MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
+int moe_vsrc_exchange(const moe_shape* shape, int32_t direction, const void* in, void* out,
+                      const int32_t* send_offsets, const int32_t* recv_counts,
+                      const int32_t* recv_offsets, moe_stream_t stream);
+
+/* Receive-side regroup of every destination from its (wave, source) messages
+ * into (local expert, source) order. direction 0: in = recv layout, out =
+ * grouped layout; direction 1: in = grouped layout, out = recv layout.
+ * src_counts, recv_offsets, expert_offsets as written by moe_vsrc_dispatch.
+ * Two launches (segment table into the workspace, then the copy).
+ * Errors: as moe_vsrc_exchange, plus MOE_ERR_WORKSPACE. */
+int moe_vsrc_regroup(const moe_shape* shape, int32_t direction, const void* in, void* out,
+                     const int32_t* src_counts, const int32_t* recv_offsets,
+                     const int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                     moe_stream_t stream);
 
 /* Kernel timing hook for benchmarks (not a step of the path). After
  * moe_set_timing_events(starts, stops, n), the kernels this library launches

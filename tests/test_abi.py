@@ -190,3 +190,37 @@ def test_wave_planner_and_p95_match_the_oracle():
         assert abs(moe.link_p95(m, B, n) - oracle.link_p95(m, B, n)) <= 1e-12 * oracle.link_p95(m, B, n)
     assert moe.plan_waves(1.0, 1e-6, 0.0, 8)[0] == -1 and moe.wave_time(1.0, 1e-6, 1e9, 0) == -1.0
     assert moe.link_p95(1.0, 0.0, 4) == -1.0
+
+
+def test_vsrc_validation_and_workspace():
+    L = moe.lib()
+    sh = _shape(T=64, E=8, k=2, R=4, W=2)
+    ws = L.moe_vsrc_workspace_bytes(ctypes.byref(sh))
+    # per-source histogram rows + per-source offsets, or the 3*E*R segment table
+    assert ws >= 3 * 8 * 4 * 4 and ws % 256 == 0
+    tabs = [FAKE] * 8  # src_counts .. pos
+    x, idx, send = FAKE, FAKE, FAKE
+    uneven = _shape(T=66, E=8, k=2, R=4)
+    assert L.moe_vsrc_workspace_bytes(ctypes.byref(_shape(E=0))) == 0
+    assert L.moe_vsrc_dispatch(ctypes.byref(uneven), x, idx, send, *tabs, FAKE, 1 << 20,
+                               None) == ARG
+    assert L.moe_vsrc_dispatch(ctypes.byref(sh), x, idx, send, *tabs, FAKE, ws - 1,
+                               None) == WORKSPACE
+    assert L.moe_vsrc_dispatch(ctypes.byref(sh), x, idx, send, *tabs[:7], None, FAKE, ws,
+                               None) == ARG
+    assert L.moe_vsrc_dispatch(ctypes.byref(sh), ctypes.c_void_p((1 << 20) + 4), idx, send, *tabs,
+                               FAKE, ws, None) == ALIGN
+    for d in (-1, 2):
+        assert L.moe_vsrc_exchange(ctypes.byref(sh), d, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ARG
+        assert L.moe_vsrc_regroup(ctypes.byref(sh), d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                  None) == ARG
+    assert L.moe_vsrc_exchange(ctypes.byref(sh), 0, FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE,
+                               FAKE, FAKE, None) == ALIGN
+    assert L.moe_vsrc_exchange(ctypes.byref(sh), 0, FAKE, FAKE, None, FAKE, FAKE, None) == ARG
+    assert L.moe_vsrc_exchange(ctypes.byref(uneven), 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None) == ARG
+    assert L.moe_vsrc_regroup(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1,
+                              None) == WORKSPACE
+    # the largest configuration's tables fit comfortably
+    big = _shape(T=16384, H=7168, E=256, k=8, R=32, W=8)
+    assert 3 * 256 * 32 * 4 <= L.moe_vsrc_workspace_bytes(ctypes.byref(big)) < 1 << 20

@@ -1,0 +1,153 @@
+"""Virtual-source exchange through the C ABI against the oracle (MoE systems
+survey section 1.1, EP flow steps 2-4; irregular AllToAll page: Alltoallv
+counts and displacements per (source, destination) pair).
+
+The path: every source's dispatch and the count exchange (moe_vsrc_dispatch),
+the block-transpose all-to-all, the receive-side regroup, the (e+1)-scaled
+experts on the regrouped rows, then ungroup, the reverse all-to-all and the
+combine at the sources.
+
+Bars: tables, positions and every row buffer bit-exact; the combine
+stage-isolated bit-exact against the oracle's fp32 fma chain and inside the
+combine tolerance against the fp64 closed form."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_03_amd as moe
+import oracle
+import synth
+from test_gpu_parity import DEV, PARITY, assert_combine_tol, dev, host, shape_of
+
+pytestmark = pytest.mark.gpu
+
+TABLES = ("src_counts", "send_counts", "send_offsets", "recv_counts", "recv_offsets",
+          "expert_counts", "expert_offsets", "pos")
+
+CASES = {
+    **{n: PARITY[n] for n in ("tiny", "zipf", "dirichlet_waves_T512", "decode_hot")},
+    "tiny_R2_W2": synth.WORKLOADS["tiny"].with_(R=2, W=2),
+    "tiny_R8": synth.WORKLOADS["tiny"].with_(R=8),
+    "zipf_R1": synth.WORKLOADS["zipf"].with_(T=1024, R=1),
+    "zipf_R4_W2": synth.WORKLOADS["zipf"].with_(T=2048, R=4, W=2),
+    # several placing chunks per source with a ragged last one
+    "zipf_T12000_R4": synth.WORKLOADS["zipf"].with_(T=12000, H=256, R=4),
+    "local_layer_T1024_R4_scaled": synth.WORKLOADS["local_layer"].with_(T=1024, R=4,
+                                                                         expert="scale"),
+}
+
+
+def run_vsrc(wl, x, idx, w32):
+    shape = shape_of(wl)
+    out = moe.alloc_vsrc(shape, DEV)
+    moe.vsrc_dispatch(dev(x), dev(idx), shape, out)
+    moe.vsrc_exchange(out["send_buf"], out["recv_buf"], shape, out, 0)
+    moe.vsrc_regroup(out["recv_buf"], out["grouped"], shape, out, 0)
+    # the grouped rows are in plain expert order: the (wave, rank, slot) order of W = 1
+    eo = moe.expert_scale_rows(out["grouped"], out["expert_offsets"], out["expert_counts"],
+                               shape_of(wl.with_(W=1)))
+    back_recv = torch.empty_like(out["recv_buf"])
+    moe.vsrc_regroup(eo, back_recv, shape, out, 1)
+    back_send = torch.empty_like(out["send_buf"])
+    moe.vsrc_exchange(back_recv, back_send, shape, out, 1)
+    y = moe.combine_rows(back_send, dev(w32), out["pos"], shape)
+    torch.cuda.synchronize()
+    return out, eo, back_recv, back_send, y
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_vsrc_parity(name):
+    wl = CASES[name]
+    print(f"[vsrc] {name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W}", flush=True)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    w32 = w.astype(np.float32)
+    ref = oracle.vsrc_exchange(x, idx, w, wl.E, wl.R, wl.W)
+    out, eo, back_recv, back_send, y = run_vsrc(wl, x, idx, w32)
+    for key in TABLES:
+        np.testing.assert_array_equal(host(out[key]), ref[key], err_msg=key)
+    n = int(ref["expert_counts"].sum())
+    np.testing.assert_array_equal(host(out["send_buf"]), ref["send"])
+    np.testing.assert_array_equal(host(out["recv_buf"])[:n], ref["recv"][:n])
+    np.testing.assert_array_equal(host(out["grouped"])[:n], ref["grouped"][:n])
+    np.testing.assert_array_equal(host(eo)[:n], ref["expert_out"][:n])
+    np.testing.assert_array_equal(host(back_recv)[:n], ref["back_recv"][:n])
+    used = ref["pos"][ref["pos"] >= 0]
+    np.testing.assert_array_equal(host(back_send)[used], ref["back_send"][used])
+    np.testing.assert_array_equal(host(y), ref["y"])
+    y64, _ = oracle.scaled_tokens(x, idx, w, wl.E, np.arange(wl.T))
+    assert_combine_tol(host(y), y64, wl.dtype)
+
+
+def test_vsrc_dropped_ids_and_empty_batch():
+    wl = synth.WORKLOADS["zipf"].with_(T=512, R=8)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    g = np.random.default_rng(7)
+    idx[g.random(idx.shape) < 0.1] = -1
+    idx[:64] = -1  # one whole source sends nothing
+    ref = oracle.vsrc_exchange(x, idx, w, wl.E, wl.R, wl.W)
+    out, eo, back_recv, back_send, y = run_vsrc(wl, x, idx, w.astype(np.float32))
+    for key in TABLES:
+        np.testing.assert_array_equal(host(out[key]), ref[key], err_msg=key)
+    n = int(ref["expert_counts"].sum())
+    used = ref["pos"][ref["pos"] >= 0]
+    np.testing.assert_array_equal(host(out["send_buf"])[used], ref["send"][used])
+    np.testing.assert_array_equal(host(out["grouped"])[:n], ref["grouped"][:n])
+    np.testing.assert_array_equal(host(y), ref["y"])
+
+    empty = wl.with_(T=0)
+    shape = shape_of(empty)
+    o = moe.alloc_vsrc(shape, DEV)
+    x0 = torch.zeros((0, wl.H), dtype=torch.bfloat16, device=DEV)
+    i0 = torch.zeros((0, wl.k), dtype=torch.int32, device=DEV)
+    moe.vsrc_dispatch(x0, i0, shape, o)
+    moe.vsrc_exchange(o["send_buf"], o["recv_buf"], shape, o, 0)
+    moe.vsrc_regroup(o["recv_buf"], o["grouped"], shape, o, 0)
+    torch.cuda.synchronize()
+    for key in ("src_counts", "send_counts", "send_offsets", "recv_counts", "recv_offsets",
+                "expert_counts", "expert_offsets"):
+        assert (host(o[key]) == 0).all(), key
+
+
+@pytest.mark.parametrize("name", ["zipf", "dirichlet_waves"])
+def test_vsrc_full_size(name):
+    """Full-size configuration in the benchmark's launch setup: every table in
+    full and, for the largest one, the row buffers on a seeded sample of rows
+    (rows identified through a token-id stand-in of x on the oracle side)."""
+    wl = synth.WORKLOADS[name].with_(expert="scale")
+    print(f"[vsrc full] {name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W}",
+          flush=True)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    tok = np.repeat(np.arange(wl.T, dtype=np.float32)[:, None], 4, axis=1)
+    ref = oracle.vsrc_exchange(tok, idx, w, wl.E, wl.R, wl.W)
+    out, eo, back_recv, back_send, y = run_vsrc(wl, x, idx, w.astype(np.float32))
+    for key in TABLES:
+        np.testing.assert_array_equal(host(out[key]), ref[key], err_msg=key)
+    n = int(ref["expert_counts"].sum())
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, 3000)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    for buf, key in (("send_buf", "send"), ("recv_buf", "recv"), ("grouped", "grouped")):
+        toks = ref[key][rows, 0].astype(np.int64)
+        np.testing.assert_array_equal(host(out[buf][ridx]), x[toks], err_msg=buf)
+    # returned expert rows at the sources: (e+1) * x of that pick, checked on sampled tokens
+    toks = np.unique(np.concatenate([[0, wl.T - 1], g.integers(0, wl.T, 300)]))
+    y64, yq = oracle.scaled_tokens(x, idx, w, wl.E, toks, w32=w.astype(np.float32))
+    yg = host(y[torch.from_numpy(toks).to(DEV)])
+    assert_combine_tol(yg, y64, wl.dtype)
+    np.testing.assert_array_equal(yg, yq)
+
+
+def test_vsrc_grouped_equals_one_rank_dispatch():
+    """W = 1: the regrouped rows of all destinations are the single-rank
+    dispatch buffer (buckets in expert order), whatever R is."""
+    wl = synth.WORKLOADS["zipf"].with_(T=1024)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    one = moe.dispatch(dev(x), dev(idx), wl.E, wl.R, 1)
+    out, *_ = run_vsrc(wl, x, idx, w.astype(np.float32))
+    n = int(host(one["expert_counts"]).sum())
+    assert torch.equal(out["grouped"][:n], one["send_buf"][:n])
+    assert torch.equal(out["expert_offsets"], one["expert_offsets"])
