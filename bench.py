@@ -378,6 +378,7 @@ def main() -> int:
     STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
     kernel_of = {st: "+".join(dict.fromkeys(kn for c in calls for g, kn in c[2] if g == st))
                  for st in STAGES_RUN}
+    launches_of = {st: sum(1 for c in calls for g, _ in c[2] if g == st) for st in STAGES_RUN}
 
     hipev = HipEvents()
     set_events = L.moe_set_timing_events
@@ -539,11 +540,15 @@ def main() -> int:
                           "stats")
               if n in STAGES_RUN and not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
+    # per launch: a stage may launch its kernel more than once a step (the
+    # exchange and the regroup run forward and back), bytes and time both scale
+    nl = launches_of[dom]
     roofline = {"bound": "hbm", "kernel": kernel_of[dom],
                 "achieved": round(gbs(dom, stage_ms[dom]), 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs(dom, stage_ms[dom]) / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(wl.name, kernel_of[dom]), "bytes_per_launch": nbytes[dom],
-                "avg_us": round(stage_ms[dom] * 1e3, 2)}
+                "traffic": stored_traffic(wl.name, kernel_of[dom]),
+                "bytes_per_launch": nbytes[dom] // nl, "launches_per_step": nl,
+                "avg_us": round(stage_ms[dom] * 1e3 / nl, 2)}
     if swiglu and stage_ms["expert"] > stage_ms[dom]:
         tf = ffn_flops(wl) / (stage_ms["expert"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": kernel_of["expert"], "achieved": round(tf, 1),
