@@ -84,6 +84,9 @@ def parse_args():
                     help="also time K steps replayed from one captured HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="separate route / dispatch_index / stats calls (7 kernels a step)")
+    ap.add_argument("--wave-sweep", action="store_true",
+                    help="local layer: wave-pipelined dispatch + FFN for every W dividing L, "
+                         "two streams vs one; T(W) and the fitted wave model")
     ap.add_argument("--vsrc", action="store_true",
                     help="the expert-parallel exchange of R virtual source ranks on one device")
     ap.add_argument("--capacity-factor", type=float, default=None,
@@ -217,6 +220,69 @@ def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) ->
             "sample": f"{sample}; {t_used:.1f} s on {platform.processor() or platform.machine()}"}
 
 
+def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
+    """T(W) of the wave-pipelined local layer: per W dividing L, K steps of
+    route+index (fused) -> per-wave gather dispatch on a copy stream overlapped
+    with the per-wave FFN on the compute stream -> combine; and the same
+    launches on one stream. Fits T(W) = a*W + b + m/W (the page's
+    W*alpha + M/beta + M/(W*beta) plus the stages outside the pipeline)."""
+    dev = torch.device("cuda:0")
+    T, H, E, k, R = wl.T, wl.H, wl.E, wl.k, wl.R
+    L = E // R
+    logits, x = to_dev(logits_np), to_dev(x_np)
+    import synth
+    gu_np, dn_np = synth.swiglu_weights(wl)
+    gu, dn = to_dev(gu_np), to_dev(dn_np)
+    side = torch.cuda.Stream()
+    res = {"W": [], "ms_two_streams": [], "ms_one_stream": []}
+    for W in [d for d in range(1, L + 1) if L % d == 0]:
+        shape = moe.Shape(T, H, E, k, R, W, torch.bfloat16)
+        buf = moe.alloc_dispatch(shape, dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+        eo = torch.empty_like(buf["send_buf"])
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
+                         device=dev)
+
+        def step(two):
+            moe.route_index(logits, shape, buf, idx, wt)
+            moe.swiglu_waves(x, buf, shape, gu, dn, expert_out=eo, workspace=ws,
+                             copy_stream=side if two else None)
+            moe.combine(eo, wt, buf["pos"], shape, y=y)
+
+        row = []
+        for two in (True, False):
+            for _ in range(args.warmup):
+                step(two)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step(two)
+            torch.cuda.synchronize()
+            row.append((time.perf_counter() - t0) * 1e3 / args.steps)
+        res["W"].append(W)
+        res["ms_two_streams"].append(round(row[0], 4))
+        res["ms_one_stream"].append(round(row[1], 4))
+        print(f"[bench] W={W}: {row[0]:.4f} ms (two streams), {row[1]:.4f} ms (one)",
+              file=sys.stderr, flush=True)
+    Ws = np.array(res["W"], float)
+    t = np.array(res["ms_two_streams"]) * 1e-3
+    A = np.stack([Ws, np.ones_like(Ws), 1.0 / Ws], axis=1)
+    (a, b, m), *_ = np.linalg.lstsq(A, t, rcond=None)
+    M = T * k * H * 2  # bytes dispatched per step (the gathered rows)
+    fit = {"alpha_us": round(a * 1e6, 3), "const_us": round(b * 1e6, 2), "m_us": round(m * 1e6, 2)}
+    if a > 0 and m > 0:
+        beta = M / m
+        w_plan, _ = moe.plan_waves(M, a, beta, L)
+        fit.update(beta_GBs=round(beta / 1e9, 1), W_star=round(float(np.sqrt(m / a)), 2),
+                   W_plan=w_plan)
+    res["fit"] = fit
+    res["W_best_measured"] = int(Ws[int(np.argmin(t))])
+    res["message_bytes"] = M
+    return res
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +313,27 @@ def main() -> int:
         return torch.from_numpy(a).to(dev)
 
     logits_np, x_np = synth.logits(wl), synth.hidden(wl)
+    if args.wave_sweep:
+        if not swiglu:
+            print("--wave-sweep runs the SwiGLU local layer (--workload local_layer)",
+                  file=sys.stderr)
+            return 2
+        ws_res = wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np)
+        best = ws_res["W"].index(ws_res["W_best_measured"])
+        ms = ws_res["ms_two_streams"][best]
+        result = {
+            "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+            "data": "synthetic (seeded logits and hidden states; random-init SwiGLU expert weights)",
+            "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
+                       "waves": ws_res["W_best_measured"], "I": wl.I, "expert": wl.expert,
+                       "step": "route+index (moe_route_index) + per wave: gather dispatch (copy "
+                               "stream) -> FFN (compute stream) + combine"},
+            "wave_sweep": ws_res,
+        }
+        print(json.dumps(result), flush=True)
+        return 0
     logits, x = to_dev(logits_np), to_dev(x_np)
     shape = moe.Shape(T, H, E, k, R, W, tdt)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)

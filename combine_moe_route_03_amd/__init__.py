@@ -66,6 +66,8 @@ SIGNATURES = {
     "moe_dispatch_capacity": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_swiglu_waves": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          ctypes.c_size_t, _vp, _vp], ctypes.c_int),
     "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
     "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp], ctypes.c_int),
@@ -402,6 +404,32 @@ def expert_swiglu(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
                                    _ptr(expert_counts), _ptr(w_gate_up), _ptr(w_down),
                                    _ptr(expert_out), _ptr(workspace), workspace.numel(),
                                    _stream()), "moe_expert_swiglu")
+    return expert_out
+
+
+def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tensor,
+                 w_down: torch.Tensor, expert_out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None,
+                 copy_stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Wave-pipelined dispatch + SwiGLU FFN: per wave a gather of its rows into
+    out["send_buf"] on `copy_stream`, then the FFN of its experts on the
+    current stream after an event. `out` holds a dispatch index of `shape`
+    (row_token, wave_offsets, expert offsets/counts). No copy stream: the same
+    launches on the current stream."""
+    I = w_down.shape[2]
+    send_buf = out["send_buf"]
+    expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
+    if workspace is None:
+        workspace = _empty((max(expert_swiglu_workspace_bytes(shape, I), 1),), torch.uint8,
+                           send_buf.device)
+    compute = _stream()
+    copy = compute if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    sh = shape.c()
+    _check(lib().moe_swiglu_waves(
+        ctypes.byref(sh), I, _ptr(x), _ptr(out["row_token"]), _ptr(out["wave_offsets"]),
+        _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(w_gate_up), _ptr(w_down),
+        _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), compute, copy),
+        "moe_swiglu_waves")
     return expert_out
 
 

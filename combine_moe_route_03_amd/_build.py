@@ -14,7 +14,7 @@ OBJDIR = os.path.join(ROOT, "_build", "csrc")
 LIB = os.path.join(PKG, "libmoe_route.so")
 
 SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "combine.hip", "expert.hip", "ffn.hip",
-           "stats.hip", "alpha.hip", "exchange.hip"]
+           "stats.hip", "alpha.hip", "exchange.hip", "waves.hip"]
 
 # -packed-fp32-ops off: plain fp32 VALU code only (no v_pk_*_f32 forms).
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

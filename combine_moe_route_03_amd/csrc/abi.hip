@@ -261,10 +261,13 @@ size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I) {
   return size_t((bytes < 256 ? 256 : bytes + 255) / 256 * 256);
 }
 
-int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
+}  // extern "C"
+
+namespace {
+int check_swiglu_args(const moe_shape* shape, int32_t I, const void* send_buf,
                       const int32_t* expert_offsets, const int32_t* expert_counts,
-                      const void* w_gate_up, const void* w_down, void* expert_out,
-                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+                      const void* w_gate_up, const void* w_down, const void* expert_out,
+                      const void* workspace, size_t workspace_bytes_given) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (shape->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -282,10 +285,41 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
     return MOE_ERR_ALIGN;
   if (int64_t(shape->T) * shape->k * I >= kIndexLimit) return MOE_ERR_ARG;
   if (workspace_bytes_given < moe_expert_swiglu_workspace_bytes(shape, I)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
+                      const int32_t* expert_offsets, const int32_t* expert_counts,
+                      const void* w_gate_up, const void* w_down, void* expert_out,
+                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+  const int st = check_swiglu_args(shape, I, send_buf, expert_offsets, expert_counts, w_gate_up,
+                                   w_down, expert_out, workspace, workspace_bytes_given);
+  if (st != MOE_OK) return st;
   const int64_t rows = int64_t(shape->T) * shape->k;
   return status_of(moe::launch_expert_swiglu(send_buf, rows, shape->H, I, shape->E,
                                              expert_offsets, expert_counts, w_gate_up, w_down,
                                              workspace, expert_out, as_stream(stream)));
+}
+
+int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
+                     const int32_t* wave_offsets, const int32_t* expert_offsets,
+                     const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
+                     void* send_buf, void* expert_out, void* workspace,
+                     size_t workspace_bytes_given, moe_stream_t compute_stream,
+                     moe_stream_t copy_stream) {
+  int st = check_swiglu_args(shape, I, send_buf, expert_offsets, expert_counts, w_gate_up,
+                             w_down, expert_out, workspace, workspace_bytes_given);
+  if (st != MOE_OK) return st;
+  if (!wave_offsets) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!x || !row_token)) return MOE_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(row_token, 4) || !aligned(wave_offsets, 4)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_swiglu_waves(
+      x, shape->T, shape->k, shape->H, I, shape->E, shape->R, shape->W, row_token, wave_offsets,
+      expert_offsets, expert_counts, w_gate_up, w_down, send_buf, workspace, expert_out,
+      as_stream(compute_stream), as_stream(copy_stream)));
 }
 
 int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_out,

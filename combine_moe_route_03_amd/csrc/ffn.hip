@@ -82,7 +82,8 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* l
 template <bool kGateUp, int BM, int BN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
-    const int32_t* __restrict__ cnts, int E, const uint16_t* __restrict__ Bw, int64_t bstride,
+    const int32_t* __restrict__ cnts, int E, int sg, int sstride, int sbase,
+    const uint16_t* __restrict__ Bw, int64_t bstride,
     int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int gm) {
   constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
   constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave per K step
@@ -108,12 +109,15 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   int ntile = 0;
   if (wid == 0) {
     if (lane == 0) info[0] = -1;  // no tile, unless a lane below finds one
-    // Expert e owns m-tiles [base_e, base_e + ceil(cnt[e] / BM)); lane l scans
-    // experts [l*c, l*c + c).
+    // The launch covers E experts: the i-th is expert (i / sg) * sstride + sbase
+    // + i % sg (all experts: sg = E, sbase = 0; one wave of W: sg = L/W slots
+    // of each of the R ranks). Expert i owns m-tiles
+    // [base_i, base_i + ceil(cnt / BM)); lane l scans experts [l*c, l*c + c).
+    const auto eid = [&](int i) { return (i / sg) * sstride + sbase + i % sg; };
     const int c = (E + kWave - 1) / kWave;
     const int e0 = lane * c, e1 = (e0 + c < E) ? e0 + c : E;
     int mine = 0;
-    for (int e = e0; e < e1; ++e) mine += (cnts[e] + BM - 1) / BM;
+    for (int i = e0; i < e1; ++i) mine += (cnts[eid(i)] + BM - 1) / BM;
     int incl = mine;
     for (int o = 1; o < kWave; o <<= 1) {
       const int y = __shfl_up(incl, o);
@@ -133,7 +137,8 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     }
     int base = incl - mine;
     if (live && mtg >= base && mtg < incl) {
-      for (int e = e0; e < e1; ++e) {
+      for (int i = e0; i < e1; ++i) {
+        const int e = eid(i);
         const int mt = (cnts[e] + BM - 1) / BM;
         if (mtg < base + mt) {
           const int m0 = (mtg - base) * BM;
@@ -312,35 +317,45 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
 }
 
 template <int BM, int BN, int OCC>
-hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, const int32_t* offs,
-                   const int32_t* cnts, const void* w_gate_up, const void* w_down, void* hbuf,
-                   void* out, hipStream_t s) {
+hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, int sstride,
+                   int sbase, const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
+                   const void* w_down, void* hbuf, void* out, hipStream_t s) {
   const int mtb = (int)((rows + BM - 1) / BM + E);  // each expert adds at most one partial tile
   auto grid_of = [&](int ntiles) {
     return (unsigned)(kXCD * ((mtb + kXCD - 1) / kXCD) * ntiles);
   };
   const int nt1 = I / (BN / 2);
   hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
-                          static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E,
-                          static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
+                          static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E, sg,
+                          sstride, sbase, static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
                           static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, kGroupM);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
   return launch(ffn_gemm_kernel<false, BM, BN, OCC>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
-                static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E,
-                static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
+                static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E, sg, sstride,
+                sbase, static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
                 static_cast<uint16_t*>(out), (int64_t)H, nt2, kGroupM);
 }
 
 }  // namespace
 
+hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, int I, int n,
+                                       int sg, int sstride, int sbase, const int32_t* offs,
+                                       const int32_t* cnts, const void* w_gate_up,
+                                       const void* w_down, void* hbuf, void* out, hipStream_t s) {
+  if (rows == 0 || n == 0) return hipSuccess;
+  if (I % 128 == 0 && H % 256 == 0)
+    return run_ffn<256, 256, 1>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts, w_gate_up,
+                                w_down, hbuf, out, s);
+  return run_ffn<128, 128, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts, w_gate_up,
+                              w_down, hbuf, out, s);
+}
+
 hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, int E,
                                 const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                 const void* w_down, void* hbuf, void* out, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  if (I % 128 == 0 && H % 256 == 0)
-    return run_ffn<256, 256, 1>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
-  return run_ffn<128, 128, 2>(send, rows, H, I, E, offs, cnts, w_gate_up, w_down, hbuf, out, s);
+  return launch_expert_swiglu_subset(send, rows, H, I, E, E, 0, 0, offs, cnts, w_gate_up, w_down,
+                                     hbuf, out, s);
 }
 
 }  // namespace moe

@@ -161,6 +161,25 @@ hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, in
                                 const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                 const void* w_down, void* hbuf, void* out, hipStream_t s);
 
+// The FFN on a subset of n experts: the i-th is expert (i / sg) * sstride +
+// sbase + i % sg (all E experts: n = sg = E, sstride = sbase = 0).
+hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, int I, int n,
+                                       int sg, int sstride, int sbase, const int32_t* offs,
+                                       const int32_t* cnts, const void* w_gate_up,
+                                       const void* w_down, void* hbuf, void* out, hipStream_t s);
+
+// Wave-pipelined local layer: per wave, gather dispatch of its rows on `copy`,
+// then the FFN of its experts on `compute` after an event (copy == compute:
+// the same work, serialised).
+hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int32_t* wave_offsets,
+                              int w, int T, int64_t rows_max, int64_t row_bytes, void* send,
+                              hipStream_t s);
+hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
+                               const int32_t* row_token, const int32_t* wave_offsets,
+                               const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
+                               const void* w_down, void* send, void* hbuf, void* out,
+                               hipStream_t compute, hipStream_t copy);
+
 // Expert id of the j-th bucket when buckets run in (wave, rank, slot) order:
 // L = E / R slots per rank, LW = L / W slots per wave.
 __host__ __device__ __forceinline__ int bucket_expert(int j, int R, int L, int LW) {

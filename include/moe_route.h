@@ -293,6 +293,30 @@ int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
 int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_out,
                         moe_stream_t stream);
 
+/* Wave-pipelined local layer (irregular AllToAll page, "Wave-Scheduled"
+ * pipelining: the experts in W waves, each wave's dispatch -> compute, the
+ * next wave's dispatch overlapping this wave's compute). Wave w owns local
+ * slots [w*L/W, (w+1)*L/W) of every rank, i.e. the send rows
+ * [wave_offsets[w], wave_offsets[w+1]) written by a dispatch-index call with
+ * the same shape. For each wave, in order: on copy_stream the gather dispatch
+ * send_buf[r] = x[row_token[r]] of the wave's rows, an event, and on
+ * compute_stream (after that event) the moe_expert_swiglu arithmetic on the
+ * wave's R*L/W experts. Results are bit-identical to moe_dispatch_copy +
+ * moe_expert_swiglu. copy_stream first waits for the work already queued on
+ * compute_stream; when this call returns, compute_stream carries every wave's
+ * FFN (follow with moe_combine there). copy_stream == compute_stream runs the
+ * same launches serialised. The library keeps W+1 reusable events per host
+ * thread (created on first use). Arguments as moe_expert_swiglu, plus x
+ * [T][H], row_token [T*k], wave_offsets [W+1] (DEVICE). 3W launches: W
+ * gathers and 2W FFN kernels.
+ * Errors: as moe_expert_swiglu; MOE_ERR_ARG also for null x / row_token /
+ *         wave_offsets. */
+int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
+                     const int32_t* wave_offsets, const int32_t* expert_offsets,
+                     const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
+                     void* send_buf, void* expert_out, void* workspace, size_t workspace_bytes,
+                     moe_stream_t compute_stream, moe_stream_t copy_stream);
+
 /* ---------------------------------------------------------------------------
  * Virtual-source exchange: the expert-parallel exchange of R ranks emulated on
  * one device (MoE systems survey, crad.ict.ac.cn, section 1.1, EP flow steps

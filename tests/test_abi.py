@@ -224,3 +224,19 @@ def test_vsrc_validation_and_workspace():
     # the largest configuration's tables fit comfortably
     big = _shape(T=16384, H=7168, E=256, k=8, R=32, W=8)
     assert 3 * 256 * 32 * 4 <= L.moe_vsrc_workspace_bytes(ctypes.byref(big)) < 1 << 20
+
+
+def test_swiglu_waves_validation():
+    L = moe.lib()
+    sh = _shape(T=64, H=256, E=8, k=2, R=1, W=2)
+    ws = L.moe_expert_swiglu_workspace_bytes(ctypes.byref(sh), 128)
+    # x, row_token, wave_offsets, offsets, counts, w_gate_up, w_down, send, out, workspace
+    a = [FAKE] * 10
+    ok = lambda *v: L.moe_swiglu_waves(ctypes.byref(v[0]), v[1], *v[2], ws if len(v) < 4 else v[3],  # noqa: E731
+                                       None, None)
+    assert ok(sh, 100, a) == ARG                              # I % 64 != 0
+    assert ok(_shape(T=64, H=256, E=8, k=2, R=1, W=2, dtype=moe.MOE_F32), 128, a) == UNSUPPORTED
+    assert ok(sh, 128, [FAKE, FAKE, None] + a[3:]) == ARG     # no wave_offsets
+    assert ok(sh, 128, [None] + a[1:]) == ARG                 # no x
+    assert ok(sh, 128, [ctypes.c_void_p((1 << 20) + 4)] + a[1:]) == ALIGN
+    assert ok(sh, 128, a, ws - 1) == WORKSPACE
