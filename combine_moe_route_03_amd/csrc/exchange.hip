@@ -197,7 +197,7 @@ __device__ __forceinline__ int64_t other_index(int i, int R, int W) {
 // find the segments of its first and last row; the segments in between
 // (their key-side begin and end and other-side begin) are staged in LDS, so
 // each thread's walk from segment to segment reads LDS. A block spanning more
-// than kSpan segments (many empty ones) walks the tables in global memory.
+// than kSpan segments (many empty ones) binary-searches the tables in memory.
 template <bool kBack, bool kTranspose>
 __global__ __launch_bounds__(kSegBlock) void segcopy_kernel(
     const v4u* __restrict__ in, v4u* __restrict__ out, const int32_t* __restrict__ key,
@@ -252,7 +252,19 @@ __global__ __launch_bounds__(kSegBlock) void segcopy_kernel(
       if ((int64_t)q >= qe) continue;
       const uint32_t rq = q / nvec;
       const int64_t r = rq, col = q - rq * nvec;
-      while (seg + 1 < span && r >= seg_end(seg)) ++seg;
+      if (staged) {
+        while (seg + 1 < span && r >= seg_end(seg)) ++seg;
+      } else {
+        // many (mostly empty) segments: binary search for the last one that
+        // begins at or before r, from the thread's current one
+        int lo = seg, hi = span - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (seg_beg(mid) <= r) lo = mid;
+          else hi = mid - 1;
+        }
+        seg = lo;
+      }
       const int64_t b = seg_beg(seg), o = seg_oth(seg) + (r - b);
       if (r < b || r >= seg_end(seg) || o < 0 || o >= other_rows) continue;  // inconsistent tables
       src[u] = (kBack ? r : o) * nvec + col;

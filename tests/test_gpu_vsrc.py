@@ -151,3 +151,39 @@ def test_vsrc_grouped_equals_one_rank_dispatch():
     n = int(host(one["expert_counts"]).sum())
     assert torch.equal(out["grouped"][:n], one["send_buf"][:n])
     assert torch.equal(out["expert_offsets"], one["expert_offsets"])
+
+
+EDGE = {
+    # 65536 (expert, source) segments and 16-byte rows: one block's 2048 rows
+    # span far more than the 512 segments staged in LDS (walk in memory)
+    "E1024_R64_H4": synth.Workload("vsrc_edge", T=640, H=4, dtype="f32", E=1024, k=4, R=64, W=1,
+                                   routing="iid", expert="scale", seed=21),
+    # one expert per rank (L = 1)
+    "E16_R16_L1": synth.Workload("vsrc_edge", T=64, H=64, dtype="bf16", E=16, k=3, R=16, W=1,
+                                 routing="zipf0.5", expert="scale", seed=22),
+    # one slot per wave (W = L)
+    "E32_R4_W8": synth.Workload("vsrc_edge", T=96, H=128, dtype="bf16", E=32, k=4, R=4, W=8,
+                                routing="iid", expert="scale", seed=23),
+    # one token per source
+    "T8_R8": synth.Workload("vsrc_edge", T=8, H=256, dtype="f32", E=64, k=8, R=8, W=2,
+                            routing="iid", expert="scale", seed=24),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_vsrc_edge_shapes(name):
+    wl = EDGE[name]
+    print(f"[vsrc edge] {name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W}",
+          flush=True)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    w32 = w.astype(np.float32)
+    ref = oracle.vsrc_exchange(x, idx, w, wl.E, wl.R, wl.W)
+    out, eo, back_recv, back_send, y = run_vsrc(wl, x, idx, w32)
+    for key in TABLES:
+        np.testing.assert_array_equal(host(out[key]), ref[key], err_msg=key)
+    n = int(ref["expert_counts"].sum())
+    np.testing.assert_array_equal(host(out["recv_buf"])[:n], ref["recv"][:n])
+    np.testing.assert_array_equal(host(out["grouped"])[:n], ref["grouped"][:n])
+    np.testing.assert_array_equal(host(back_recv)[:n], ref["back_recv"][:n])
+    np.testing.assert_array_equal(host(y), ref["y"])
