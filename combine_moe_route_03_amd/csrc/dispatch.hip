@@ -28,14 +28,15 @@
 // output; with one shard this is the plain single-rank dispatch.
 #include "block_stats.h"
 #include "device.h"
+#include "index_tables.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
 constexpr int kB = kIndexBlock;  // 1024 threads, 16 waves
-constexpr int kWaves = kB / kWave;
-constexpr int kMaxE = 1024;
+constexpr int kWaves = kIndexWaves;
+constexpr int kMaxE = kIndexMaxE;
 
 // Picks [p0, p1) of block b: chunk b - src*spc of shard src.
 __device__ __forceinline__ void chunk_range(int b, int spc, int nsrc, int64_t chunk,
@@ -153,45 +154,14 @@ __global__ __launch_bounds__(kB) void place_kernel(
     return;
   }
 
-  // 2. Exclusive scan of the bucket sizes in (wave, rank, slot) order; thread j
-  //    owns bucket j. With a capacity every bucket is cap rows long.
-  const int cj = (tid < E) ? (cap >= 0 ? cap : cnt[bucket_expert(tid, R, L, LW)]) : 0;
-  int incl = cj;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == kWave - 1) part[wid] = incl;
-  __syncthreads();
-  int excl = incl - cj, total = 0;
-#pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    excl += (q < wid) ? part[q] : 0;
-    total += part[q];
-  }
-  if (tid < E) off[bucket_expert(tid, R, L, LW)] = excl;
-  __syncthreads();
-
-  if (b == h0) {  // the shard's first block publishes its counts and offsets
-    int32_t* ec = expert_counts + (int64_t)src * E;
-    int32_t* eo = expert_offsets + (int64_t)src * E;
-    int32_t* rc = rank_counts + (int64_t)src * W * R;
-    int32_t* ro = rank_offsets + (int64_t)src * W * R;
-    int32_t* wo = wave_offsets + (int64_t)src * (W + 1);
-    if (tid < E) {
-      ec[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];  // rows kept
-      eo[tid] = (int32_t)(base + off[tid]);
-    }
-    for (int q = tid; q < W * R; q += kB) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
-      int s = 0;
-      for (int j = q * LW; j < q * LW + LW; ++j)
-        s += cap >= 0 ? cap : cnt[bucket_expert(j, R, L, LW)];
-      rc[q] = s;
-      ro[q] = (int32_t)(base + off[bucket_expert(q * LW, R, L, LW)]);
-    }
-    for (int w = tid; w <= W; w += kB)
-      wo[w] = (int32_t)(base + ((w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total));
-  }
+  // 2. Bucket offsets in (wave, rank, slot) order; with a capacity every
+  //    bucket is cap rows long. The shard's first block publishes its counts
+  //    and offsets.
+  const int total = bucket_scan(cnt, E, R, W, cap, off, part);
+  if (b == h0)
+    publish_index(cnt, off, total, E, R, W, cap, base, expert_counts + (int64_t)src * E,
+                  expert_offsets + (int64_t)src * E, rank_counts + (int64_t)src * W * R,
+                  rank_offsets + (int64_t)src * W * R, wave_offsets + (int64_t)src * (W + 1));
   // run[e]: picks of expert e before this chunk; with a capacity the rank
   // inside the bucket decides between a row and a drop, so it stays relative.
   if (tid < E && cap < 0) run[tid] += (int32_t)base + off[tid];
@@ -199,38 +169,19 @@ __global__ __launch_bounds__(kB) void place_kernel(
 
   // 3. Stable ranks inside the chunk, 1024 picks per batch.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-  for (int64_t base = p0; base < p1; base += kB) {
-    const int64_t p = base + tid;
+  for (int64_t base_p = p0; base_p < p1; base_p += kB) {
+    const int64_t p = base_p + tid;
     const int e = e_next;
     e_next = (p + kB < p1) ? idx[p + kB] : -1;  // prefetch the next batch
     const bool valid = (p < p1) && ((unsigned)e < (unsigned)E);
-    uint64_t peers = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const uint64_t bal = __ballot(valid && set);
-      peers &= set ? bal : ~bal;
-    }
-    const int rk = __popcll(peers & lanemask_lt());
-    const int nw = __popcll(peers);
-    const bool leader = valid && (rk == nw - 1);
-    if (leader) wcnt[wid][e] = nw;
-    __syncthreads();
+    const int rel = batch_rank(e, valid, nbits, wcnt, run);
     if (valid) {
-      int before = 0;
-      for (int q = 0; q < wid; ++q) before += wcnt[q][e];
-      const int rel = run[e] + before + rk;
       const int P = cap < 0 ? rel : (rel < cap ? off[e] + rel : -1);
       pos[p] = P;
       if (row_token && P >= 0 && (int64_t)P < rows) row_token[P] = (int32_t)(p / k);
     } else if (p < p1) {
       pos[p] = -1;
     }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&run[e], nw);
-      wcnt[wid][e] = 0;
-    }
-    __syncthreads();
   }
 }
 

@@ -1,0 +1,104 @@
+// index_tables.h -- block-level pieces of the placing kernel's index stage
+// (1024-thread blocks, E <= 1024, so thread j owns bucket j and expert j): the
+// bucket scan, the published tables, the stable in-batch rank.
+//
+// The send buffer holds one bucket per expert in (wave, rank, slot) order
+// (bucket_expert); the Alltoallv tables are the per-(wave, rank) sums and the
+// first rows of those buckets (irregular AllToAll page, Alltoallv counts and
+// displacements in rows).
+#pragma once
+
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kIndexWaves = kIndexBlock / kWave;
+constexpr int kIndexMaxE = 1024;
+
+// Exclusive scan of the bucket sizes in (wave, rank, slot) order: off[e] = first
+// row of expert e's bucket (relative); returns the total. Sizes are cnt[e], or
+// cap for every bucket when cap >= 0. Called by every thread of the block;
+// part holds kIndexWaves ints of LDS. Ends with a barrier.
+__device__ __forceinline__ int bucket_scan(const int32_t* cnt, int E, int R, int W, int cap,
+                                           int32_t* off, int32_t* part) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int L = E / R, LW = L / W;
+  const int cj = (tid < E) ? (cap >= 0 ? cap : cnt[bucket_expert(tid, R, L, LW)]) : 0;
+  int incl = cj;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) part[wid] = incl;
+  __syncthreads();
+  int excl = incl - cj, total = 0;
+#pragma unroll
+  for (int q = 0; q < kIndexWaves; ++q) {
+    excl += (q < wid) ? part[q] : 0;
+    total += part[q];
+  }
+  if (tid < E) off[bucket_expert(tid, R, L, LW)] = excl;
+  __syncthreads();
+  return total;
+}
+
+// Counts and offsets of one dispatch (rows from `base`): expert_counts (kept
+// rows: min(c, cap) with a capacity), expert_offsets, per-(wave, rank)
+// rank_counts / rank_offsets (whole buckets) and wave_offsets[W+1].
+__device__ __forceinline__ void publish_index(const int32_t* cnt, const int32_t* off, int total,
+                                              int E, int R, int W, int cap, int64_t base,
+                                              int32_t* ec, int32_t* eo, int32_t* rc, int32_t* ro,
+                                              int32_t* wo) {
+  const int tid = threadIdx.x;
+  const int L = E / R, LW = L / W;
+  if (tid < E) {
+    ec[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];
+    eo[tid] = (int32_t)(base + off[tid]);
+  }
+  for (int q = tid; q < W * R; q += kIndexBlock) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
+    int s = 0;
+    for (int j = q * LW; j < q * LW + LW; ++j) s += cap >= 0 ? cap : cnt[bucket_expert(j, R, L, LW)];
+    rc[q] = s;
+    ro[q] = (int32_t)(base + off[bucket_expert(q * LW, R, L, LW)]);
+  }
+  for (int w = tid; w <= W; w += kIndexBlock)
+    wo[w] = (int32_t)(base + ((w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total));
+}
+
+// Stable rank of this thread's pick (expert e, valid) among the block's picks
+// of e so far: run[e] (earlier batches) + picks of e in lower waves of this
+// batch + lower lanes of this wave (bit-sliced ballot match on the id,
+// popcount of the lower peers). Then run[] advances by the batch's counts.
+// wcnt must be zero for the experts used; it is left zero. Every thread of
+// the block calls it (three barriers).
+__device__ __forceinline__ int batch_rank(int e, bool valid, int nbits,
+                                          int32_t (*wcnt)[kIndexMaxE], int32_t* run) {
+  const int wid = threadIdx.x / kWave;
+  uint64_t peers = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t bal = __ballot(valid && set);
+    peers &= set ? bal : ~bal;
+  }
+  const int rk = __popcll(peers & lanemask_lt());
+  const int nw = __popcll(peers);
+  const bool leader = valid && (rk == nw - 1);
+  if (leader) wcnt[wid][e] = nw;
+  __syncthreads();
+  int rel = 0;
+  if (valid) {
+    int before = 0;
+    for (int q = 0; q < wid; ++q) before += wcnt[q][e];
+    rel = run[e] + before + rk;
+  }
+  __syncthreads();
+  if (leader) {
+    atomicAdd(&run[e], nw);
+    wcnt[wid][e] = 0;
+  }
+  __syncthreads();
+  return rel;
+}
+
+}  // namespace moe
