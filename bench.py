@@ -89,6 +89,9 @@ def parse_args():
                          "two streams vs one; T(W) and the fitted wave model")
     ap.add_argument("--vsrc", action="store_true",
                     help="the expert-parallel exchange of R virtual source ranks on one device")
+    ap.add_argument("--direct", action="store_true",
+                    help="with --vsrc: the exchange straight into the grouped layout (one copy "
+                         "each way) instead of all-to-all + regroup")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="capacity-factor dispatch (buckets of ceil(k*f*T/E) rows, overflow "
                          "dropped, zero padding) instead of count-sized buckets")
@@ -440,7 +443,7 @@ def main() -> int:
              [("route", "route_kernel")]),
             (L.moe_vsrc_dispatch, (
                 shp, P(x), P(topk_idx), P(vb["send_buf"]), P(vb["src_counts"]),
-                P(vb["send_counts"]), P(vb["send_offsets"]), P(vb["recv_counts"]),
+                P(vb["src_offsets"]), P(vb["send_counts"]), P(vb["send_offsets"]), P(vb["recv_counts"]),
                 P(vb["recv_offsets"]), P(vb["expert_counts"]), P(vb["expert_offsets"]),
                 P(vb["pos"]), *vws, stream),
              [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(sources)"),
@@ -462,6 +465,19 @@ def main() -> int:
             (L.moe_stats, (P(vb["expert_counts"]), E, R, P(stats_raw), stream),
              [("stats", "stats_kernel")]),
         ]
+        if args.direct:  # one copy each way: send <-> grouped
+            dr_tabs = (P(vb["src_counts"]), P(vb["src_offsets"]), P(vb["expert_offsets"]))
+            calls[2:7] = [
+                (L.moe_vsrc_exchange_direct, (shp, 0, P(vb["send_buf"]), P(vb["grouped"]),
+                                              *dr_tabs, *vws, stream),
+                 [("dispatch_index", "regroup_plan_kernel"),
+                  ("exchange", "segcopy_kernel<direct>")]),
+                calls[4],  # the experts on the grouped rows
+                (L.moe_vsrc_exchange_direct, (shp, 1, P(veo), P(vback_send), *dr_tabs, *vws,
+                                              stream),
+                 [("dispatch_index", "regroup_plan_kernel"),
+                  ("exchange", "segcopy_kernel<direct>")]),
+            ]
     STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
     kernel_of = {st: "+".join(dict.fromkeys(kn for c in calls for g, kn in c[2] if g == st))
                  for st in STAGES_RUN}
@@ -646,7 +662,8 @@ def main() -> int:
 
     dc_keys = ("dispatch_index", "dispatch_copy", "combine")
     if args.vsrc:
-        dc_keys = ("dispatch_index", "dispatch_copy", "exchange", "regroup", "combine")
+        dc_keys = tuple(n for n in ("dispatch_index", "dispatch_copy", "exchange", "regroup",
+                                    "combine") if n in stage_ms)
     dc_ms = sum(stage_ms[n] for n in dc_keys)
     dc_bytes = sum(nbytes[n] for n in dc_keys)
     result = {
@@ -694,8 +711,11 @@ def main() -> int:
         result["config"].update(capacity_factor=args.capacity_factor, capacity=cap,
                                 kept_picks=kept, dropped_picks=T * k - kept)
     if args.vsrc:
-        result["config"]["step"] = ("route+vsrc_dispatch(count,place,plan,copy)+exchange"
-                                    "+regroup+expert+ungroup+exchange back+combine+stats")
+        result["config"]["step"] = (
+            "route+vsrc_dispatch(count,place,plan,copy)+"
+            + ("direct exchange+expert+direct exchange back" if args.direct else
+               "exchange+regroup+expert+ungroup+exchange back")
+            + "+combine+stats")
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}

@@ -69,8 +69,10 @@ SIGNATURES = {
     "moe_swiglu_waves": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           ctypes.c_size_t, _vp, _vp], ctypes.c_int),
     "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
-    "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_vsrc_exchange_direct": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                                 ctypes.c_int),
     "moe_vsrc_exchange": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_vsrc_regroup": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                          ctypes.c_int),
@@ -308,6 +310,7 @@ def alloc_vsrc(shape: Shape, device) -> dict:
     return dict(
         send_buf=_empty((rows, H), shape.dtype, device), recv_buf=_empty((rows, H), shape.dtype, device),
         grouped=_empty((rows, H), shape.dtype, device), src_counts=_empty((R, E), i32, device),
+        src_offsets=_empty((R, E), i32, device),
         send_counts=_empty((R, W, R), i32, device), send_offsets=_empty((R, W, R), i32, device),
         recv_counts=_empty((R, W, R), i32, device), recv_offsets=_empty((R, W, R), i32, device),
         expert_counts=_empty((E,), i32, device), expert_offsets=_empty((E,), i32, device),
@@ -321,7 +324,7 @@ def vsrc_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, shape: Shape, out: di
     sh = shape.c()
     _check(lib().moe_vsrc_dispatch(
         ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]), _ptr(out["src_counts"]),
-        _ptr(out["send_counts"]), _ptr(out["send_offsets"]), _ptr(out["recv_counts"]),
+        _ptr(out["src_offsets"]), _ptr(out["send_counts"]), _ptr(out["send_offsets"]), _ptr(out["recv_counts"]),
         _ptr(out["recv_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
         _ptr(out["pos"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
         "moe_vsrc_dispatch")
@@ -336,6 +339,18 @@ def vsrc_exchange(src: torch.Tensor, dst: torch.Tensor, shape: Shape, out: dict,
     _check(lib().moe_vsrc_exchange(
         ctypes.byref(sh), direction, _ptr(src), _ptr(dst), _ptr(out["send_offsets"]),
         _ptr(out["recv_counts"]), _ptr(out["recv_offsets"]), _stream()), "moe_vsrc_exchange")
+    return dst
+
+
+def vsrc_exchange_direct(src: torch.Tensor, dst: torch.Tensor, shape: Shape, out: dict,
+                         direction: int = 0) -> torch.Tensor:
+    """The exchange straight into the grouped layout: send -> grouped
+    (direction 0) or grouped -> send (1), one copy."""
+    sh = shape.c()
+    _check(lib().moe_vsrc_exchange_direct(
+        ctypes.byref(sh), direction, _ptr(src), _ptr(dst), _ptr(out["src_counts"]),
+        _ptr(out["src_offsets"]), _ptr(out["expert_offsets"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream()), "moe_vsrc_exchange_direct")
     return dst
 
 

@@ -81,14 +81,14 @@ int check_vsrc_shape(const moe_shape* sh) {
   return MOE_OK;
 }
 
-// Per-source hist rows, per-source expert offsets and wave offsets (dispatch),
-// or the 3 * E * R segment table (regroup).
+// Per-source hist rows and wave offsets (dispatch), or the 3 * E * R segment
+// table (regroup, direct exchange).
 size_t vsrc_workspace_bytes(const moe_shape* sh) {
   int64_t chunk;
   int spc;
   moe::source_chunks(int64_t(sh->T / sh->R) * sh->k, sh->E, chunk, spc);
   const int64_t R = sh->R, E = sh->E;
-  const int64_t disp = (R * spc * E + R * E + R * (sh->W + 1)) * 4;
+  const int64_t disp = (R * spc * E + R * (sh->W + 1)) * 4;
   const int64_t regroup = 3 * E * R * 4;
   const int64_t bytes = disp > regroup ? disp : regroup;
   return size_t((bytes + 255) / 256 * 256);
@@ -441,17 +441,18 @@ size_t moe_vsrc_workspace_bytes(const moe_shape* shape) {
 }
 
 int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
-                      void* send_buf, int32_t* src_counts, int32_t* send_counts,
+                      void* send_buf, int32_t* src_counts, int32_t* src_offsets,
+                      int32_t* send_counts,
                       int32_t* send_offsets, int32_t* recv_counts, int32_t* recv_offsets,
                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
                       void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
   int st = check_vsrc_shape(shape);
   if (st != MOE_OK) return st;
-  if (!src_counts || !send_counts || !send_offsets || !recv_counts || !recv_offsets ||
-      !expert_counts || !expert_offsets || !workspace)
+  if (!src_counts || !src_offsets || !send_counts || !send_offsets || !recv_counts ||
+      !recv_offsets || !expert_counts || !expert_offsets || !workspace)
     return MOE_ERR_ARG;
   if (shape->T > 0 && (!topk_idx || !pos)) return MOE_ERR_ARG;
-  const void* p4[] = {topk_idx, src_counts, send_counts, send_offsets, recv_counts,
+  const void* p4[] = {topk_idx, src_counts, src_offsets, send_counts, send_offsets, recv_counts,
                       recv_offsets, expert_counts, expert_offsets, pos, workspace};
   for (const void* p : p4)
     if (!aligned(p, 4)) return MOE_ERR_ALIGN;
@@ -464,8 +465,7 @@ int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk
   int spc;
   moe::source_chunks(src_picks, E, chunk, spc);
   int32_t* hist = static_cast<int32_t*>(workspace);
-  int32_t* src_offsets = hist + int64_t(R) * spc * E;
-  int32_t* wave_offsets = src_offsets + int64_t(R) * E;
+  int32_t* wave_offsets = hist + int64_t(R) * spc * E;
   hipStream_t s = as_stream(stream);
   st = status_of(moe::launch_count_sources(topk_idx, R, src_picks, E, hist, s));
   if (st != MOE_OK) return st;
@@ -495,6 +495,26 @@ int moe_vsrc_exchange(const moe_shape* shape, int32_t direction, const void* in,
   return status_of(moe::launch_vsrc_exchange(in, out, row_bytes, int64_t(shape->T) * shape->k,
                                              shape->R, shape->W, send_offsets, recv_counts,
                                              recv_offsets, direction == 1, as_stream(stream)));
+}
+
+int moe_vsrc_exchange_direct(const moe_shape* shape, int32_t direction, const void* in,
+                             void* out, const int32_t* src_counts, const int32_t* src_offsets,
+                             const int32_t* expert_offsets, void* workspace,
+                             size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_vsrc_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_vsrc_move(shape, direction, in, out);
+  if (st != MOE_OK) return st;
+  if (!src_counts || !src_offsets || !expert_offsets || !workspace) return MOE_ERR_ARG;
+  if (!aligned(src_counts, 4) || !aligned(src_offsets, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(workspace, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_given < vsrc_workspace_bytes(shape)) return MOE_ERR_WORKSPACE;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_vsrc_direct(
+      in, out, row_bytes, int64_t(shape->T) * shape->k, shape->E, shape->R, shape->W, src_counts,
+      src_offsets, expert_offsets, static_cast<int32_t*>(workspace), direction == 1,
+      as_stream(stream)));
 }
 
 int moe_vsrc_regroup(const moe_shape* shape, int32_t direction, const void* in, void* out,

@@ -133,14 +133,15 @@ __global__ __launch_bounds__(kPlanBlock) void vsrc_plan_kernel(
 }
 
 // Segment t = e*R + s, one thread each: its first grouped row (the expert's
-// offset plus the counts of the earlier sources for that expert) and its
-// first recv row (the source's message of that destination and wave plus the
-// counts of the wave's earlier slots).
+// offset plus the counts of the earlier sources for that expert) and the first
+// row of the other side: in recv, the source's message of that destination and
+// wave plus the counts of the wave's earlier slots; or, for the direct
+// exchange (src_offsets non-null), the source's own bucket of expert e in send.
 __global__ __launch_bounds__(256) void regroup_plan_kernel(
     int R, int W, int E, const int32_t* __restrict__ src_counts,
-    const int32_t* __restrict__ recv_offsets, const int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ grp_start, int32_t* __restrict__ seg_count,
-    int32_t* __restrict__ recv_sub) {
+    const int32_t* __restrict__ recv_offsets, const int32_t* __restrict__ src_offsets,
+    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ grp_start,
+    int32_t* __restrict__ seg_count, int32_t* __restrict__ other) {
   const int L = E / R, LW = L / W;
   const int64_t nseg = (int64_t)E * R;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -149,9 +150,13 @@ __global__ __launch_bounds__(256) void regroup_plan_kernel(
     const int d = e / L, j = e % L, w = j / LW;
     grp_start[t] = (int32_t)(expert_offsets[e] + sum_strided(src_counts + e, s, E));
     seg_count[t] = src_counts[(int64_t)s * E + e];
-    const int32_t* row = src_counts + (int64_t)s * E + (int64_t)d * L;
-    recv_sub[t] = (int32_t)(recv_offsets[((int64_t)d * W + w) * R + s] +
-                            sum_strided(row + w * LW, j - w * LW, 1));
+    if (src_offsets != nullptr) {
+      other[t] = src_offsets[(int64_t)s * E + e];
+    } else {
+      const int32_t* row = src_counts + (int64_t)s * E + (int64_t)d * L;
+      other[t] = (int32_t)(recv_offsets[((int64_t)d * W + w) * R + s] +
+                           sum_strided(row + w * LW, j - w * LW, 1));
+    }
   }
 }
 
@@ -321,22 +326,39 @@ hipError_t launch_vsrc_exchange(const void* in, void* out, int64_t row_bytes, in
                        row_bytes, rows, rows, back, s);
 }
 
+// Grouped layout against recv (regroup) or against send (direct exchange).
+static hipError_t grouped_copy(const void* in, void* out, int64_t row_bytes, int64_t rows, int E, int R,
+                        int W, const int32_t* src_counts, const int32_t* recv_offsets,
+                        const int32_t* src_offsets, const int32_t* expert_offsets,
+                        int32_t* tables, bool back, hipStream_t s) {
+  const int64_t nseg = (int64_t)E * R;
+  int32_t* grp_start = tables;
+  int32_t* seg_count = tables + nseg;
+  int32_t* other = tables + 2 * nseg;
+  const int64_t want = (nseg + 255) / 256;
+  const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
+  hipError_t e = launch(regroup_plan_kernel, dim3(grid), dim3(256), 0, s, R, W, E, src_counts,
+                        recv_offsets, src_offsets, expert_offsets, grp_start, seg_count, other);
+  if (e != hipSuccess) return e;
+  // key side: grouped
+  return segcopy<false>(in, out, grp_start, seg_count, other, (int)nseg, R, W, row_bytes, rows,
+                        rows, back, s);
+}
+
 hipError_t launch_vsrc_regroup(const void* in, void* out, int64_t row_bytes, int64_t rows, int E,
                                int R, int W, const int32_t* src_counts,
                                const int32_t* recv_offsets, const int32_t* expert_offsets,
                                int32_t* tables, bool back, hipStream_t s) {
-  const int64_t nseg = (int64_t)E * R;
-  int32_t* grp_start = tables;
-  int32_t* seg_count = tables + nseg;
-  int32_t* recv_sub = tables + 2 * nseg;
-  const int64_t want = (nseg + 255) / 256;
-  const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
-  hipError_t e = launch(regroup_plan_kernel, dim3(grid), dim3(256), 0, s, R, W, E, src_counts,
-                        recv_offsets, expert_offsets, grp_start, seg_count, recv_sub);
-  if (e != hipSuccess) return e;
-  // key side: grouped; other side: recv
-  return segcopy<false>(in, out, grp_start, seg_count, recv_sub, (int)nseg, R, W, row_bytes, rows,
-                        rows, back, s);
+  return grouped_copy(in, out, row_bytes, rows, E, R, W, src_counts, recv_offsets, nullptr,
+                      expert_offsets, tables, back, s);
+}
+
+hipError_t launch_vsrc_direct(const void* in, void* out, int64_t row_bytes, int64_t rows, int E,
+                              int R, int W, const int32_t* src_counts, const int32_t* src_offsets,
+                              const int32_t* expert_offsets, int32_t* tables, bool back,
+                              hipStream_t s) {
+  return grouped_copy(in, out, row_bytes, rows, E, R, W, src_counts, nullptr, src_offsets,
+                      expert_offsets, tables, back, s);
 }
 
 }  // namespace moe

@@ -144,6 +144,12 @@ hipError_t launch_vsrc_plan(int R, int W, int E, const int32_t* src_counts,
 hipError_t launch_vsrc_exchange(const void* in, void* out, int64_t row_bytes, int64_t rows, int R,
                                 int W, const int32_t* send_offsets, const int32_t* recv_counts,
                                 const int32_t* recv_offsets, bool back, hipStream_t s);
+// Direct exchange send -> grouped (back: grouped -> send): each (expert,
+// source) segment straight from the source's bucket; tables as the regroup.
+hipError_t launch_vsrc_direct(const void* in, void* out, int64_t row_bytes, int64_t rows, int E,
+                              int R, int W, const int32_t* src_counts, const int32_t* src_offsets,
+                              const int32_t* expert_offsets, int32_t* tables, bool back,
+                              hipStream_t s);
 // Receive-side regroup recv -> grouped (back: grouped -> recv); tables holds
 // 3 * E * R int32.
 hipError_t launch_vsrc_regroup(const void* in, void* out, int64_t row_bytes, int64_t rows, int E,

@@ -347,6 +347,7 @@ size_t moe_vsrc_workspace_bytes(const moe_shape* shape);
  * of each shard, then the receive side's tables).
  * x [T][H] in; topk_idx [T][k] in; send_buf [T*k][H] out.
  * src_counts   [R][E] out: picks of expert e among source s's tokens.
+ * src_offsets  [R][E] out: first send row of source s's bucket of expert e.
  * send_counts  [R][W][R] out: rows source s sends in wave w to destination d.
  * send_offsets [R][W][R] out: first send row of that message.
  * recv_counts  [R][W][R] out: rows destination d receives in wave w from
@@ -360,7 +361,8 @@ size_t moe_vsrc_workspace_bytes(const moe_shape* shape);
  * Errors: MOE_ERR_ARG (T % R != 0, shape outside the limits, null pointers),
  *         MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
-                      void* send_buf, int32_t* src_counts, int32_t* send_counts,
+                      void* send_buf, int32_t* src_counts, int32_t* src_offsets,
+                      int32_t* send_counts,
                       int32_t* send_offsets, int32_t* recv_counts, int32_t* recv_offsets,
                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
                       void* workspace, size_t workspace_bytes, moe_stream_t stream);
@@ -375,6 +377,20 @@ int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk
 int moe_vsrc_exchange(const moe_shape* shape, int32_t direction, const void* in, void* out,
                       const int32_t* send_offsets, const int32_t* recv_counts,
                       const int32_t* recv_offsets, moe_stream_t stream);
+
+/* The exchange written straight into the receivers' grouped layout, one pass:
+ * every (expert, source) segment goes from source s's bucket of expert e in the
+ * send layout to its rows in the grouped layout (what one-sided stores into
+ * peer receive buffers do, with the counts exchanged first), i.e.
+ * moe_vsrc_exchange followed by moe_vsrc_regroup in one copy. direction 0:
+ * in = send layout, out = grouped layout; direction 1: in = grouped layout,
+ * out = send layout. src_counts, src_offsets, expert_offsets as written by
+ * moe_vsrc_dispatch. Two launches (segment table into the workspace, then the
+ * copy). Errors: as moe_vsrc_regroup. */
+int moe_vsrc_exchange_direct(const moe_shape* shape, int32_t direction, const void* in,
+                             void* out, const int32_t* src_counts, const int32_t* src_offsets,
+                             const int32_t* expert_offsets, void* workspace,
+                             size_t workspace_bytes, moe_stream_t stream);
 
 /* Receive-side regroup of every destination from its (wave, source) messages
  * into (local expert, source) order. direction 0: in = recv layout, out =

@@ -361,6 +361,7 @@ def vsrc_exchange(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, R: int,
                the one-rank dispatch layout of its own tokens (buckets in (wave,
                destination, slot) order, token order inside a bucket);
     src_counts [R][E]: picks of expert e made by source s's tokens;
+    src_offsets [R][E]: first send row of source s's bucket of expert e;
     send_counts / send_offsets [R][W][R] (source, wave, destination): the
                Alltoallv send side;
     recv_counts / recv_offsets [R][W][R] (destination, wave, source): the receive
@@ -381,6 +382,7 @@ def vsrc_exchange(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, R: int,
     send = np.zeros((rows, H), x.dtype)
     pos = np.full((T, k), -1, np.int32)
     src_counts = np.zeros((R, E), np.int32)
+    src_offsets = np.zeros((R, E), np.int64)
     send_counts = np.zeros((R, W, R), np.int64)
     send_offsets = np.zeros((R, W, R), np.int64)
     for s in range(R):
@@ -388,6 +390,7 @@ def vsrc_exchange(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, R: int,
         d_s = dispatch(x[sl], idx[sl], E, R, W)
         base = s * Ts * k
         src_counts[s] = d_s["expert_counts"]
+        src_offsets[s] = d_s["expert_offsets"] + base
         send[base:base + d_s["nrows"]] = d_s["send_buf"]
         pos[sl] = np.where(d_s["pos"] >= 0, d_s["pos"] + base, -1)
         send_counts[s] = d_s["rank_counts"].reshape(W, R)
@@ -444,7 +447,8 @@ def vsrc_exchange(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, R: int,
                 back_send[a:a + c] = back_recv[b:b + c]
     y = combine_f32fma(back_send, np.asarray(w, np.float32), pos, T)
     i32 = lambda a: np.asarray(a, np.int32)
-    return dict(send=send, pos=pos, src_counts=src_counts, send_counts=i32(send_counts),
+    return dict(send=send, pos=pos, src_counts=src_counts, src_offsets=i32(src_offsets),
+                send_counts=i32(send_counts),
                 send_offsets=i32(send_offsets), recv_counts=i32(recv_counts),
                 recv_offsets=i32(recv_offsets), recv=recv, expert_counts=i32(expert_counts),
                 expert_offsets=i32(expert_offsets), grp_start=i32(grp_start),

@@ -198,7 +198,7 @@ def test_vsrc_validation_and_workspace():
     ws = L.moe_vsrc_workspace_bytes(ctypes.byref(sh))
     # per-source histogram rows + per-source offsets, or the 3*E*R segment table
     assert ws >= 3 * 8 * 4 * 4 and ws % 256 == 0
-    tabs = [FAKE] * 8  # src_counts .. pos
+    tabs = [FAKE] * 9  # src_counts .. pos
     x, idx, send = FAKE, FAKE, FAKE
     uneven = _shape(T=66, E=8, k=2, R=4)
     assert L.moe_vsrc_workspace_bytes(ctypes.byref(_shape(E=0))) == 0
@@ -206,7 +206,7 @@ def test_vsrc_validation_and_workspace():
                                None) == ARG
     assert L.moe_vsrc_dispatch(ctypes.byref(sh), x, idx, send, *tabs, FAKE, ws - 1,
                                None) == WORKSPACE
-    assert L.moe_vsrc_dispatch(ctypes.byref(sh), x, idx, send, *tabs[:7], None, FAKE, ws,
+    assert L.moe_vsrc_dispatch(ctypes.byref(sh), x, idx, send, *tabs[:8], None, FAKE, ws,
                                None) == ARG
     assert L.moe_vsrc_dispatch(ctypes.byref(sh), ctypes.c_void_p((1 << 20) + 4), idx, send, *tabs,
                                FAKE, ws, None) == ALIGN
@@ -221,6 +221,13 @@ def test_vsrc_validation_and_workspace():
                                None) == ARG
     assert L.moe_vsrc_regroup(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1,
                               None) == WORKSPACE
+    for d in (-1, 2):
+        assert L.moe_vsrc_exchange_direct(ctypes.byref(sh), d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          ws, None) == ARG
+    assert L.moe_vsrc_exchange_direct(ctypes.byref(sh), 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws,
+                                      None) == ARG
+    assert L.moe_vsrc_exchange_direct(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      ws - 1, None) == WORKSPACE
     # the largest configuration's tables fit comfortably
     big = _shape(T=16384, H=7168, E=256, k=8, R=32, W=8)
     assert 3 * 256 * 32 * 4 <= L.moe_vsrc_workspace_bytes(ctypes.byref(big)) < 1 << 20

@@ -21,8 +21,8 @@ from test_gpu_parity import DEV, PARITY, assert_combine_tol, dev, host, shape_of
 
 pytestmark = pytest.mark.gpu
 
-TABLES = ("src_counts", "send_counts", "send_offsets", "recv_counts", "recv_offsets",
-          "expert_counts", "expert_offsets", "pos")
+TABLES = ("src_counts", "src_offsets", "send_counts", "send_offsets", "recv_counts",
+          "recv_offsets", "expert_counts", "expert_offsets", "pos")
 
 CASES = {
     **{n: PARITY[n] for n in ("tiny", "zipf", "dirichlet_waves_T512", "decode_hot")},
@@ -186,4 +186,33 @@ def test_vsrc_edge_shapes(name):
     np.testing.assert_array_equal(host(out["recv_buf"])[:n], ref["recv"][:n])
     np.testing.assert_array_equal(host(out["grouped"])[:n], ref["grouped"][:n])
     np.testing.assert_array_equal(host(back_recv)[:n], ref["back_recv"][:n])
+    np.testing.assert_array_equal(host(y), ref["y"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "zipf", "dirichlet_waves_T512", "decode_hot",
+                                  "tiny_R2_W2", "zipf_R4_W2", "zipf_T12000_R4"])
+def test_vsrc_direct_exchange(name):
+    """The one-pass exchange into the grouped layout gives the oracle's grouped
+    rows (what exchange + regroup give), and back the oracle's returned rows."""
+    wl = CASES[name]
+    print(f"[vsrc direct] {name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W}",
+          flush=True)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    ref = oracle.vsrc_exchange(x, idx, w, wl.E, wl.R, wl.W)
+    shape = shape_of(wl)
+    out = moe.alloc_vsrc(shape, DEV)
+    moe.vsrc_dispatch(dev(x), dev(idx), shape, out)
+    moe.vsrc_exchange_direct(out["send_buf"], out["grouped"], shape, out, 0)
+    eo = moe.expert_scale_rows(out["grouped"], out["expert_offsets"], out["expert_counts"],
+                               shape_of(wl.with_(W=1)))
+    back = torch.zeros_like(out["send_buf"])
+    moe.vsrc_exchange_direct(eo, back, shape, out, 1)
+    y = moe.combine_rows(back, dev(w.astype(np.float32)), out["pos"], shape)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out["src_offsets"]), ref["src_offsets"])
+    n = int(ref["expert_counts"].sum())
+    np.testing.assert_array_equal(host(out["grouped"])[:n], ref["grouped"][:n])
+    used = ref["pos"][ref["pos"] >= 0]
+    np.testing.assert_array_equal(host(back)[used], ref["back_send"][used])
     np.testing.assert_array_equal(host(y), ref["y"])

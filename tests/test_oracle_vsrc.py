@@ -29,6 +29,7 @@ def test_golden_hand_worked(W):
     eq(v["src_counts"], np.array(g["src_counts"], np.int32))
     eq(v["expert_counts"], np.array(g["expert_counts"], np.int32))
     eq(v["expert_offsets"], np.array(g["expert_offsets"], np.int32))
+    eq(v["src_offsets"], np.array(g[p + "src_offsets"], np.int32))
     eq(v["send_counts"].reshape(R, -1), np.array(g[p + "send_counts"], np.int32))
     eq(v["send_offsets"].reshape(R, -1), np.array(g[p + "send_offsets"], np.int32))
     eq(v["recv_counts"].reshape(R, -1), np.array(g[p + "recv_counts"], np.int32))
@@ -51,15 +52,19 @@ def _brute(idx, E, R, W):
         return (e % L) * W // L
 
     send, pos = [], {}
+    src_offsets = np.zeros((R, E), np.int64)
+    bucket_key = lambda e: (wave(e), e // L, e % L)  # noqa: E731
     for s in range(R):
         mine = sorted((p for p in picks if p[0] // Ts == s),
-                      key=lambda p: (wave(p[2]), p[2] // L, p[2] % L, p[0]))
+                      key=lambda p: (*bucket_key(p[2]), p[0]))
         for j, p in enumerate(mine):
             pos[(p[0], p[1])] = s * Ts * k + j
+        for e in range(E):  # rows of the source's buckets that come before e's
+            src_offsets[s, e] = s * Ts * k + sum(bucket_key(p[2]) < bucket_key(e) for p in mine)
         send += mine
     recv = sorted(picks, key=lambda p: (p[2] // L, wave(p[2]), p[0] // Ts, p[2] % L, p[0]))
     grouped = sorted(picks, key=lambda p: (p[2], p[0]))
-    return send, pos, recv, grouped
+    return send, pos, recv, grouped, src_offsets
 
 
 CASES = [(0, 24, 8, 2, 4, 1), (1, 30, 12, 3, 3, 2), (2, 32, 16, 4, 2, 4), (3, 18, 6, 6, 6, 1),
@@ -76,7 +81,8 @@ def test_against_sort_brute_force(seed, T, E, k, R, W):
     x = (np.arange(T, dtype=np.float32)[:, None] * 16 + np.arange(4, dtype=np.float32))
     w = g.random((T, k))
     v = oracle.vsrc_exchange(x, idx, w, E, R, W)
-    send, pos, recv, grouped = _brute(idx, E, R, W)
+    send, pos, recv, grouped, src_offsets = _brute(idx, E, R, W)
+    np.testing.assert_array_equal(v["src_offsets"], src_offsets)
     n = len(send)
     Ts = T // R
     # source shards keep their own row ranges; unused rows (invalid picks) are zero
