@@ -30,6 +30,8 @@
 // dealt to the 8 XCDs round-robin; each XCD takes one contiguous share of the
 // m-major tile order, so it reads its rows once and the weights of the experts
 // they belong to through its L2.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -45,16 +47,23 @@ constexpr int kGroupM = 1;  // m-tiles per rasterisation patch (2, 4, 8 measured
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
-// K step: 64 bf16 = 128 bytes of every tile row, eight 16-byte chunks.
-constexpr int kBK = 64;
+// XOR key of tile row r for a K step of BK bf16 (BK/8 16-byte chunks a row).
+// The 64 four-byte banks span 256 bytes; a fragment read (ds_read_b128)
+// services 16 lanes = 16 consecutive rows at one chunk index at once.
+//   BK = 64: 128-byte rows, two rows per bank sweep; the key (r >> 1) & 7
+//            gives the 8 row pairs distinct chunk slots.
+//   BK = 32: 64-byte rows, four rows per bank sweep; the key (r >> 2) & 3
+//            gives the 4 row quads distinct chunk slots.
+// Either way the 16 lanes hit 64 distinct banks.
+template <int BK>
+__device__ __forceinline__ int swz_key(int r) {
+  if constexpr (BK == 64) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
 
-// Element offset of 16-byte chunk c of tile row r in an LDS tile (XOR swizzle,
-// no padding). The 64 four-byte banks span 256 bytes = two tile rows; a
-// fragment read (ds_read_b128) services 16 lanes = 16 consecutive rows at
-// once. Rows r and r + 1 fall in opposite bank halves, and the key
-// (r >> 1) & 7 gives the 8 row pairs distinct chunk slots, so the 16 lanes hit
-// 64 distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
+// Element offset of 16-byte chunk c of tile row r in an LDS tile (no padding).
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ swz_key<BK>(r)) << 3); }
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -62,9 +71,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // no swizzle, no index stride).
 constexpr int kRsrcWord3 = 0x00020000;
 
-// s_waitcnt with vmcnt = 0 and the other counters left free (gfx9 encoding:
-// vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for vmcnt <= n with the other counters left free (gfx9
+// encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitVmcnt0 = wait_vmcnt(0);
 
 // Buffer-instruction helpers (plain device functions, so that the kernel's
 // lambdas stay valid in the host compilation pass).
@@ -78,21 +88,35 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* l
 }
 
 // BM x BN block tile; each of the 2 x 2 waves computes (BM/2) x (BN/2) as
-// MI x NI tiles of 32 x 32.
-template <bool kGateUp, int BM, int BN, int OCC>
+// MI x NI tiles of 32 x 32. K steps of BK, NS LDS stages.
+template <bool kGateUp, int BM, int BN, int OCC, int BK, int NS>
 __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, int sg, int sstride, int sbase,
     const uint16_t* __restrict__ Bw, int64_t bstride,
     int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int gm) {
   constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
-  constexpr int AI = BM / 32, BI = BN / 32;  // 8-row load instructions per wave per K step
-  constexpr int kStage = (BM + BN) * kBK;    // elements of one A + B stage
-  // Two stages as two arrays, so the compiler can tell the loads into one stage
-  // from the fragment reads of the other and need not wait for them.
+  constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
+  constexpr int RPI = kWave / CPR;           // tile rows per load instruction (1 KiB)
+  constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // load instructions per wave per K step
+  constexpr int kStage = (BM + BN) * BK;     // elements of one A + B stage
+  static_assert(NS >= 2 && NS <= 5, "LDS stages");
+  // The stages as separate arrays, so the compiler can tell the loads into one
+  // stage from the fragment reads of another and need not wait for them.
   __shared__ __attribute__((aligned(1024))) uint16_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) uint16_t lds1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds2[NS > 2 ? kStage : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds3[NS > 3 ? kStage : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds4[NS > 4 ? kStage : 1];
   __shared__ int info[4];  // expert, first row, rows in tile, n-tile
+  const auto stage = [&](auto S) -> uint16_t* {
+    constexpr int st = decltype(S)::value % NS;
+    if constexpr (st == 0) return lds0;
+    else if constexpr (st == 1) return lds1;
+    else if constexpr (st == 2) return lds2;
+    else if constexpr (st == 3) return lds3;
+    else return lds4;
+  };
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int wm = wid >> 1, wn = wid & 1;
@@ -161,8 +185,8 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
 
   // ---- global -> LDS without registers (global_load_lds_dwordx4): one wave
   // instruction fills 64 consecutive 16-byte LDS slots, lane l slot l, i.e.
-  // 8 tile rows. Lane l therefore fetches the global chunk that the swizzle
-  // puts in slot l & 7 of row (l >> 3). Wave w fills A rows [w*BM/4, (w+1)*BM/4)
+  // RPI tile rows. Lane l therefore fetches the global chunk that the swizzle
+  // puts in slot l % CPR of row l / CPR. Wave w fills A rows [w*BM/4, (w+1)*BM/4)
   // and B rows [w*BN/4, (w+1)*BN/4). A rows past the tile's last row re-read
   // that row: MFMA output rows depend on their own A row only, and those rows
   // are never stored.
@@ -173,7 +197,7 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
     else
       return ntile * BN + r;
   };
-  const int lr = lane >> 3, ls = lane & 7;
+  const int lr = lane / CPR, ls = lane % CPR;
   // Buffer descriptors over this tile's A rows and this expert's weights. The
   // descriptor's range check returns zeros for A rows past the tile's last row
   // (those MFMA output rows are never stored), so no clamping is needed.
@@ -184,22 +208,22 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   uint32_t aoff[AI], boff[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int r = wid * (BM / 4) + 8 * i + lr;
-    aoff[i] = (uint32_t)(((int64_t)r * lda + ((ls ^ ((r >> 1) & 7)) << 3)) * 2);
+    const int r = wid * (BM / 4) + RPI * i + lr;
+    aoff[i] = (uint32_t)(((int64_t)r * lda + ((ls ^ swz_key<BK>(r)) << 3)) * 2);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int r = wid * (BN / 4) + 8 * i + lr;
-    boff[i] = (uint32_t)(((int64_t)brow(r) * K + ((ls ^ ((r >> 1) & 7)) << 3)) * 2);
+    const int r = wid * (BN / 4) + RPI * i + lr;
+    boff[i] = (uint32_t)(((int64_t)brow(r) * K + ((ls ^ swz_key<BK>(r)) << 3)) * 2);
   }
   auto issue = [&](uint16_t* As, int k0) __attribute__((always_inline)) {
-    uint16_t* Bs = As + BM * kBK;
+    uint16_t* Bs = As + BM * BK;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
-      load_lds16(arsrc, As + (wid * (BM / 4) + 8 * i) * kBK, aoff[i], 2 * k0);
+      load_lds16(arsrc, As + (wid * (BM / 4) + RPI * i) * BK, aoff[i], 2 * k0);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      load_lds16(brsrc, Bs + (wid * (BN / 4) + 8 * i) * kBK, boff[i], 2 * k0);
+      load_lds16(brsrc, Bs + (wid * (BN / 4) + RPI * i) * BK, boff[i], 2 * k0);
   };
 
   // B tile row of fragment ni for this wave: gate/up tiles put the wave's gate
@@ -222,15 +246,16 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   // are in flight during the MFMAs of kk.
   bf16x8 fa[2][MI], fb[2][NI];
   auto fload = [&](int f, const uint16_t* As, int kk) __attribute__((always_inline)) {
-    const uint16_t* Bs = As + BM * kBK;
+    const uint16_t* Bs = As + BM * BK;
     const int kc = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
       fa[f][mi] = *reinterpret_cast<const bf16x8*>(
-          &As[swz(wm * (BM / 2) + mi * 32 + (lane & 31), kc)]);
+          &As[swz<BK>(wm * (BM / 2) + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
-      fb[f][ni] = *reinterpret_cast<const bf16x8*>(&Bs[swz(bfrag_row(ni) + (lane & 31), kc)]);
+      fb[f][ni] =
+          *reinterpret_cast<const bf16x8*>(&Bs[swz<BK>(bfrag_row(ni) + (lane & 31), kc)]);
   };
   auto mfmas = [&](int f) __attribute__((always_inline)) {
 #pragma unroll
@@ -242,17 +267,23 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   };
   constexpr int kMF = MI * NI, kFR = MI + NI;  // MFMAs and fragment reads per sub-step
 
-  // Software pipeline over K steps, two LDS stages. In step kt (stage s = kt&1):
-  // sub-steps 0..2 run their MFMAs while reading the next sub-step's fragments;
-  // then, once this wave's stage-s reads and its loads of step kt+1 are done,
-  // one barrier, after which the loads of step kt+2 refill stage s while
-  // sub-step 3's MFMAs run alongside the first fragment reads of step kt+1.
-  // Past the last step the loads repeat step nk-1 into a stage nobody reads
-  // again, which keeps the loop free of branches around them.
-  const int nk = K / kBK;
-  auto step = [&](const uint16_t* cur, const uint16_t* nxt, int kt) __attribute__((always_inline)) {
+  // Software pipeline over K steps, NS LDS stages; step kt reads stage kt % NS.
+  // In step kt: sub-steps 0 .. BK/16-2 run their MFMAs while reading the next
+  // sub-step's fragments; then, once this wave's loads of step kt+1 have
+  // landed (those of steps kt+2 .. kt+NS-1 may still be in flight), one
+  // barrier, after which the loads of step kt+NS refill stage kt % NS (every
+  // wave is done reading it) while the last sub-step's MFMAs run alongside the
+  // first fragment reads of step kt+1. A load therefore has NS-1 steps of
+  // compute to land in. Past the last step the loads repeat step nk-1 into a
+  // stage nobody reads again, which keeps the loop free of branches around
+  // them.
+  const int nk = K / BK;
+  constexpr int kLast = BK / 16 - 1;  // last sub-step of a K step
+  auto step = [&](auto S, int kt) __attribute__((always_inline)) {
+    const uint16_t* cur = stage(S);
+    const uint16_t* nxt = stage(std::integral_constant<int, decltype(S)::value + 1>{});
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+    for (int kk = 0; kk < kLast; ++kk) {
       fload((kk + 1) & 1, cur, kk + 1);
       mfmas(kk & 1);
       // the reads go out early, one per MFMA, so they land before sub-step kk+1
@@ -263,31 +294,47 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
       }
       if constexpr (kMF > kFR) __builtin_amdgcn_sched_group_barrier(0x008, kMF - kFR, 0);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt((NS - 2) * (AI + BI)));
     __syncthreads();
-    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
-    issue(const_cast<uint16_t*>(cur), kn * kBK);
+    const int kn = kt + NS < nk ? kt + NS : nk - 1;
+    issue(const_cast<uint16_t*>(cur), kn * BK);
     fload(0, nxt, 0);
-    mfmas(1);
+    mfmas(kLast & 1);
 #pragma unroll
     for (int i = 0; i < kFR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, (AI + BI) / kFR, 0);  // global -> LDS
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, (AI + BI + kFR - 1) / kFR, 0);  // global -> LDS
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
     if constexpr (kMF > kFR) __builtin_amdgcn_sched_group_barrier(0x008, kMF - kFR, 0);
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  // prologue: steps 0 .. NS-1 into stages 0 .. NS-1, step 0 landed
+  const auto clampk = [&](int k) { return (k < nk ? k : nk - 1) * BK; };
   issue(lds0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  issue(lds1, clampk(1));
+  if constexpr (NS > 2) issue(lds2, clampk(2));
+  if constexpr (NS > 3) issue(lds3, clampk(3));
+  if constexpr (NS > 4) issue(lds4, clampk(4));
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt((NS - 1) * (AI + BI)));
   __syncthreads();
-  issue(lds1, (nk > 1 ? 1 : 0) * kBK);
   fload(0, lds0, 0);
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(lds0, lds1, kt);
-    step(lds1, lds0, kt + 1);
+  for (; kt + NS <= nk; kt += NS) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    if constexpr (NS > 2) step(I2{}, kt + 2);
+    if constexpr (NS > 3) step(I3{}, kt + 3);
+    if constexpr (NS > 4) step(I4{}, kt + 4);
   }
-  if (kt < nk) step(lds0, lds1, kt);
+  if (kt < nk) step(I0{}, kt);
+  if (kt + 1 < nk) step(I1{}, kt + 1);
+  if constexpr (NS > 2) if (kt + 2 < nk) step(I2{}, kt + 2);
+  if constexpr (NS > 3) if (kt + 3 < nk) step(I3{}, kt + 3);
   // the trailing loads must land before the block's LDS is released
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -316,7 +363,13 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   }
 }
 
-template <int BM, int BN, int OCC>
+// Large tiles: K step and LDS stages of the pipeline. 64 x 2 measured faster
+// than 32 x 3 and 32 x 4 (local layer 806 vs 889 and 880 us): the schedule,
+// not uncovered load latency, bounds this kernel.
+constexpr int kLargeBK = 64;
+constexpr int kLargeNS = 2;
+
+template <int BM, int BN, int OCC, int BK, int NS>
 hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, int sstride,
                    int sbase, const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                    const void* w_down, void* hbuf, void* out, hipStream_t s) {
@@ -325,13 +378,13 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, 
     return (unsigned)(kXCD * ((mtb + kXCD - 1) / kXCD) * ntiles);
   };
   const int nt1 = I / (BN / 2);
-  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
+  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC, BK, NS>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E, sg,
                           sstride, sbase, static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
                           static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, kGroupM);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
-  return launch(ffn_gemm_kernel<false, BM, BN, OCC>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
+  return launch(ffn_gemm_kernel<false, BM, BN, OCC, BK, NS>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E, sg, sstride,
                 sbase, static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
                 static_cast<uint16_t*>(out), (int64_t)H, nt2, kGroupM);
@@ -345,10 +398,10 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
                                        const void* w_down, void* hbuf, void* out, hipStream_t s) {
   if (rows == 0 || n == 0) return hipSuccess;
   if (I % 128 == 0 && H % 256 == 0)
-    return run_ffn<256, 256, 1>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts, w_gate_up,
-                                w_down, hbuf, out, s);
-  return run_ffn<128, 128, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts, w_gate_up,
-                              w_down, hbuf, out, s);
+    return run_ffn<256, 256, 1, kLargeBK, kLargeNS>(send, rows, H, I, n, sg, sstride, sbase, offs,
+                                                    cnts, w_gate_up, w_down, hbuf, out, s);
+  return run_ffn<128, 128, 2, 64, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts,
+                                     w_gate_up, w_down, hbuf, out, s);
 }
 
 hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, int E,
