@@ -9,12 +9,13 @@
 //
 // Both are A[M_e x K] * B[N x K]^T with K contiguous in both operands, on
 // v_mfma_f32_32x32x16_bf16. Two tile shapes, one kernel template:
-//   large: 256 x 256 x 64 per 256-thread block, each wave 128 x 128 (4 x 4 MFMA
-//          tiles, 256 fp32 accumulators per lane): 8 fragment reads per 16 MFMAs
-//          and half the L2 traffic per flop of the small tile. Needs I % 128 == 0
-//          and H % 256 == 0.
-//   small: 128 x 128 x 64, each wave 64 x 64 (2 x 2 tiles); any I % 64 == 0 and
-//          H % 128 == 0.
+//   large: 256 x 256 x 64 per 512-thread block, 8 waves as 2 x 4, each wave
+//          128 x 64 (4 x 2 MFMA tiles, 128 fp32 accumulators per lane), two
+//          waves per SIMD so one issues MFMAs while the other waits on LDS or
+//          the barrier (11% faster than 4 waves of 128 x 128). Needs
+//          I % 128 == 0 and H % 256 == 0.
+//   small: 128 x 128 x 64, 4 waves of 64 x 64 (2 x 2 tiles), two blocks per
+//          compute unit; any I % 64 == 0 and H % 128 == 0.
 // Global -> LDS moves go through buffer loads with the LDS bit (16 bytes a
 // lane straight into LDS, no registers, hardware range check for partial
 // m-tiles). LDS holds two K steps of A and B; a tile row is 64 bf16 = eight
@@ -41,9 +42,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+constexpr int kWavesM = 2;  // waves along M in a block (WN along N)
 constexpr int kXCD = 8;
-constexpr int kGroupM = 1;  // m-tiles per rasterisation patch (2, 4, 8 measured no faster)
+// m-tiles per rasterisation patch: on the local layer 1 measured 701 us against
+// 714 for 4 (an even split of rows favours 4-16 by ~3%; the layer is skewed)
+constexpr int kGroupM = 1;
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
@@ -87,18 +90,19 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-// BM x BN block tile; each of the 2 x 2 waves computes (BM/2) x (BN/2) as
+// BM x BN block tile; each of the 2 x WN waves computes (BM/2) x (BN/WN) as
 // MI x NI tiles of 32 x 32. K steps of BK, NS LDS stages.
-template <bool kGateUp, int BM, int BN, int OCC, int BK, int NS>
-__global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
+template <bool kGateUp, int BM, int BN, int OCC, int BK, int NS, int WN>
+__global__ __launch_bounds__(kWave * kWavesM * WN, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, int sg, int sstride, int sbase,
     const uint16_t* __restrict__ Bw, int64_t bstride,
     int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int gm) {
-  constexpr int MI = BM / 64, NI = BN / 64;  // 32x32 tiles per wave
+  constexpr int NW = kWavesM * WN;           // waves in the block
+  constexpr int MI = BM / kWavesM / 32, NI = BN / WN / 32;  // 32x32 tiles per wave
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
   constexpr int RPI = kWave / CPR;           // tile rows per load instruction (1 KiB)
-  constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // load instructions per wave per K step
+  constexpr int AI = BM / NW / RPI, BI = BN / NW / RPI;  // load instructions per wave per K step
   constexpr int kStage = (BM + BN) * BK;     // elements of one A + B stage
   static_assert(NS >= 2 && NS <= 5, "LDS stages");
   // The stages as separate arrays, so the compiler can tell the loads into one
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   };
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WN, wn = wid % WN;
 
   // ---- which tile. The m-tiles (every expert's rows in BM-row tiles, in
   // expert order) are split into 8 contiguous shares, one per XCD, so an XCD
@@ -208,31 +212,32 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
   uint32_t aoff[AI], boff[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int r = wid * (BM / 4) + RPI * i + lr;
+    const int r = wid * (BM / NW) + RPI * i + lr;
     aoff[i] = (uint32_t)(((int64_t)r * lda + ((ls ^ swz_key<BK>(r)) << 3)) * 2);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int r = wid * (BN / 4) + RPI * i + lr;
+    const int r = wid * (BN / NW) + RPI * i + lr;
     boff[i] = (uint32_t)(((int64_t)brow(r) * K + ((ls ^ swz_key<BK>(r)) << 3)) * 2);
   }
   auto issue = [&](uint16_t* As, int k0) __attribute__((always_inline)) {
     uint16_t* Bs = As + BM * BK;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
-      load_lds16(arsrc, As + (wid * (BM / 4) + RPI * i) * BK, aoff[i], 2 * k0);
+      load_lds16(arsrc, As + (wid * (BM / NW) + RPI * i) * BK, aoff[i], 2 * k0);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      load_lds16(brsrc, Bs + (wid * (BN / 4) + RPI * i) * BK, boff[i], 2 * k0);
+      load_lds16(brsrc, Bs + (wid * (BN / NW) + RPI * i) * BK, boff[i], 2 * k0);
   };
 
   // B tile row of fragment ni for this wave: gate/up tiles put the wave's gate
   // columns in ni < NI/2 and the matching up columns in ni >= NI/2.
   auto bfrag_row = [&](int ni) -> int {
     if constexpr (kGateUp)
-      return ni < NI / 2 ? wn * (BN / 4) + ni * 32 : BN / 2 + wn * (BN / 4) + (ni - NI / 2) * 32;
+      return ni < NI / 2 ? wn * (BN / 2 / WN) + ni * 32
+                         : BN / 2 + wn * (BN / 2 / WN) + (ni - NI / 2) * 32;
     else
-      return wn * (BN / 2) + ni * 32;
+      return wn * (BN / WN) + ni * 32;
   };
 
   f32x16 acc[MI][NI];
@@ -352,12 +357,12 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
         for (int ni = 0; ni < NI / 2; ++ni) {
           const float g = acc[mi][ni][r], u = acc[mi][ni + NI / 2][r];
           const float h = (g / (1.0f + expf(-g))) * u;
-          crow[ntile * (BN / 2) + wn * (BN / 4) + ni * 32 + (lane & 31)] = bf16_bits(h);
+          crow[ntile * (BN / 2) + wn * (BN / 2 / WN) + ni * 32 + (lane & 31)] = bf16_bits(h);
         }
       } else {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          crow[ntile * BN + wn * (BN / 2) + ni * 32 + (lane & 31)] = bf16_bits(acc[mi][ni][r]);
+          crow[ntile * BN + wn * (BN / WN) + ni * 32 + (lane & 31)] = bf16_bits(acc[mi][ni][r]);
       }
     }
   }
@@ -368,8 +373,9 @@ __global__ __launch_bounds__(kThreads, OCC) void ffn_gemm_kernel(
 // not uncovered load latency, bounds this kernel.
 constexpr int kLargeBK = 64;
 constexpr int kLargeNS = 2;
+constexpr int kLargeWN = 4;  // waves along N: 8 waves, two per SIMD
 
-template <int BM, int BN, int OCC, int BK, int NS>
+template <int BM, int BN, int OCC, int BK, int NS, int WN>
 hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, int sstride,
                    int sbase, const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                    const void* w_down, void* hbuf, void* out, hipStream_t s) {
@@ -378,13 +384,15 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, 
     return (unsigned)(kXCD * ((mtb + kXCD - 1) / kXCD) * ntiles);
   };
   const int nt1 = I / (BN / 2);
-  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC, BK, NS>, dim3(grid_of(nt1)), dim3(kThreads), 0, s,
+  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC, BK, NS, WN>, dim3(grid_of(nt1)),
+                          dim3(kWave * kWavesM * WN), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E, sg,
                           sstride, sbase, static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
                           static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, kGroupM);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
-  return launch(ffn_gemm_kernel<false, BM, BN, OCC, BK, NS>, dim3(grid_of(nt2)), dim3(kThreads), 0, s,
+  return launch(ffn_gemm_kernel<false, BM, BN, OCC, BK, NS, WN>, dim3(grid_of(nt2)),
+                dim3(kWave * kWavesM * WN), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E, sg, sstride,
                 sbase, static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
                 static_cast<uint16_t*>(out), (int64_t)H, nt2, kGroupM);
@@ -398,9 +406,9 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
                                        const void* w_down, void* hbuf, void* out, hipStream_t s) {
   if (rows == 0 || n == 0) return hipSuccess;
   if (I % 128 == 0 && H % 256 == 0)
-    return run_ffn<256, 256, 1, kLargeBK, kLargeNS>(send, rows, H, I, n, sg, sstride, sbase, offs,
+    return run_ffn<256, 256, 1, kLargeBK, kLargeNS, kLargeWN>(send, rows, H, I, n, sg, sstride, sbase, offs,
                                                     cnts, w_gate_up, w_down, hbuf, out, s);
-  return run_ffn<128, 128, 2, 64, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts,
+  return run_ffn<128, 128, 2, 64, 2, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts,
                                      w_gate_up, w_down, hbuf, out, s);
 }
 
