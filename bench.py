@@ -35,6 +35,7 @@ import os
 import platform
 import sys
 import time
+from types import SimpleNamespace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -286,6 +287,334 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
     return res
 
 
+def make_context(wl, moe, torch, np):
+    """Device inputs, the shared output buffers and the pre-marshalled C-ABI
+    arguments of one workload (everything the mode builders draw on)."""
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    c = SimpleNamespace(wl=wl, moe=moe, torch=torch, dev=dev, tdt=tdt, to_dev=to_dev,
+                        T=wl.T, H=wl.H, E=wl.E, k=wl.k, R=wl.R, W=wl.W,
+                        swiglu=wl.expert == "swiglu")
+    c.logits_np, c.x_np = synth.logits(wl), synth.hidden(wl)
+    c.logits, c.x = to_dev(c.logits_np), to_dev(c.x_np)
+    c.shape = moe.Shape(c.T, c.H, c.E, c.k, c.R, c.W, tdt)
+    c.topk_idx = torch.empty((c.T, c.k), dtype=torch.int32, device=dev)
+    c.topk_w = torch.empty((c.T, c.k), dtype=torch.float32, device=dev)
+    c.y = torch.empty((c.T, c.H), dtype=tdt, device=dev)
+    c.stats_raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=dev)
+    c.ffn_np = synth.swiglu_weights(wl) if c.swiglu else None
+    # Pre-marshalled C-ABI calls: the per-step host cost is a few foreign calls.
+    c.L = moe.lib()
+    c.sh = c.shape.c()
+    c.shp = ctypes.byref(c.sh)
+    c.P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    c.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return c
+
+
+# A mode builder returns the step as a list of calls, each (C function,
+# arguments, [(stage, kernel) per kernel it launches, in order]), plus what the
+# report needs: the algorithmic byte model (evaluated after the timed loops),
+# the counts the Dirichlet fit reads, the step's description and extra config.
+
+def path_default(c, args):
+    """route + index (+ stats) + copy + experts + combine: moe_route_index (5
+    kernels a step) or, with --unfused, separate calls (7)."""
+    moe, L, P, shp, s = c.moe, c.L, c.P, c.shp, c.stream
+    buf = moe.alloc_dispatch(c.shape, c.dev)
+    expert_out = torch_empty_like(c, buf["send_buf"])
+    index_args = (P(buf["expert_counts"]), P(buf["expert_offsets"]), P(buf["rank_counts"]),
+                  P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
+                  P(buf["row_token"]))
+    if c.swiglu:
+        gu, dn = c.to_dev(c.ffn_np[0]), c.to_dev(c.ffn_np[1])
+        ws = c.torch.empty((moe.expert_swiglu_workspace_bytes(c.shape, c.wl.I),),
+                           dtype=c.torch.uint8, device=c.dev)
+        c.keep = (gu, dn, ws)
+        expert = (L.moe_expert_swiglu, (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]),
+                                        P(buf["expert_counts"]), P(gu), P(dn), P(expert_out),
+                                        P(ws), ws.numel(), s),
+                  [("expert", "ffn_gemm_kernel<gate_up>"), ("expert", "ffn_gemm_kernel<down>")])
+    else:
+        expert = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
+                                       P(buf["expert_counts"]), P(expert_out), s),
+                  [("expert", "expert_scale_kernel")])
+    if args.unfused:
+        calls = [
+            (L.moe_route, (P(c.logits), c.T, c.E, c.k, P(c.topk_idx), P(c.topk_w), s),
+             [("route", "route_kernel")]),
+            (L.moe_dispatch_index, (shp, P(c.topk_idx), *index_args, P(buf["workspace"]),
+                                    buf["workspace"].numel(), s),
+             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel")]),
+        ]
+        desc = "route+dispatch_index+stats (separate calls)+dispatch_copy+expert+combine"
+    else:
+        calls = [
+            (L.moe_route_index, (shp, P(c.logits), P(c.topk_idx), P(c.topk_w), *index_args,
+                                 P(c.stats_raw), P(buf["workspace"]), buf["workspace"].numel(), s),
+             [("route", "route_count_kernel"), ("dispatch_index", "place_kernel(+stats block)")]),
+        ]
+        desc = "route+dispatch_index+stats (moe_route_index)+dispatch_copy+expert+combine"
+    calls += [
+        (L.moe_dispatch_copy, (shp, P(c.x), P(buf["pos"]), P(buf["send_buf"]), s),
+         [("dispatch_copy", "copy_kernel")]),
+        expert,
+        (L.moe_combine, (shp, P(expert_out), P(c.topk_w), P(buf["pos"]), P(c.y), s),
+         [("combine", "combine_kernel")]),
+    ]
+    if args.unfused:
+        calls.append((L.moe_stats, (P(buf["expert_counts"]), c.E, c.R, P(c.stats_raw), s),
+                      [("stats", "stats_kernel")]))
+    return SimpleNamespace(calls=calls, nbytes=lambda: algorithmic_bytes(c.wl),
+                           counts=buf["expert_counts"], desc=desc, config=lambda: {})
+
+
+def path_capacity(c, args):
+    """Capacity-factor dispatch: route, count/place/copy/pad, experts and
+    combine over the padded buckets, stats of the kept counts."""
+    moe, L, P, shp, s = c.moe, c.L, c.P, c.shp, c.stream
+    cap = moe.expert_capacity(c.k, args.capacity_factor, c.T, c.E)
+    cbuf = moe.alloc_dispatch_capacity(c.shape, cap, c.dev)
+    ceo = torch_empty_like(c, cbuf["send_buf"])
+    rows = cbuf["rows"]
+    calls = [
+        (L.moe_route, (P(c.logits), c.T, c.E, c.k, P(c.topk_idx), P(c.topk_w), s),
+         [("route", "route_kernel")]),
+        (L.moe_dispatch_capacity, (
+            shp, cap, P(c.x), P(c.topk_idx), P(cbuf["send_buf"]), P(cbuf["kept_counts"]),
+            P(cbuf["expert_offsets"]), P(cbuf["rank_counts"]), P(cbuf["rank_offsets"]),
+            P(cbuf["wave_offsets"]), P(cbuf["pos"]), P(cbuf["row_token"]),
+            P(cbuf["workspace"]), cbuf["workspace"].numel(), s),
+         [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(capacity)"),
+          ("dispatch_copy", "copy_kernel"), ("dispatch_copy", "pad_kernel")]),
+        (L.moe_expert_scale_rows, (shp, rows, P(cbuf["send_buf"]), P(cbuf["expert_offsets"]),
+                                   P(cbuf["kept_counts"]), P(ceo), s),
+         [("expert", "expert_scale_kernel")]),
+        (L.moe_combine_rows, (shp, rows, P(ceo), P(c.topk_w), P(cbuf["pos"]), P(c.y), s),
+         [("combine", "combine_kernel")]),
+        (L.moe_stats, (P(cbuf["kept_counts"]), c.E, c.R, P(c.stats_raw), s),
+         [("stats", "stats_kernel")]),
+    ]
+
+    def kept():
+        return int(cbuf["kept_counts"].sum().item())
+
+    return SimpleNamespace(
+        calls=calls, nbytes=lambda: capacity_bytes(c.wl, cap, kept()),
+        counts=cbuf["kept_counts"],
+        desc="route+dispatch_capacity(count,place,copy,pad)+expert+combine+stats",
+        config=lambda: dict(capacity_factor=args.capacity_factor, capacity=cap,
+                            kept_picks=kept(), dropped_picks=c.T * c.k - kept()))
+
+
+def path_vsrc(c, args):
+    """The exchange of R virtual ranks on one device: route, every source's
+    dispatch + the count exchange, the all-to-all and the regroup (or, with
+    --direct, one copy into the grouped layout), experts, the way back,
+    combine, stats."""
+    moe, L, P, shp, s = c.moe, c.L, c.P, c.shp, c.stream
+    vb = moe.alloc_vsrc(c.shape, c.dev)
+    veo = torch_empty_like(c, vb["send_buf"])
+    back_recv = torch_empty_like(c, vb["recv_buf"])
+    back_send = torch_empty_like(c, vb["send_buf"])
+    # the regrouped rows are in plain expert order: the bucket order of W = 1
+    c.sh1 = moe.Shape(c.T, c.H, c.E, c.k, c.R, 1, c.tdt).c()
+    shp1 = ctypes.byref(c.sh1)
+    vws = (P(vb["workspace"]), vb["workspace"].numel())
+    ex_tabs = (P(vb["send_offsets"]), P(vb["recv_counts"]), P(vb["recv_offsets"]))
+    rg_tabs = (P(vb["src_counts"]), P(vb["recv_offsets"]), P(vb["expert_offsets"]))
+    dr_tabs = (P(vb["src_counts"]), P(vb["src_offsets"]), P(vb["expert_offsets"]))
+    head = [
+        (L.moe_route, (P(c.logits), c.T, c.E, c.k, P(c.topk_idx), P(c.topk_w), s),
+         [("route", "route_kernel")]),
+        (L.moe_vsrc_dispatch, (
+            shp, P(c.x), P(c.topk_idx), P(vb["send_buf"]), P(vb["src_counts"]),
+            P(vb["src_offsets"]), P(vb["send_counts"]), P(vb["send_offsets"]),
+            P(vb["recv_counts"]), P(vb["recv_offsets"]), P(vb["expert_counts"]),
+            P(vb["expert_offsets"]), P(vb["pos"]), *vws, s),
+         [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(sources)"),
+          ("dispatch_index", "vsrc_plan_kernel"), ("dispatch_copy", "copy_kernel")]),
+    ]
+    experts = (L.moe_expert_scale_rows, (shp1, c.T * c.k, P(vb["grouped"]),
+                                         P(vb["expert_offsets"]), P(vb["expert_counts"]),
+                                         P(veo), s),
+               [("expert", "expert_scale_kernel")])
+    if args.direct:  # one copy each way: send <-> grouped
+        middle = [
+            (L.moe_vsrc_exchange_direct, (shp, 0, P(vb["send_buf"]), P(vb["grouped"]), *dr_tabs,
+                                          *vws, s),
+             [("dispatch_index", "regroup_plan_kernel"), ("exchange", "segcopy_kernel<direct>")]),
+            experts,
+            (L.moe_vsrc_exchange_direct, (shp, 1, P(veo), P(back_send), *dr_tabs, *vws, s),
+             [("dispatch_index", "regroup_plan_kernel"), ("exchange", "segcopy_kernel<direct>")]),
+        ]
+        desc = "direct exchange+expert+direct exchange back"
+    else:
+        middle = [
+            (L.moe_vsrc_exchange, (shp, 0, P(vb["send_buf"]), P(vb["recv_buf"]), *ex_tabs, s),
+             [("exchange", "segcopy_kernel<exchange>")]),
+            (L.moe_vsrc_regroup, (shp, 0, P(vb["recv_buf"]), P(vb["grouped"]), *rg_tabs, *vws, s),
+             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
+            experts,
+            (L.moe_vsrc_regroup, (shp, 1, P(veo), P(back_recv), *rg_tabs, *vws, s),
+             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
+            (L.moe_vsrc_exchange, (shp, 1, P(back_recv), P(back_send), *ex_tabs, s),
+             [("exchange", "segcopy_kernel<exchange>")]),
+        ]
+        desc = "exchange+regroup+expert+ungroup+exchange back"
+    tail = [
+        (L.moe_combine, (shp, P(back_send), P(c.topk_w), P(vb["pos"]), P(c.y), s),
+         [("combine", "combine_kernel")]),
+        (L.moe_stats, (P(vb["expert_counts"]), c.E, c.R, P(c.stats_raw), s),
+         [("stats", "stats_kernel")]),
+    ]
+    return SimpleNamespace(
+        calls=head + middle + tail,
+        nbytes=lambda: vsrc_bytes(c.wl, int(vb["expert_counts"].sum().item())),
+        counts=vb["expert_counts"],
+        desc="route+vsrc_dispatch(count,place,plan,copy)+" + desc + "+combine+stats",
+        config=lambda: {})
+
+
+def torch_empty_like(c, t):
+    return c.torch.empty_like(t)
+
+
+class StepRunner:
+    """Runs the calls of one step; with event arrays, every kernel a call
+    launches records start/stop events through the library's timing hook."""
+
+    NPAIR = 4  # event pairs per call (a call launches at most 4 kernels)
+
+    def __init__(self, c, calls):
+        self.c, self.calls = c, calls
+        self.hipev = HipEvents()
+        self.stages = [st for st in STAGES if any(st == g for cl in calls for g, _ in cl[2])]
+        self.kernel_of = {st: "+".join(dict.fromkeys(kn for cl in calls for g, kn in cl[2]
+                                                     if g == st)) for st in self.stages}
+        self.launches_of = {st: sum(1 for cl in calls for g, _ in cl[2] if g == st)
+                            for st in self.stages}
+        self.kernel_ms = {}
+
+    def step(self, evs=None):
+        """One pass of the path; evs[i] = (starts, stops) event arrays of call i."""
+        L = self.c.L
+        for i, (fn, a, kernels) in enumerate(self.calls):
+            if evs is not None:
+                L.moe_set_timing_events(evs[i][0], evs[i][1], self.NPAIR)
+            st = fn(*a)
+            if evs is not None:
+                n = L.moe_timed_launches()
+                L.moe_set_timing_events(None, None, 0)
+                if n != len(kernels):
+                    raise RuntimeError(f"call {i} launched {n} kernels, expected {len(kernels)}")
+            if st != 0:
+                raise RuntimeError(f"call {i}: {self.c.moe.status_string(st)}")
+
+    def new_events(self, n):
+        def arr():
+            return (ctypes.c_void_p * self.NPAIR)(*[self.hipev.create() for _ in range(self.NPAIR)])
+        return [[(arr(), arr()) for _ in self.calls] for _ in range(n)]
+
+    def stage_means(self, evs):
+        """Per stage: summed execution time of its kernels, averaged over steps
+        (and each kernel's mean time per launch into kernel_ms)."""
+        tot = {st: 0.0 for st in self.stages}
+        per, n = {}, {}
+        for e in evs:
+            for i, (_, _, kernels) in enumerate(self.calls):
+                for j, (st, kn) in enumerate(kernels):
+                    t = self.hipev.ms(e[i][0][j], e[i][1][j])
+                    tot[st] += t
+                    per[kn] = per.get(kn, 0.0) + t
+                    n[kn] = n.get(kn, 0) + 1
+        self.kernel_ms = {kn: per[kn] / n[kn] for kn in per}
+        return {st: v / len(evs) for st, v in tot.items()}
+
+    def graph_wall(self, K):
+        """K replays of the step captured in one HIP graph on a side stream."""
+        torch = self.c.torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        stream_c = ctypes.c_void_p(side.cuda_stream)
+        saved = list(self.calls)
+        for i, (fn, a, kn) in enumerate(self.calls):  # rebind the stream argument
+            self.calls[i] = (fn, tuple(stream_c if v is self.c.stream else v for v in a), kn)
+        with torch.cuda.stream(side):
+            self.step()
+            torch.cuda.current_stream().synchronize()
+            with torch.cuda.graph(g, stream=side):
+                self.step()
+        torch.cuda.synchronize()
+        self.calls[:] = saved
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+
+def plain_copy_gbs(torch, dev) -> float:
+    """The HIP runtime's own copy of 1 GiB (beyond the Infinity Cache): a
+    reference streaming rate on this machine, read + write."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(5):
+        dst.copy_(src)
+    cb.record()
+    torch.cuda.synchronize()
+    return 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+
+
+def dirichlet_fit(moe, torch, counts, dev) -> dict:
+    """Fitted symmetric Dirichlet alpha of this step's counts: a summary of S
+    computed on demand (its own launch), timed apart from the step."""
+    alpha_t = torch.empty((1,), dtype=torch.float64, device=dev)
+    moe.dirichlet_alpha_device(counts, alpha_t)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(20):
+        moe.dirichlet_alpha_device(counts, alpha_t)
+    eb.record()
+    torch.cuda.synchronize()
+    return {"value": float(alpha_t.item()), "us": round(ea.elapsed_time(eb) * 1e3 / 20, 2),
+            "kernel": "dirichlet_alpha_kernel", "in_step": False}
+
+
+def wave_sweep_result(args, wl, moe, torch, np, c) -> dict:
+    ws_res = wave_sweep(args, wl, moe, torch, np, c.to_dev, c.logits_np, c.x_np)
+    best = ws_res["W"].index(ws_res["W_best_measured"])
+    ms = ws_res["ms_two_streams"][best]
+    return {
+        "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded logits and hidden states; random-init SwiGLU expert weights)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k,
+                   "virtual_ranks": wl.R, "waves": ws_res["W_best_measured"], "I": wl.I,
+                   "expert": wl.expert,
+                   "step": "route+index (moe_route_index) + per wave: gather dispatch (copy "
+                           "stream) -> FFN (compute stream) + combine"},
+        "wave_sweep": ws_res,
+    }
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -303,332 +632,79 @@ def main() -> int:
 
     wl = synth.WORKLOADS[args.workload]
     swiglu = wl.expert == "swiglu"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    T, H, E, k, R, W = wl.T, wl.H, wl.E, wl.k, wl.R, wl.W
-    print(f"[bench] workload {wl.name}: T={T} H={H} E={E} k={k} R={R} W={W} {wl.dtype} "
-          f"expert={wl.expert}", file=sys.stderr, flush=True)
-
-    def to_dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    logits_np, x_np = synth.logits(wl), synth.hidden(wl)
+    if args.wave_sweep and not swiglu:
+        print("--wave-sweep runs the SwiGLU local layer (--workload local_layer)", file=sys.stderr)
+        return 2
+    if (args.capacity_factor is not None or args.vsrc) and swiglu:
+        print("--capacity-factor and --vsrc run the identity-scaled experts", file=sys.stderr)
+        return 2
+    if args.capacity_factor is not None and args.vsrc:
+        print("--vsrc runs without a capacity", file=sys.stderr)
+        return 2
+    print(f"[bench] workload {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W} "
+          f"{wl.dtype} expert={wl.expert}", file=sys.stderr, flush=True)
+    c = make_context(wl, moe, torch, np)
     if args.wave_sweep:
-        if not swiglu:
-            print("--wave-sweep runs the SwiGLU local layer (--workload local_layer)",
-                  file=sys.stderr)
-            return 2
-        ws_res = wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np)
-        best = ws_res["W"].index(ws_res["W_best_measured"])
-        ms = ws_res["ms_two_streams"][best]
-        result = {
-            "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-            "data": "synthetic (seeded logits and hidden states; random-init SwiGLU expert weights)",
-            "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
-                       "waves": ws_res["W_best_measured"], "I": wl.I, "expert": wl.expert,
-                       "step": "route+index (moe_route_index) + per wave: gather dispatch (copy "
-                               "stream) -> FFN (compute stream) + combine"},
-            "wave_sweep": ws_res,
-        }
-        print(json.dumps(result), flush=True)
+        print(json.dumps(wave_sweep_result(args, wl, moe, torch, np, c)), flush=True)
         return 0
-    logits, x = to_dev(logits_np), to_dev(x_np)
-    shape = moe.Shape(T, H, E, k, R, W, tdt)
-    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    buf = moe.alloc_dispatch(shape, dev)
-    expert_out = torch.empty_like(buf["send_buf"])
-    y = torch.empty((T, H), dtype=tdt, device=dev)
-    stats_raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=dev)
-    ffn_np = None
-    if swiglu:
-        ffn_np = synth.swiglu_weights(wl)
-        w_gu, w_dn = to_dev(ffn_np[0]), to_dev(ffn_np[1])
-        ffn_ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
-                             device=dev)
-
-    # Pre-marshalled C-ABI calls: the per-step host cost is six foreign calls.
-    L = moe.lib()
-    sh = shape.c()
-    shp = ctypes.byref(sh)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    index_args = (P(buf["expert_counts"]), P(buf["expert_offsets"]), P(buf["rank_counts"]),
-                  P(buf["rank_offsets"]), P(buf["wave_offsets"]), P(buf["pos"]),
-                  P(buf["row_token"]))
-    if swiglu:
-        expert_call = (L.moe_expert_swiglu, (
-            shp, wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
-            P(w_gu), P(w_dn), P(expert_out), P(ffn_ws), ffn_ws.numel(), stream))
-        expert_kernels = [("expert", "ffn_gemm_kernel<gate_up>"),
-                          ("expert", "ffn_gemm_kernel<down>")]
-    else:
-        expert_call = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
-                                            P(buf["expert_counts"]), P(expert_out), stream))
-        expert_kernels = [("expert", "expert_scale_kernel")]
-    # Each call: (C function, arguments, [(stage, kernel) per kernel it launches, in order]).
-    if args.unfused:
-        calls = [
-            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
-             [("route", "route_kernel")]),
-            (L.moe_dispatch_index, (shp, P(topk_idx), *index_args, P(buf["workspace"]),
-                                    buf["workspace"].numel(), stream),
-             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel")]),
-        ]
-    else:
-        calls = [
-            (L.moe_route_index, (shp, P(logits), P(topk_idx), P(topk_w), *index_args,
-                                 P(stats_raw), P(buf["workspace"]), buf["workspace"].numel(),
-                                 stream),
-             [("route", "route_count_kernel"), ("dispatch_index", "place_kernel(+stats block)")]),
-        ]
-    calls += [
-        (L.moe_dispatch_copy, (shp, P(x), P(buf["pos"]), P(buf["send_buf"]), stream),
-         [("dispatch_copy", "copy_kernel")]),
-        (*expert_call, expert_kernels),
-        (L.moe_combine, (shp, P(expert_out), P(topk_w), P(buf["pos"]), P(y), stream),
-         [("combine", "combine_kernel")]),
-    ]
-    if args.unfused:
-        calls.append((L.moe_stats, (P(buf["expert_counts"]), E, R, P(stats_raw), stream),
-                      [("stats", "stats_kernel")]))
-    cap = kept = None
     if args.capacity_factor is not None:
-        if swiglu:
-            print("--capacity-factor runs the identity-scaled experts only", file=sys.stderr)
-            return 2
-        cap = moe.expert_capacity(k, args.capacity_factor, T, E)
-        cbuf = moe.alloc_dispatch_capacity(shape, cap, dev)
-        ceo = torch.empty_like(cbuf["send_buf"])
-        rows = cbuf["rows"]
-        calls = [
-            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
-             [("route", "route_kernel")]),
-            (L.moe_dispatch_capacity, (
-                shp, cap, P(x), P(topk_idx), P(cbuf["send_buf"]), P(cbuf["kept_counts"]),
-                P(cbuf["expert_offsets"]), P(cbuf["rank_counts"]), P(cbuf["rank_offsets"]),
-                P(cbuf["wave_offsets"]), P(cbuf["pos"]), P(cbuf["row_token"]),
-                P(cbuf["workspace"]), cbuf["workspace"].numel(), stream),
-             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(capacity)"),
-              ("dispatch_copy", "copy_kernel"), ("dispatch_copy", "pad_kernel")]),
-            (L.moe_expert_scale_rows, (shp, rows, P(cbuf["send_buf"]), P(cbuf["expert_offsets"]),
-                                       P(cbuf["kept_counts"]), P(ceo), stream),
-             [("expert", "expert_scale_kernel")]),
-            (L.moe_combine_rows, (shp, rows, P(ceo), P(topk_w), P(cbuf["pos"]), P(y), stream),
-             [("combine", "combine_kernel")]),
-            (L.moe_stats, (P(cbuf["kept_counts"]), E, R, P(stats_raw), stream),
-             [("stats", "stats_kernel")]),
-        ]
-    if args.vsrc:
-        if swiglu or cap is not None:
-            print("--vsrc runs the identity-scaled experts without a capacity", file=sys.stderr)
-            return 2
-        vb = moe.alloc_vsrc(shape, dev)
-        veo = torch.empty_like(vb["send_buf"])
-        vback_recv = torch.empty_like(vb["recv_buf"])
-        vback_send = torch.empty_like(vb["send_buf"])
-        # the regrouped rows are in plain expert order: the bucket order of W = 1
-        sh1 = moe.Shape(T, H, E, k, R, 1, tdt).c()
-        shp1 = ctypes.byref(sh1)
-        vws = (P(vb["workspace"]), vb["workspace"].numel())
-        ex_tabs = (P(vb["send_offsets"]), P(vb["recv_counts"]), P(vb["recv_offsets"]))
-        rg_tabs = (P(vb["src_counts"]), P(vb["recv_offsets"]), P(vb["expert_offsets"]))
-        calls = [
-            (L.moe_route, (P(logits), T, E, k, P(topk_idx), P(topk_w), stream),
-             [("route", "route_kernel")]),
-            (L.moe_vsrc_dispatch, (
-                shp, P(x), P(topk_idx), P(vb["send_buf"]), P(vb["src_counts"]),
-                P(vb["src_offsets"]), P(vb["send_counts"]), P(vb["send_offsets"]), P(vb["recv_counts"]),
-                P(vb["recv_offsets"]), P(vb["expert_counts"]), P(vb["expert_offsets"]),
-                P(vb["pos"]), *vws, stream),
-             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel(sources)"),
-              ("dispatch_index", "vsrc_plan_kernel"), ("dispatch_copy", "copy_kernel")]),
-            (L.moe_vsrc_exchange, (shp, 0, P(vb["send_buf"]), P(vb["recv_buf"]), *ex_tabs, stream),
-             [("exchange", "segcopy_kernel<exchange>")]),
-            (L.moe_vsrc_regroup, (shp, 0, P(vb["recv_buf"]), P(vb["grouped"]), *rg_tabs, *vws,
-                                  stream),
-             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
-            (L.moe_expert_scale_rows, (shp1, T * k, P(vb["grouped"]), P(vb["expert_offsets"]),
-                                       P(vb["expert_counts"]), P(veo), stream),
-             [("expert", "expert_scale_kernel")]),
-            (L.moe_vsrc_regroup, (shp, 1, P(veo), P(vback_recv), *rg_tabs, *vws, stream),
-             [("dispatch_index", "regroup_plan_kernel"), ("regroup", "segcopy_kernel<regroup>")]),
-            (L.moe_vsrc_exchange, (shp, 1, P(vback_recv), P(vback_send), *ex_tabs, stream),
-             [("exchange", "segcopy_kernel<exchange>")]),
-            (L.moe_combine, (shp, P(vback_send), P(topk_w), P(vb["pos"]), P(y), stream),
-             [("combine", "combine_kernel")]),
-            (L.moe_stats, (P(vb["expert_counts"]), E, R, P(stats_raw), stream),
-             [("stats", "stats_kernel")]),
-        ]
-        if args.direct:  # one copy each way: send <-> grouped
-            dr_tabs = (P(vb["src_counts"]), P(vb["src_offsets"]), P(vb["expert_offsets"]))
-            calls[2:7] = [
-                (L.moe_vsrc_exchange_direct, (shp, 0, P(vb["send_buf"]), P(vb["grouped"]),
-                                              *dr_tabs, *vws, stream),
-                 [("dispatch_index", "regroup_plan_kernel"),
-                  ("exchange", "segcopy_kernel<direct>")]),
-                calls[4],  # the experts on the grouped rows
-                (L.moe_vsrc_exchange_direct, (shp, 1, P(veo), P(vback_send), *dr_tabs, *vws,
-                                              stream),
-                 [("dispatch_index", "regroup_plan_kernel"),
-                  ("exchange", "segcopy_kernel<direct>")]),
-            ]
-    STAGES_RUN = [st for st in STAGES if any(st == g for c in calls for g, _ in c[2])]
-    kernel_of = {st: "+".join(dict.fromkeys(kn for c in calls for g, kn in c[2] if g == st))
-                 for st in STAGES_RUN}
-    launches_of = {st: sum(1 for c in calls for g, _ in c[2] if g == st) for st in STAGES_RUN}
-
-    hipev = HipEvents()
-    set_events = L.moe_set_timing_events
-
-    NPAIR = 4  # event pairs per call (a call launches at most 2 kernels)
-
-    def step(evs=None):
-        """One pass of the path; evs[i] = (starts, stops) event arrays of call i."""
-        for i, (fn, a, kernels) in enumerate(calls):
-            if evs is not None:
-                set_events(evs[i][0], evs[i][1], NPAIR)
-            st = fn(*a)
-            if evs is not None:
-                n = L.moe_timed_launches()
-                set_events(None, None, 0)
-                if n != len(kernels):
-                    raise RuntimeError(f"call {i} launched {n} kernels, expected {len(kernels)}")
-            if st != 0:
-                raise RuntimeError(f"call {i}: {moe.status_string(st)}")
-
-    def new_events(n):
-        def arr():
-            return (ctypes.c_void_p * NPAIR)(*[hipev.create() for _ in range(NPAIR)])
-        return [[(arr(), arr()) for _ in calls] for _ in range(n)]
-
-    kernel_ms = {}
-
-    def stage_means(evs):
-        """Per stage: summed execution time of its kernels, averaged over steps
-        (and each kernel's mean time per launch into kernel_ms)."""
-        tot = {st: 0.0 for st in STAGES_RUN}
-        per, n = {}, {}
-        for e in evs:
-            for i, (_, _, kernels) in enumerate(calls):
-                for j, (st, kn) in enumerate(kernels):
-                    t = hipev.ms(e[i][0][j], e[i][1][j])
-                    tot[st] += t
-                    per[kn] = per.get(kn, 0.0) + t
-                    n[kn] = n.get(kn, 0) + 1
-        kernel_ms.clear()
-        kernel_ms.update({kn: per[kn] / n[kn] for kn in per})
-        return {st: v / len(evs) for st, v in tot.items()}
+        path = path_capacity(c, args)
+    elif args.vsrc:
+        path = path_vsrc(c, args)
+    else:
+        path = path_default(c, args)
+    run = StepRunner(c, path.calls)
+    T, K = wl.T, args.steps
 
     for _ in range(args.warmup):
-        step()
+        run.step()
     torch.cuda.synchronize()
 
     # ---- timed region 1: K plain steps -> value
-    K = args.steps
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
-        step()
+        run.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {K} timed steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
     # ---- timed region 2: K instrumented steps -> per-stage kernel times
-    evs = new_events(K)
+    evs = run.new_events(K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(evs[i])
+        run.step(evs[i])
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t0
-    stage_ms = stage_means(evs)
-    kernel_us = {kn: round(v * 1e3, 2) for kn, v in kernel_ms.items()}
-    nbytes = algorithmic_bytes(wl)
-    if cap is not None:
-        kept = int(cbuf["kept_counts"].sum().item())
-        nbytes = capacity_bytes(wl, cap, kept)
-    if args.vsrc:
-        nbytes = vsrc_bytes(wl, int(vb["expert_counts"].sum().item()))
+    stage_ms = run.stage_means(evs)
+    kernel_us = {kn: round(v * 1e3, 2) for kn, v in run.kernel_ms.items()}
+    nbytes = path.nbytes()
 
-    graph_wall = None
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        stream_c = ctypes.c_void_p(side.cuda_stream)
-        saved = list(calls)
-        for i, (fn, a, kn) in enumerate(calls):  # rebind the stream argument
-            calls[i] = (fn, tuple(stream_c if v is stream else v for v in a), kn)
-        with torch.cuda.stream(side):
-            step()
-            torch.cuda.current_stream().synchronize()
-            with torch.cuda.graph(g, stream=side):
-                step()
-        torch.cuda.synchronize()
-        calls[:] = saved
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_wall = time.perf_counter() - t0
-
-    # Plain device copy of 1 GiB (beyond the Infinity Cache) with the HIP
-    # runtime's own copy kernel: a reference streaming rate on this box.
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ca.record()
-    for _ in range(5):
-        dst.copy_(src)
-    cb.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
-    del src, dst
+    graph_wall = run.graph_wall(K) if args.graph else None
+    copy_gbs = plain_copy_gbs(torch, c.dev)
 
     cold_ms = None
     if not args.no_cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # the same instrumented step after evicting the 256 MB Infinity Cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=c.dev)
         Kc = max(5, min(K, 50))
-        cevs = new_events(Kc)
+        cevs = run.new_events(Kc)
         for i in range(Kc):
             flush.fill_(i & 0xFF)
-            step(cevs[i])
+            run.step(cevs[i])
         torch.cuda.synchronize()
-        cold_ms = stage_means(cevs)
+        cold_ms = run.stage_means(cevs)
         del flush
 
-    # Fitted symmetric Dirichlet alpha of this step's counts: a summary of S
-    # computed on demand (its own launch), timed apart from the step.
-    counts_t = (cbuf["kept_counts"] if cap is not None
-                else vb["expert_counts"] if args.vsrc else buf["expert_counts"])
-    alpha_t = torch.empty((1,), dtype=torch.float64, device=dev)
-    moe.dirichlet_alpha_device(counts_t, alpha_t)
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.record()
-    for _ in range(20):
-        moe.dirichlet_alpha_device(counts_t, alpha_t)
-    eb.record()
-    torch.cuda.synchronize()
-    alpha_fit = {"value": float(alpha_t.item()), "us": round(ea.elapsed_time(eb) * 1e3 / 20, 2),
-                 "kernel": "dirichlet_alpha_kernel", "in_step": False}
+    alpha_fit = dirichlet_fit(moe, torch, path.counts, c.dev)
+    stages, kernel_of, launches_of = run.stages, run.kernel_of, run.launches_of
 
     def gbs(name, ms):
         return nbytes[name] / (ms * 1e-3) / 1e9
 
-
     def stage_report(ms):
         rep = {}
-        for n in STAGES_RUN:
+        for n in stages:
             rep[n] = {"us": round(ms[n] * 1e3, 2), "GB/s": round(gbs(n, ms[n]), 1),
                       "frac_hbm_peak": round(gbs(n, ms[n]) / HBM_PEAK_GBS, 4),
                       "kernels": kernel_of[n]}
@@ -641,7 +717,7 @@ def main() -> int:
     # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
     single = [n for n in ("route", "dispatch_copy", "exchange", "regroup", "expert", "combine",
                           "stats")
-              if n in STAGES_RUN and not (swiglu and n == "expert")]
+              if n in stages and not (swiglu and n == "expert")]
     dom = max(single, key=lambda n: stage_ms[n])
     # per launch: a stage may launch its kernel more than once a step (the
     # exchange and the regroup run forward and back), bytes and time both scale
@@ -660,10 +736,8 @@ def main() -> int:
                     "traffic": stored_traffic(wl.name, "ffn_gemm_kernel<gate_up>+ffn_gemm_kernel<down>"),
                     "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
 
-    dc_keys = ("dispatch_index", "dispatch_copy", "combine")
-    if args.vsrc:
-        dc_keys = tuple(n for n in ("dispatch_index", "dispatch_copy", "exchange", "regroup",
-                                    "combine") if n in stage_ms)
+    dc_keys = tuple(n for n in ("dispatch_index", "dispatch_copy", "exchange", "regroup",
+                                "combine") if n in stage_ms)
     dc_ms = sum(stage_ms[n] for n in dc_keys)
     dc_bytes = sum(nbytes[n] for n in dc_keys)
     result = {
@@ -680,12 +754,11 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic (seeded logits and hidden states"
                 + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
-        "config": {"workload": wl.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
-                   "waves": W, "routing": wl.routing, "expert": wl.expert,
-                   "step": ("route+dispatch_index+stats (moe_route_index)" if not args.unfused
-                            else "route+dispatch_index+stats (separate calls)")
-                           + "+dispatch_copy+expert+combine",
-                   "kernels_per_step": sum(len(c[2]) for c in calls)},
+        "config": {"workload": wl.name, "T": T, "H": wl.H, "E": wl.E, "k": wl.k,
+                   "virtual_ranks": wl.R, "waves": wl.W, "routing": wl.routing,
+                   "expert": wl.expert, "step": path.desc,
+                   "kernels_per_step": sum(len(cl[2]) for cl in path.calls),
+                   **({"I": wl.I} if swiglu else {}), **path.config()},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
             "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
@@ -703,19 +776,6 @@ def main() -> int:
         "plain_copy_GBs": round(copy_gbs, 1),
         "dirichlet_alpha": alpha_fit,
     }
-    if swiglu:
-        result["config"]["I"] = wl.I
-    if cap is not None:
-        result["config"]["step"] = ("route+dispatch_capacity(count,place,copy,pad)"
-                                    "+expert+combine+stats")
-        result["config"].update(capacity_factor=args.capacity_factor, capacity=cap,
-                                kept_picks=kept, dropped_picks=T * k - kept)
-    if args.vsrc:
-        result["config"]["step"] = (
-            "route+vsrc_dispatch(count,place,plan,copy)+"
-            + ("direct exchange+expert+direct exchange back" if args.direct else
-               "exchange+regroup+expert+ungroup+exchange back")
-            + "+combine+stats")
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}
@@ -729,7 +789,7 @@ def main() -> int:
                                  "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9
                                                         / HBM_PEAK_GBS, 4)}}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, logits_np, x_np, args.cpu_seconds, ffn_np,
+        result["cpu_baseline"] = cpu_baseline(wl, c.logits_np, c.x_np, args.cpu_seconds, c.ffn_np,
                                               vsrc=args.vsrc)
     print(json.dumps(result), flush=True)
     return 0
