@@ -9,11 +9,11 @@
 //
 // Both are A[M_e x K] * B[N x K]^T with K contiguous in both operands, on
 // v_mfma_f32_32x32x16_bf16. Two tile shapes, one kernel template:
-//   large: 256 x 256 x 64 per 512-thread block, 8 waves as 2 x 4, each wave
-//          128 x 64 (4 x 2 MFMA tiles, 128 fp32 accumulators per lane), two
-//          waves per SIMD so one issues MFMAs while the other waits on LDS or
-//          the barrier (11% faster than 4 waves of 128 x 128). Needs
-//          I % 128 == 0 and H % 256 == 0.
+//   large: 256 x 256 x 64 per 1024-thread block, 16 waves as 4 x 4, each wave
+//          64 x 64 (2 x 2 MFMA tiles, 64 fp32 accumulators per lane), four
+//          waves per SIMD so some issue MFMAs while others wait on LDS or the
+//          barrier (one wave of 128 x 128 per SIMD measured 13% slower, two of
+//          128 x 64 2% slower). Needs I % 128 == 0 and H % 256 == 0.
 //   small: 128 x 128 x 64, 4 waves of 64 x 64 (2 x 2 tiles), two blocks per
 //          compute unit; any I % 64 == 0 and H % 128 == 0.
 // Global -> LDS moves go through buffer loads with the LDS bit (16 bytes a
@@ -42,7 +42,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWavesM = 2;  // waves along M in a block (WN along N)
 constexpr int kXCD = 8;
 // m-tiles per rasterisation patch: on the local layer 1 measured 701 us against
 // 714 for 4 (an even split of rows favours 4-16 by ~3%; the layer is skewed)
@@ -90,16 +89,16 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-// BM x BN block tile; each of the 2 x WN waves computes (BM/2) x (BN/WN) as
+// BM x BN block tile; each of the WM x WN waves computes (BM/WM) x (BN/WN) as
 // MI x NI tiles of 32 x 32. K steps of BK, NS LDS stages.
-template <bool kGateUp, int BM, int BN, int OCC, int BK, int NS, int WN>
-__global__ __launch_bounds__(kWave * kWavesM * WN, OCC) void ffn_gemm_kernel(
+template <bool kGateUp, int BM, int BN, int OCC, int BK, int NS, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN, OCC) void ffn_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ cnts, int E, int sg, int sstride, int sbase,
     const uint16_t* __restrict__ Bw, int64_t bstride,
     int I, int K, uint16_t* __restrict__ C, int64_t ldc, int ntiles, int gm) {
-  constexpr int NW = kWavesM * WN;           // waves in the block
-  constexpr int MI = BM / kWavesM / 32, NI = BN / WN / 32;  // 32x32 tiles per wave
+  constexpr int NW = WM * WN;                // waves in the block
+  constexpr int MI = BM / WM / 32, NI = BN / WN / 32;  // 32x32 tiles per wave
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
   constexpr int RPI = kWave / CPR;           // tile rows per load instruction (1 KiB)
   constexpr int AI = BM / NW / RPI, BI = BN / NW / RPI;  // load instructions per wave per K step
@@ -256,7 +255,7 @@ __global__ __launch_bounds__(kWave * kWavesM * WN, OCC) void ffn_gemm_kernel(
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
       fa[f][mi] = *reinterpret_cast<const bf16x8*>(
-          &As[swz<BK>(wm * (BM / 2) + mi * 32 + (lane & 31), kc)]);
+          &As[swz<BK>(wm * (BM / WM) + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
       fb[f][ni] =
@@ -349,7 +348,7 @@ __global__ __launch_bounds__(kWave * kWavesM * WN, OCC) void ffn_gemm_kernel(
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tr = wm * (BM / 2) + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int tr = wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (tr >= rows) continue;
       uint16_t* crow = C + (int64_t)(row0 + tr) * ldc;
       if constexpr (kGateUp) {
@@ -373,9 +372,9 @@ __global__ __launch_bounds__(kWave * kWavesM * WN, OCC) void ffn_gemm_kernel(
 // not uncovered load latency, bounds this kernel.
 constexpr int kLargeBK = 64;
 constexpr int kLargeNS = 2;
-constexpr int kLargeWN = 4;  // waves along N: 8 waves, two per SIMD
+constexpr int kLargeWM = 4, kLargeWN = 4;  // 4 x 4 waves, four per SIMD (2 x 4: 698 us, 4 x 2: 692, 4 x 4: 683)
 
-template <int BM, int BN, int OCC, int BK, int NS, int WN>
+template <int BM, int BN, int OCC, int BK, int NS, int WM, int WN>
 hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, int sstride,
                    int sbase, const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                    const void* w_down, void* hbuf, void* out, hipStream_t s) {
@@ -384,15 +383,15 @@ hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, 
     return (unsigned)(kXCD * ((mtb + kXCD - 1) / kXCD) * ntiles);
   };
   const int nt1 = I / (BN / 2);
-  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC, BK, NS, WN>, dim3(grid_of(nt1)),
-                          dim3(kWave * kWavesM * WN), 0, s,
+  hipError_t err = launch(ffn_gemm_kernel<true, BM, BN, OCC, BK, NS, WM, WN>, dim3(grid_of(nt1)),
+                          dim3(kWave * WM * WN), 0, s,
                           static_cast<const uint16_t*>(send), (int64_t)H, offs, cnts, E, sg,
                           sstride, sbase, static_cast<const uint16_t*>(w_gate_up), (int64_t)2 * I * H, I, H,
                           static_cast<uint16_t*>(hbuf), (int64_t)I, nt1, kGroupM);
   if (err != hipSuccess) return err;
   const int nt2 = H / BN;
-  return launch(ffn_gemm_kernel<false, BM, BN, OCC, BK, NS, WN>, dim3(grid_of(nt2)),
-                dim3(kWave * kWavesM * WN), 0, s,
+  return launch(ffn_gemm_kernel<false, BM, BN, OCC, BK, NS, WM, WN>, dim3(grid_of(nt2)),
+                dim3(kWave * WM * WN), 0, s,
                 static_cast<const uint16_t*>(hbuf), (int64_t)I, offs, cnts, E, sg, sstride,
                 sbase, static_cast<const uint16_t*>(w_down), (int64_t)H * I, I, I,
                 static_cast<uint16_t*>(out), (int64_t)H, nt2, kGroupM);
@@ -406,9 +405,9 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
                                        const void* w_down, void* hbuf, void* out, hipStream_t s) {
   if (rows == 0 || n == 0) return hipSuccess;
   if (I % 128 == 0 && H % 256 == 0)
-    return run_ffn<256, 256, 1, kLargeBK, kLargeNS, kLargeWN>(send, rows, H, I, n, sg, sstride, sbase, offs,
+    return run_ffn<256, 256, 1, kLargeBK, kLargeNS, kLargeWM, kLargeWN>(send, rows, H, I, n, sg, sstride, sbase, offs,
                                                     cnts, w_gate_up, w_down, hbuf, out, s);
-  return run_ffn<128, 128, 2, 64, 2, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts,
+  return run_ffn<128, 128, 2, 64, 2, 2, 2>(send, rows, H, I, n, sg, sstride, sbase, offs, cnts,
                                      w_gate_up, w_down, hbuf, out, s);
 }
 
