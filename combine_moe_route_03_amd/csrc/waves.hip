@@ -56,17 +56,25 @@ __global__ __launch_bounds__(kBlock) void gather_wave_kernel(
   }
 }
 
-// Events of the pipeline, created once per thread and reused by later calls
+// Events of the pipeline, created once per host thread and device (an event
+// belongs to the device current when it was created) and reused by later calls
 // (a wait takes the event's most recent record at the time it is enqueued).
+constexpr int kMaxDevices = 64;
+
 hipError_t wave_events(int n, std::vector<hipEvent_t>*& out) {
-  thread_local std::vector<hipEvent_t> pool;
-  while ((int)pool.size() < n) {
+  thread_local std::vector<hipEvent_t> pool[kMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::vector<hipEvent_t>& p = pool[dev];
+  while ((int)p.size() < n) {
     hipEvent_t e;
-    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
     if (err != hipSuccess) return err;
-    pool.push_back(e);
+    p.push_back(e);
   }
-  out = &pool;
+  out = &p;
   return hipSuccess;
 }
 

@@ -306,7 +306,8 @@ int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_o
  * compute_stream; when this call returns, compute_stream carries every wave's
  * FFN (follow with moe_combine there). copy_stream == compute_stream runs the
  * same launches serialised. The library keeps W+1 reusable events per host
- * thread (created on first use). Arguments as moe_expert_swiglu, plus x
+ * thread and device (created on first use, on the device current at the call,
+ * which must be the device of both streams). Arguments as moe_expert_swiglu, plus x
  * [T][H], row_token [T*k], wave_offsets [W+1] (DEVICE). 3W launches: W
  * gathers and 2W FFN kernels.
  * Errors: as moe_expert_swiglu; MOE_ERR_ARG also for null x / row_token /
