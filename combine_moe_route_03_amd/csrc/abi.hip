@@ -442,8 +442,8 @@ size_t moe_vsrc_workspace_bytes(const moe_shape* shape) {
 
 int moe_vsrc_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                       void* send_buf, int32_t* src_counts, int32_t* src_offsets,
-                      int32_t* send_counts,
-                      int32_t* send_offsets, int32_t* recv_counts, int32_t* recv_offsets,
+                      int32_t* send_counts, int32_t* send_offsets, int32_t* recv_counts,
+                      int32_t* recv_offsets,
                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
                       void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
   int st = check_vsrc_shape(shape);
