@@ -1,0 +1,109 @@
+"""The library's calls captured in one HIP graph (torch.cuda.graph on a side
+stream) and replayed: every replay must reproduce the eager results bit for
+bit. Replays are separated by eager work on other buffers and by
+synchronisations, and every output is overwritten with garbage before each
+replay, so a replay that skipped or repeated a node would show. No kernel of
+the library clears memory with a runtime memset, which is what graph replays
+can get wrong; this checks the whole step as captured."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_03_amd as moe
+import synth
+from test_gpu_parity import DEV, PARITY, dev, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(step, outputs, eager_noise):
+    """Eager reference, then capture, then three replays checked one by one."""
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outputs:
+            t.view(torch.uint8).fill_(0xA5)
+        eager_noise()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outputs, ref)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}, output {i}"
+
+
+def test_graph_replay_default_step():
+    wl = PARITY["zipf"]
+    print(f"[graph] zipf step: T={wl.T} H={wl.H} E={wl.E} k={wl.k}", flush=True)
+    shape = shape_of(wl)
+    logits, x = dev(synth.logits(wl)), dev(synth.hidden(wl))
+    out = moe.alloc_dispatch(shape, DEV)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=DEV)
+    raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=DEV)
+    eo = torch.empty_like(out["send_buf"])
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    # eager work between replays: the same path on a second set of buffers
+    out2 = moe.alloc_dispatch(shape, DEV)
+    idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
+
+    def step():
+        moe.route_index(logits, shape, out, idx, w, stats_out=raw)
+        moe.dispatch_copy(x, out["pos"], shape, out["send_buf"])
+        moe.expert_scale(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                         expert_out=eo)
+        moe.combine(eo, w, out["pos"], shape, y=y)
+
+    def noise():
+        moe.route_index(logits, shape, out2, idx2, w2)
+        moe.dispatch_copy(x, out2["pos"], shape, out2["send_buf"])
+
+    n = wl.T * wl.k
+    outputs = [idx, w, raw, out["expert_counts"], out["expert_offsets"], out["rank_counts"],
+               out["rank_offsets"], out["wave_offsets"], out["pos"], out["row_token"][:n],
+               out["send_buf"], eo, y]
+    _replays_match(step, outputs, noise)
+
+
+def test_graph_replay_capacity_and_direct_exchange():
+    wl = PARITY["zipf"]
+    print(f"[graph] capacity + direct exchange: T={wl.T} H={wl.H} E={wl.E}", flush=True)
+    shape = shape_of(wl)
+    logits, x = dev(synth.logits(wl)), dev(synth.hidden(wl))
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=DEV)
+    cap = moe.expert_capacity(wl.k, 1.0, wl.T, wl.E)
+    cb = moe.alloc_dispatch_capacity(shape, cap, DEV)
+    vb = moe.alloc_vsrc(shape, DEV)
+    shape1 = shape_of(wl.with_(W=1))
+    veo = torch.empty_like(vb["send_buf"])
+    back = torch.empty_like(vb["send_buf"])
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        moe.route(logits, wl.k, topk_idx=idx, topk_w=w)
+        moe.dispatch_capacity(x, idx, wl.E, wl.R, wl.W, cap, out=cb)
+        moe.vsrc_dispatch(x, idx, shape, vb)
+        moe.vsrc_exchange_direct(vb["send_buf"], vb["grouped"], shape, vb, 0)
+        moe.expert_scale_rows(vb["grouped"], vb["expert_offsets"], vb["expert_counts"], shape1,
+                              expert_out=veo)
+        moe.vsrc_exchange_direct(veo, back, shape, vb, 1)
+        moe.combine_rows(back, w, vb["pos"], shape, y=y)
+
+    def noise():
+        moe.route(logits, wl.k)
+
+    n = int(np.prod(idx.shape))
+    outputs = [idx, w, cb["kept_counts"], cb["pos"], cb["row_token"], cb["send_buf"],
+               vb["src_counts"], vb["src_offsets"], vb["send_counts"], vb["recv_offsets"],
+               vb["expert_offsets"], vb["pos"], vb["send_buf"][:n], vb["grouped"][:n], y]
+    _replays_match(step, outputs, noise)
