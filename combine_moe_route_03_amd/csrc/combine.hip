@@ -3,14 +3,17 @@
 // flow step 4: restore the original order, weight by the gate confidence).
 //
 // Flat over (token, 16-byte column): each thread gathers its column from the k
-// expert rows of its token (all k loads issued before any arithmetic; each
-// expert row is read exactly once; through the caches when the expert rows fit
-// the cache-reuse budget, as the expert stage has just written them there,
-// streaming otherwise), runs the
+// expert rows of its token (each expert row is read exactly once; through the
+// caches when the expert rows fit the cache-reuse budget, as the expert stage
+// has just written them there, streaming otherwise), runs the
 // fp32 fused multiply-add chain in pick order (seeded with -0, the additive
 // identity, so an all -0 sum stays -0), rounds once to the output dtype
 // and writes one 16-byte vector. Lanes of a wave cover consecutive columns of
-// one row, so every gather and the store are contiguous 1 KiB segments.
+// one row, so every gather and the store are contiguous 1 KiB segments; with
+// rows a multiple of 64 vectors (kUniform) the wave's token is uniform and its
+// k positions and weights can come through the scalar cache.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -18,8 +21,16 @@ namespace moe {
 namespace {
 
 constexpr int kBlock = 256;
+// Cached rows: positions through the scalar cache (rows of 64k vectors) and
+// all k gathers in flight. Streamed rows: one gather in flight per thread and
+// positions through the vector path; on k = 8 over 14 KiB rows that measured
+// 351 us against 357 (scalar positions) and 365-368 (all eight in flight),
+// and on k = 2 the same or better.
+constexpr bool kCombineUniform = true;
+constexpr bool kStreamUniform = false;
+constexpr int kStreamGroup = 1;  // gathers in flight per thread on streamed rows
 
-template <int KMAX, bool kBF16, bool kCacheIn>
+template <int KMAX, bool kBF16, bool kCacheIn, bool kUniform>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__ eo,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ pos, int k,
@@ -27,56 +38,63 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__
                                                          uint32_t nrows, v4u* __restrict__ y) {
   const uint32_t q = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
   if (q >= total) return;
-  const uint32_t t = q / nvec, col = q - t * nvec;
+  if (nrows == 0) {  // no expert rows: every output is the empty sum, -0
+    store_stream(y + q, kBF16 ? v4u{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                              : v4u{0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u});
+    return;
+  }
+  uint32_t t = q / nvec;
+  if constexpr (kUniform) t = __builtin_amdgcn_readfirstlane(t);  // whole waves: total % 64 == 0
+  const uint32_t col = q - t * nvec;
   const int32_t* pp = pos + (size_t)t * k;
   const float* ww = w + (size_t)t * k;
 
-  v4u v[KMAX];
+  // every position and weight first (one wait), then the gathers in groups of
+  // kGroup, each group issued back to back and then accumulated (pick order is
+  // kept). A pick without a row loads row 0 (discarded) instead of branching
+  // around the load, so no gather result has to land before the next issue.
+  int32_t P[KMAX];
   float wt[KMAX];
-  bool ok[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    ok[i] = false;
-    wt[i] = 0.f;
-    v[i] = v4u{0u, 0u, 0u, 0u};
-    if (i < k) {
-      const int32_t P = pp[i];
-      wt[i] = ww[i];
-      ok[i] = (uint32_t)P < nrows;
-      if (ok[i]) {
-        const v4u* src = eo + (size_t)P * nvec + col;
-        v[i] = kCacheIn ? *src : load_stream(src);
+    P[i] = (i < k) ? pp[i] : -1;
+    wt[i] = (i < k) ? ww[i] : 0.f;
+  }
+  constexpr int kGroup = kCacheIn ? KMAX : kStreamGroup;
+  constexpr int G = kGroup < KMAX ? kGroup : KMAX;
+  float a[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};  // -0: additive identity
+#pragma unroll
+  for (int g0 = 0; g0 < KMAX; g0 += G) {
+    v4u v[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int i = g0 + j;
+      if (i < k) {
+        const bool ok = (uint32_t)P[i] < nrows;
+        const v4u* src = eo + (ok ? (size_t)P[i] * nvec : 0) + col;
+        v[j] = kCacheIn ? *src : load_stream(src);
       }
     }
-  }
-
-  v4u out;
-  if constexpr (kBF16) {
-    float a[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};  // -0: additive identity
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if (i < k && ok[i]) {
+    for (int j = 0; j < G; ++j) {
+      const int i = g0 + j;
+      if (i < k && (uint32_t)P[i] < nrows) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[2 * j] = fmaf(wt[i], bf16_lo(v[i][j]), a[2 * j]);
-          a[2 * j + 1] = fmaf(wt[i], bf16_hi(v[i][j]), a[2 * j + 1]);
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (kBF16) {
+            a[2 * c] = fmaf(wt[i], bf16_lo(v[j][c]), a[2 * c]);
+            a[2 * c + 1] = fmaf(wt[i], bf16_hi(v[j][c]), a[2 * c + 1]);
+          } else {
+            a[c] = fmaf(wt[i], __uint_as_float(v[j][c]), a[c]);
+          }
         }
       }
     }
-    out = v4u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
-              pack_bf16x2(a[6], a[7])};
-  } else {
-    float a[4] = {-0.f, -0.f, -0.f, -0.f};
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if (i < k && ok[i]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = fmaf(wt[i], __uint_as_float(v[i][j]), a[j]);
-      }
-    }
-    out = v4u{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
-              __float_as_uint(a[3])};
   }
+  const v4u out = kBF16 ? v4u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                              pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])}
+                        : v4u{__float_as_uint(a[0]), __float_as_uint(a[1]),
+                              __float_as_uint(a[2]), __float_as_uint(a[3])};
   store_stream(y + q, out);
 }
 
@@ -88,11 +106,18 @@ hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int
   v4u* out = static_cast<v4u*>(y);
   // the expert rows (nrows x nvec vectors) decide the policy, as in the expert stage
   const bool cache = (int64_t)nrows * nvec * 16 <= kCacheReuseBytes;
+  const bool uniform = kCombineUniform && nvec % kWave == 0 && (cache || kStreamUniform);
   auto run = [&](auto kernel) {
     return launch(kernel, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec, total, nrows, out);
   };
-  if (bf16) return cache ? run(combine_kernel<KMAX, true, true>) : run(combine_kernel<KMAX, true, false>);
-  return cache ? run(combine_kernel<KMAX, false, true>) : run(combine_kernel<KMAX, false, false>);
+  auto pick = [&](auto bf, auto ca) {
+    constexpr bool B = decltype(bf)::value, C = decltype(ca)::value;
+    return uniform ? run(combine_kernel<KMAX, B, C, true>) : run(combine_kernel<KMAX, B, C, false>);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (bf16) return cache ? pick(T_{}, T_{}) : pick(T_{}, F_{});
+  return cache ? pick(F_{}, T_{}) : pick(F_{}, F_{});
 }
 
 }  // namespace
