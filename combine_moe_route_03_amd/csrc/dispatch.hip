@@ -228,8 +228,9 @@ __global__ __launch_bounds__(kCopyBlock) void copy_kernel(const v4u* __restrict_
   }
 }
 
-// Zero padding of the capacity layout: block j fills bucket j's rows past the
-// kept ones with zero vectors and marks them row_token = -1.
+// Zero padding of the capacity layout: the gridDim.y blocks of column j fill
+// bucket j's rows past the kept ones with zero vectors (interleaved by block)
+// and mark them row_token = -1.
 __global__ __launch_bounds__(kCopyBlock) void pad_kernel(int E, int R, int W, int cap,
                                                          const int32_t* __restrict__ kept,
                                                          uint32_t nvec, v4u* __restrict__ send,
@@ -237,10 +238,11 @@ __global__ __launch_bounds__(kCopyBlock) void pad_kernel(int E, int R, int W, in
   const int j = blockIdx.x, L = E / R, LW = L / W;
   const int e = bucket_expert(j, R, L, LW);
   const int64_t r0 = (int64_t)j * cap + kept[e], r1 = (int64_t)(j + 1) * cap;
-  for (int64_t r = r0 + threadIdx.x; r < r1; r += kCopyBlock) row_token[r] = -1;
+  const int64_t first = (int64_t)blockIdx.y * kCopyBlock + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.y * kCopyBlock;
+  for (int64_t r = r0 + first; r < r1; r += step) row_token[r] = -1;
   const int64_t n = (r1 - r0) * nvec;
-  for (int64_t q = threadIdx.x; q < n; q += kCopyBlock)
-    send[r0 * nvec + q] = v4u{0u, 0u, 0u, 0u};
+  for (int64_t q = first; q < n; q += step) send[r0 * nvec + q] = v4u{0u, 0u, 0u, 0u};
 }
 
 int ilog2_ceil(int v) {
@@ -314,8 +316,15 @@ hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t 
 hipError_t launch_pad(int E, int R, int W, int cap, const int32_t* kept, int64_t row_bytes,
                       void* send, int32_t* row_token, hipStream_t s) {
   if (cap == 0) return hipSuccess;
-  return launch(pad_kernel, dim3((unsigned)E), dim3(kCopyBlock), 0, s, E, R, W, cap, kept,
-                (uint32_t)(row_bytes / 16), static_cast<v4u*>(send), row_token);
+  // enough blocks per bucket for ~4096 in all (a bucket's padding is at most
+  // cap rows), so that the fill is not limited to E blocks
+  const int64_t vecs = (int64_t)cap * (row_bytes / 16);
+  int64_t per = (vecs + kCopyBlock - 1) / kCopyBlock;
+  const int64_t want = (4096 + E - 1) / E;
+  if (per > want) per = want;
+  if (per < 1) per = 1;
+  return launch(pad_kernel, dim3((unsigned)E, (unsigned)per), dim3(kCopyBlock), 0, s, E, R, W,
+                cap, kept, (uint32_t)(row_bytes / 16), static_cast<v4u*>(send), row_token);
 }
 
 // Source shards: nsrc shards of src_picks picks, spc chunks each (spc >= 1).
