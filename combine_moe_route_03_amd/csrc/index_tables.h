@@ -16,6 +16,20 @@ namespace moe {
 constexpr int kIndexWaves = kIndexBlock / kWave;
 constexpr int kIndexMaxE = 1024;
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP (the whole wave must
+// be active): row_shr 1, 2, 4, 8 inside each row of 16 lanes (lanes shifted in
+// from outside the row read 0), then row_bcast 15 (last lane of rows 0 and 2
+// into rows 1 and 3) and row_bcast 31 (lane 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
 // Exclusive scan of the bucket sizes in (wave, rank, slot) order: off[e] = first
 // row of expert e's bucket (relative); returns the total. Sizes are cnt[e], or
 // cap for every bucket when cap >= 0. Called by every thread of the block;
@@ -25,11 +39,7 @@ __device__ __forceinline__ int bucket_scan(const int32_t* cnt, int E, int R, int
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int L = E / R, LW = L / W;
   const int cj = (tid < E) ? (cap >= 0 ? cap : cnt[bucket_expert(tid, R, L, LW)]) : 0;
-  int incl = cj;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(cj);  // DPP: no LDS round trips (local layer index 8.6 vs 8.9 us)
   if (lane == kWave - 1) part[wid] = incl;
   __syncthreads();
   int excl = incl - cj, total = 0;
