@@ -165,6 +165,12 @@ EDGES = {
     "f32_row16B": _edge(64, 4, 16, 4, 4, 1, dtype="f32"),
     "many_chunks": _edge(70000, 8, 16, 1, 2, 1),
     "wide_chunks": _edge(300000, 8, 16, 4, 4, 2),
+    # the copy's two-vectors-a-thread launch (one-to-two rounds of blocks), rows
+    # of 6 vectors (per-lane positions) and of 64 (wave-uniform), ragged tails
+    "copy_two_rows6": _edge(90001, 48, 16, 3, 4, 1),
+    "copy_two_rows64": _edge(9001, 512, 32, 4, 4, 2),
+    # expert rows beyond the cache-reuse budget: the streamed combine, ragged
+    "combine_streamed": _edge(70001, 1024, 16, 1, 4, 1),
 }
 
 
