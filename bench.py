@@ -340,10 +340,15 @@ def path_default(c, args):
         ws = c.torch.empty((moe.expert_swiglu_workspace_bytes(c.shape, c.wl.I),),
                            dtype=c.torch.uint8, device=c.dev)
         c.keep = (gu, dn, ws)
-        expert = (L.moe_expert_swiglu, (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]),
-                                        P(buf["expert_counts"]), P(gu), P(dn), P(expert_out),
-                                        P(ws), ws.numel(), s),
-                  [("expert", "ffn_gemm_kernel<gate_up>"), ("expert", "ffn_gemm_kernel<down>")])
+        a = (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
+             P(gu), P(dn), P(expert_out), P(ws), ws.numel(), s)
+        # two GEMMs, each with its tail launch (the last partial round as
+        # half-width tiles) where the tile shape has one
+        names = (["ffn_gemm_kernel<gate_up>", "ffn_gemm_kernel<gate_up,tail>",
+                  "ffn_gemm_kernel<down>", "ffn_gemm_kernel<down,tail>"]
+                 if launches_of(c, L.moe_expert_swiglu, a) == 4 else
+                 ["ffn_gemm_kernel<gate_up>", "ffn_gemm_kernel<down>"])
+        expert = (L.moe_expert_swiglu, a, [("expert", n) for n in names])
     else:
         expert = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
                                        P(buf["expert_counts"]), P(expert_out), s),
@@ -376,6 +381,22 @@ def path_default(c, args):
                       [("stats", "stats_kernel")]))
     return SimpleNamespace(calls=calls, nbytes=lambda: algorithmic_bytes(c.wl),
                            counts=buf["expert_counts"], desc=desc, config=lambda: {})
+
+
+def launches_of(c, fn, a) -> int:
+    """Kernels one call launches (counted by the library's timing hook)."""
+    hipev = HipEvents()
+    n = StepRunner.NPAIR
+    starts = (ctypes.c_void_p * n)(*[hipev.create() for _ in range(n)])
+    stops = (ctypes.c_void_p * n)(*[hipev.create() for _ in range(n)])
+    c.L.moe_set_timing_events(starts, stops, n)
+    st = fn(*a)
+    got = c.L.moe_timed_launches()
+    c.L.moe_set_timing_events(None, None, 0)
+    if st != 0:
+        raise RuntimeError(c.moe.status_string(st))
+    c.torch.cuda.synchronize()
+    return got
 
 
 def path_capacity(c, args):
@@ -530,15 +551,27 @@ class StepRunner:
         (and each kernel's mean time per launch into kernel_ms)."""
         tot = {st: 0.0 for st in self.stages}
         per, n = {}, {}
+        self.step_stage_ms = []  # per step: stage -> ms
         for e in evs:
+            one = {st: 0.0 for st in self.stages}
             for i, (_, _, kernels) in enumerate(self.calls):
                 for j, (st, kn) in enumerate(kernels):
                     t = self.hipev.ms(e[i][0][j], e[i][1][j])
                     tot[st] += t
+                    one[st] += t
                     per[kn] = per.get(kn, 0.0) + t
                     n[kn] = n.get(kn, 0) + 1
+            self.step_stage_ms.append(one)
         self.kernel_ms = {kn: per[kn] / n[kn] for kn in per}
         return {st: v / len(evs) for st, v in tot.items()}
+
+    @staticmethod
+    def median_of(steps, keys) -> float:
+        """Median over `steps` (per-step stage -> ms, as stage_means leaves in
+        step_stage_ms) of the summed time of `keys` (ms)."""
+        v = sorted(sum(one[k] for k in keys) for one in steps)
+        m = len(v) // 2
+        return v[m] if len(v) % 2 else 0.5 * (v[m - 1] + v[m])
 
     def graph_wall(self, K):
         """K replays of the step captured in one HIP graph on a side stream."""
@@ -677,6 +710,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t0
     stage_ms = run.stage_means(evs)
+    warm_steps = list(run.step_stage_ms)
     kernel_us = {kn: round(v * 1e3, 2) for kn, v in run.kernel_ms.items()}
     nbytes = path.nbytes()
 
@@ -694,6 +728,7 @@ def main() -> int:
             run.step(cevs[i])
         torch.cuda.synchronize()
         cold_ms = run.stage_means(cevs)
+        cold_steps = list(run.step_stage_ms)
         del flush
 
     alpha_fit = dirichlet_fit(moe, torch, path.counts, c.dev)
@@ -733,7 +768,7 @@ def main() -> int:
         roofline = {"bound": "mfma", "kernel": kernel_of["expert"], "achieved": round(tf, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": stored_traffic(wl.name, "ffn_gemm_kernel<gate_up>+ffn_gemm_kernel<down>"),
+                    "traffic": stored_traffic(wl.name, kernel_of["expert"]),
                     "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
 
     dc_keys = tuple(n for n in ("dispatch_index", "dispatch_copy", "exchange", "regroup",
@@ -761,6 +796,7 @@ def main() -> int:
                    **({"I": wl.I} if swiglu else {}), **path.config()},
         "dispatch_combine": {
             "us": round(dc_ms * 1e3, 2),
+            "median_us": round(StepRunner.median_of(warm_steps, dc_keys) * 1e3, 2),
             "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
             "GB/s": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -784,6 +820,8 @@ def main() -> int:
         result["cold_cache"] = {
             "stages": stage_report(cold_ms),
             "dispatch_combine": {"us": round(cdc * 1e3, 2),
+                                 "median_us": round(StepRunner.median_of(cold_steps, dc_keys) * 1e3,
+                                                    2),
                                  "tokens_per_s": round(T / (cdc * 1e-3), 1),
                                  "GB/s": round(dc_bytes / (cdc * 1e-3) / 1e9, 1),
                                  "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9
