@@ -47,3 +47,13 @@ def test_stored_traffic_record_and_guard(tmp_path, monkeypatch):
 def test_byte_model_positive(name):
     b = bench.algorithmic_bytes(synth.WORKLOADS[name])
     assert all(v > 0 for v in b.values())
+
+
+def test_median_of_steps():
+    import bench
+    steps = [{"a": 1.0, "b": 2.0}, {"a": 5.0, "b": 0.0}, {"a": 2.0, "b": 2.0}]
+    # per-step sums of a + b: 3, 5, 4 -> median 4
+    assert bench.StepRunner.median_of(steps, ("a", "b")) == 4.0
+    # even count: mean of the middle two (a alone: 1, 2, 5, 7 -> 3.5)
+    steps.append({"a": 7.0, "b": 0.0})
+    assert bench.StepRunner.median_of(steps, ("a",)) == 3.5
