@@ -50,7 +50,6 @@ def test_byte_model_positive(name):
 
 
 def test_median_of_steps():
-    import bench
     steps = [{"a": 1.0, "b": 2.0}, {"a": 5.0, "b": 0.0}, {"a": 2.0, "b": 2.0}]
     # per-step sums of a + b: 3, 5, 4 -> median 4
     assert bench.StepRunner.median_of(steps, ("a", "b")) == 4.0
