@@ -39,6 +39,8 @@ namespace {
 constexpr int kB = kIndexBlock;  // 1024 threads, 16 waves
 constexpr int kWaves = kIndexWaves;
 constexpr int kMaxE = kIndexMaxE;
+// placing blocks resident at once: one per compute unit (1024 threads, ~86 KiB LDS)
+constexpr int kPlaceResident = 256;
 
 // Picks [p0, p1) of block b: chunk b - src*spc of shard src.
 __device__ __forceinline__ void chunk_range(int b, int spc, int nsrc, int64_t chunk,
@@ -166,7 +168,11 @@ __global__ __launch_bounds__(kB) void place_kernel(
     cnt[tid] = A;
   }
   __syncthreads();
-  if (b == sblock) {  // the statistics block (only launched when stats is non-null)
+  // The statistics: an extra block past the placing ones computes them and
+  // leaves, or (when the placing blocks already fill the chip) placing block
+  // sblock computes them after its own placement.
+  const bool stats_here = stats != nullptr && b == sblock;
+  if (stats_here && sblock >= nsrc * spc) {
     block_stats(cnt, E, R, *reinterpret_cast<StatsScratch*>(&wcnt[0][0]), stats);
     return;
   }
@@ -199,6 +205,10 @@ __global__ __launch_bounds__(kB) void place_kernel(
     } else if (p < p1) {
       pos[p] = -1;
     }
+  }
+  if (stats_here) {
+    __syncthreads();  // wcnt, the statistics scratch, is free again
+    block_stats(cnt, E, R, *reinterpret_cast<StatsScratch*>(&wcnt[0][0]), stats);
   }
 }
 
@@ -281,10 +291,16 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
                                int32_t* expert_offsets, int32_t* rank_counts,
                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
                                int32_t* row_token, moe_stats_t* stats, int cap, hipStream_t s) {
-  // With no picks one block still runs to publish zero counts and offsets; the
-  // statistics block, if any, comes after the placing blocks.
-  const int sblock = nb == 0 ? 1 : nb;
-  const unsigned grid = (unsigned)sblock + (stats != nullptr ? 1u : 0u);
+  // With no picks one block still runs to publish zero counts and offsets. The
+  // statistics come from one extra block after the placing blocks, unless
+  // those already take every compute unit (one 1024-thread block each): the
+  // extra block would then wait for a second round (dirichlet_waves, 256
+  // chunks: 26.5 us against 13.6 without statistics), so placing block 0
+  // computes them after its placement.
+  const int nplace = nb == 0 ? 1 : nb;
+  const bool in_place = stats != nullptr && nplace >= kPlaceResident;
+  const int sblock = in_place ? 0 : nplace;
+  const unsigned grid = (unsigned)nplace + (stats != nullptr && !in_place ? 1u : 0u);
   return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, 1, nb, npicks, chunk, k,
                 E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
                 rank_offsets, wave_offsets, pos, row_token, stats, sblock, cap);

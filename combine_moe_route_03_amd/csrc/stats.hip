@@ -20,8 +20,10 @@ __global__ __launch_bounds__(1024) void stats_kernel(const int32_t* __restrict__
 }  // namespace
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s) {
-  // One thread per expert (rounded to whole waves): E <= 1024.
-  const int threads = (E + kWave - 1) / kWave * kWave;
+  // One thread per expert, rounded up to a power of two and to whole waves
+  // (the sorted pair sums hold one element a thread): E <= 1024.
+  int threads = kWave;
+  while (threads < E) threads <<= 1;
   return launch(stats_kernel, dim3(1), dim3(threads), 0, s, counts, E, R,
                 static_cast<moe_stats_t*>(out));
 }
