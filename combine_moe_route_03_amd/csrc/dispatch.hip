@@ -295,11 +295,12 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
   // statistics come from one extra block after the placing blocks, unless
   // those already take every compute unit (one 1024-thread block each): the
   // extra block would then wait for a second round (dirichlet_waves, 256
-  // chunks: 26.5 us against 13.6 without statistics), so placing block 0
-  // computes them after its placement.
+  // chunks: 26.5 us against 13.6 without statistics), so the last placing
+  // block computes them after its placement (19.1 us; block 0, which also
+  // publishes the tables, 20.4).
   const int nplace = nb == 0 ? 1 : nb;
   const bool in_place = stats != nullptr && nplace >= kPlaceResident;
-  const int sblock = in_place ? 0 : nplace;
+  const int sblock = in_place ? nplace - 1 : nplace;
   const unsigned grid = (unsigned)nplace + (stats != nullptr && !in_place ? 1u : 0u);
   return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, 1, nb, npicks, chunk, k,
                 E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
