@@ -107,3 +107,40 @@ def test_graph_replay_capacity_and_direct_exchange():
                vb["src_counts"], vb["src_offsets"], vb["send_counts"], vb["recv_offsets"],
                vb["expert_offsets"], vb["pos"], vb["send_buf"][:n], vb["grouped"][:n], y]
     _replays_match(step, outputs, noise)
+
+
+def test_graph_replay_exchange_and_regroup():
+    """The emulated exchange the long way: all-to-all, regroup, experts,
+    ungroup, reverse all-to-all, combine (segment copies storing through the
+    caches)."""
+    wl = PARITY["zipf"]
+    print(f"[graph] exchange + regroup: T={wl.T} H={wl.H} E={wl.E} R={wl.R}", flush=True)
+    shape = shape_of(wl)
+    logits, x = dev(synth.logits(wl)), dev(synth.hidden(wl))
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=DEV)
+    vb = moe.alloc_vsrc(shape, DEV)
+    shape1 = shape_of(wl.with_(W=1))
+    veo = torch.empty_like(vb["send_buf"])
+    ung = torch.empty_like(vb["send_buf"])
+    back = torch.empty_like(vb["send_buf"])
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        moe.route(logits, wl.k, topk_idx=idx, topk_w=w)
+        moe.vsrc_dispatch(x, idx, shape, vb)
+        moe.vsrc_exchange(vb["send_buf"], vb["recv_buf"], shape, vb, 0)
+        moe.vsrc_regroup(vb["recv_buf"], vb["grouped"], shape, vb, 0)
+        moe.expert_scale_rows(vb["grouped"], vb["expert_offsets"], vb["expert_counts"], shape1,
+                              expert_out=veo)
+        moe.vsrc_regroup(veo, ung, shape, vb, 1)
+        moe.vsrc_exchange(ung, back, shape, vb, 1)
+        moe.combine_rows(back, w, vb["pos"], shape, y=y)
+
+    def noise():
+        moe.route(logits, wl.k)
+
+    n = int(np.prod(idx.shape))
+    outputs = [idx, w, vb["recv_counts"], vb["recv_offsets"], vb["send_buf"][:n],
+               vb["recv_buf"][:n], vb["grouped"][:n], veo[:n], back[:n], y]
+    _replays_match(step, outputs, noise)
