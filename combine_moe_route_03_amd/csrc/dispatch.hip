@@ -5,7 +5,7 @@
 // products by count + scan + index (MoE systems survey section 4.1) and places
 // same-expert rows contiguously (survey section 1.1, EP flow step 2).
 //
-// Three kernels, all on the caller's stream:
+// Four kernels, all on the caller's stream:
 //   count_kernel  one 1024-thread block per chunk of picks: LDS histogram ->
 //                 hist[chunk][E] (LDS integer atomics: order-free, exact).
 //   place_kernel  one 1024-thread block per chunk. Each block re-derives what it
@@ -18,8 +18,11 @@
 //                 match on the expert id, popcount of lower lanes) and an LDS
 //                 prefix across the block's 16 waves; the next batch of ids is
 //                 prefetched while the current one is placed.
+//                 The optional statistics come from one extra block, or from
+//                 the last placing block when the placing blocks fill the chip.
 //   copy_kernel   flat over (token, 16-byte column): one streaming load of x,
-//                 k stores.
+//                 k stores; a wave's k positions through the scalar cache.
+//   pad_kernel    capacity layout: zero rows past each bucket's kept picks.
 //
 // Source shards: count and place also run over nsrc equal shards of the picks
 // at once (the virtual source ranks of the emulated exchange). Shard s owns
