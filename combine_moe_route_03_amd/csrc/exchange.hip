@@ -28,7 +28,9 @@
 //                        8192 segments), the segments in between go to LDS,
 //                        and each thread walks them while it moves 4 vectors
 //                        at a time (all loads before the stores). Forward
-//                        writes the key side, back reads it.
+//                        writes the key side, back reads it. Loads stream;
+//                        stores go through the caches when the output fits
+//                        the cache-reuse budget (the next stage reads it).
 #include "device.h"
 #include "launch.h"
 
