@@ -160,38 +160,31 @@ __global__ __launch_bounds__(kB) void place_kernel(
     }
   }
   __syncthreads();
-  if (tid < E) {
-    const int nrow = ep < kWave ? kWaves : nslice;  // partial rows
-    int P = 0, A = 0;
-    for (int s = 0; s < nrow; ++s) {
-      P += ppre[s * ep + tid];
-      A += pall[s * ep + tid];
-    }
-    run[tid] = P;
-    cnt[tid] = A;
-  }
-  __syncthreads();
+  const int nrow = ep < kWave ? kWaves : nslice;  // partial rows
   // The statistics: an extra block past the placing ones computes them and
   // leaves, or (when the placing blocks already fill the chip) placing block
   // sblock computes them after its own placement.
   const bool stats_here = stats != nullptr && b == sblock;
   if (stats_here && sblock >= nsrc * spc) {
+    if (tid < E) {
+      int A = 0;
+      for (int s = 0; s < nrow; ++s) A += pall[s * ep + tid];
+      cnt[tid] = A;
+    }
+    __syncthreads();
     block_stats(cnt, E, R, *reinterpret_cast<StatsScratch*>(&wcnt[0][0]), stats);
     return;
   }
 
-  // 2. Bucket offsets in (wave, rank, slot) order; with a capacity every
-  //    bucket is cap rows long. The shard's first block publishes its counts
-  //    and offsets.
-  const int total = bucket_scan(cnt, E, R, W, cap, off, part);
+  // 2. Totals, bucket offsets in (wave, rank, slot) order (with a capacity
+  //    every bucket is cap rows long) and this block's first free row of each
+  //    bucket, one bucket per thread. The shard's first block publishes its
+  //    counts and offsets.
+  const int total = bucket_scan(ppre, pall, nrow, ep, E, R, W, cap, base, cnt, off, run, part);
   if (b == h0)
     publish_index(cnt, off, total, E, R, W, cap, base, expert_counts + (int64_t)src * E,
                   expert_offsets + (int64_t)src * E, rank_counts + (int64_t)src * W * R,
                   rank_offsets + (int64_t)src * W * R, wave_offsets + (int64_t)src * (W + 1));
-  // run[e]: picks of expert e before this chunk; with a capacity the rank
-  // inside the bucket decides between a row and a drop, so it stays relative.
-  if (tid < E && cap < 0) run[tid] += (int32_t)base + off[tid];
-  __syncthreads();
 
   // 3. Stable ranks inside the chunk, 1024 picks per batch.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
@@ -200,7 +193,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
     const int e = e_next;
     e_next = (p + kB < p1) ? idx[p + kB] : -1;  // prefetch the next batch
     const bool valid = (p < p1) && ((unsigned)e < (unsigned)E);
-    const int rel = batch_rank(e, valid, nbits, wcnt, run);
+    const int rel = batch_rank(e, valid, nbits, wcnt, run, base_p + kB >= p1);
     if (valid) {
       const int P = cap < 0 ? rel : (rel < cap ? off[e] + rel : -1);
       pos[p] = P;

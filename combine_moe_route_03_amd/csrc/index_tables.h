@@ -30,15 +30,31 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Exclusive scan of the bucket sizes in (wave, rank, slot) order: off[e] = first
-// row of expert e's bucket (relative); returns the total. Sizes are cnt[e], or
-// cap for every bucket when cap >= 0. Called by every thread of the block;
-// part holds kIndexWaves ints of LDS. Ends with a barrier.
-__device__ __forceinline__ int bucket_scan(const int32_t* cnt, int E, int R, int W, int cap,
-                                           int32_t* off, int32_t* part) {
+// Thread j < E owns bucket j of the (wave, rank, slot) order and its expert
+// e = bucket_expert(j). It sums e's nrow partial rows (row stride ep) of the
+// picks before this block (ppre) and of all picks (pall); the bucket sizes
+// (that total, or cap for every bucket when cap >= 0) are scanned in bucket
+// order, and the thread writes cnt[e] (total), off[e] (first row of the
+// bucket, relative) and run[e] (next free row: picks before this block, plus
+// base + off[e] without a capacity; with one the rank inside the bucket
+// decides between a row and a drop, so it stays relative). Returns the total.
+// Called by every thread of the block; part holds kIndexWaves ints of LDS.
+// Two barriers, the last at the end.
+__device__ __forceinline__ int bucket_scan(const int32_t* ppre, const int32_t* pall, int nrow,
+                                           int ep, int E, int R, int W, int cap, int64_t base,
+                                           int32_t* cnt, int32_t* off, int32_t* run,
+                                           int32_t* part) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int L = E / R, LW = L / W;
-  const int cj = (tid < E) ? (cap >= 0 ? cap : cnt[bucket_expert(tid, R, L, LW)]) : 0;
+  const int e = (tid < E) ? bucket_expert(tid, R, L, LW) : 0;
+  int P = 0, A = 0;
+  if (tid < E) {
+    for (int s = 0; s < nrow; ++s) {
+      P += ppre[s * ep + e];
+      A += pall[s * ep + e];
+    }
+  }
+  const int cj = (tid < E) ? (cap >= 0 ? cap : A) : 0;
   const int incl = wave_incl_scan(cj);  // DPP: no LDS round trips (local layer index 8.6 vs 8.9 us)
   if (lane == kWave - 1) part[wid] = incl;
   __syncthreads();
@@ -48,7 +64,11 @@ __device__ __forceinline__ int bucket_scan(const int32_t* cnt, int E, int R, int
     excl += (q < wid) ? part[q] : 0;
     total += part[q];
   }
-  if (tid < E) off[bucket_expert(tid, R, L, LW)] = excl;
+  if (tid < E) {
+    cnt[e] = A;
+    off[e] = excl;
+    run[e] = cap < 0 ? (int32_t)base + excl + P : P;
+  }
   __syncthreads();
   return total;
 }
@@ -81,9 +101,10 @@ __device__ __forceinline__ void publish_index(const int32_t* cnt, const int32_t*
 // batch + lower lanes of this wave (bit-sliced ballot match on the id,
 // popcount of the lower peers). Then run[] advances by the batch's counts.
 // wcnt must be zero for the experts used; it is left zero. Every thread of
-// the block calls it (three barriers).
+// the block calls it (three barriers). After the block's last batch (`last`,
+// uniform) nothing reads run or wcnt again: one barrier, neither is updated.
 __device__ __forceinline__ int batch_rank(int e, bool valid, int nbits,
-                                          int32_t (*wcnt)[kIndexMaxE], int32_t* run) {
+                                          int32_t (*wcnt)[kIndexMaxE], int32_t* run, bool last) {
   const int wid = threadIdx.x / kWave;
   uint64_t peers = __ballot(valid);
   for (int bit = 0; bit < nbits; ++bit) {
@@ -102,6 +123,7 @@ __device__ __forceinline__ int batch_rank(int e, bool valid, int nbits,
     for (int q = 0; q < wid; ++q) before += wcnt[q][e];
     rel = run[e] + before + rk;
   }
+  if (last) return rel;
   __syncthreads();
   if (leader) {
     atomicAdd(&run[e], nw);
