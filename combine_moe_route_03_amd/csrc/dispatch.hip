@@ -8,7 +8,8 @@
 // Four kernels, all on the caller's stream:
 //   count_kernel  one 1024-thread block per chunk of picks: LDS histogram ->
 //                 hist[chunk][E] (LDS integer atomics: order-free, exact).
-//   place_kernel  one 1024-thread block per chunk. Each block re-derives what it
+//   place_kernel  one block (256 to 1024 threads) per chunk. Each block
+//                 re-derives what it
 //                 needs from the small hist matrix instead of waiting for a
 //                 separate scan launch: the prefix of earlier chunks and the
 //                 totals (threads laid out as (row slice, expert) so all loads
@@ -16,7 +17,7 @@
 //                 bucket per thread). Block 0 publishes counts and offsets.
 //                 Stable in-chunk ranks come from wave64 ballots (bit-sliced
 //                 match on the expert id, popcount of lower lanes) and an LDS
-//                 prefix across the block's 16 waves; the next batch of ids is
+//                 prefix across the block's waves; the next batch of ids is
 //                 prefetched while the current one is placed.
 //                 The optional statistics come from one extra block, or from
 //                 the last placing block when the placing blocks fill the chip.
@@ -39,8 +40,7 @@
 namespace moe {
 namespace {
 
-constexpr int kB = kIndexBlock;  // 1024 threads, 16 waves
-constexpr int kWaves = kIndexWaves;
+constexpr int kB = kIndexBlock;  // counting block: 1024 threads, 16 waves
 constexpr int kMaxE = kIndexMaxE;
 // placing blocks resident at once: one per compute unit (1024 threads, ~86 KiB LDS)
 constexpr int kPlaceResident = 256;
@@ -81,7 +81,8 @@ __global__ __launch_bounds__(kB) void count_kernel(const int32_t* __restrict__ i
   if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = h[tid];
 }
 
-__global__ __launch_bounds__(kB) void place_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void place_kernel(
     const int32_t* __restrict__ idx, int64_t npicks, int nsrc, int spc, int64_t src_picks,
     int64_t chunk, int k, int E, int elog, int R, int W, const int32_t* __restrict__ hist,
     int32_t* __restrict__ expert_counts,
@@ -95,17 +96,19 @@ __global__ __launch_bounds__(kB) void place_kernel(
   __shared__ int32_t run[kMaxE];           // next free row per expert for this block
   __shared__ int32_t cnt[kMaxE];           // total picks per expert
   __shared__ int32_t off[kMaxE];           // first row of each expert's bucket
-  __shared__ int32_t ppre[kB];             // (slice, expert) partial prefix
-  __shared__ int32_t pall[kB];             // (slice, expert) partial total
-  __shared__ __attribute__((aligned(16))) int32_t wcnt[kWaves][kMaxE];  // per-wave counts of a batch
-  __shared__ int32_t part[kWaves];
+  constexpr int NW = NT / kWave;           // waves of the block
+  __shared__ int32_t ppre[NT];             // (slice, expert) partial prefix
+  __shared__ int32_t pall[NT];             // (slice, expert) partial total
+  __shared__ __attribute__((aligned(16))) int32_t wcnt[NW][kMaxE];  // per-wave counts of a batch
+  __shared__ int32_t part[NW];
+  static_assert(sizeof(wcnt) >= sizeof(StatsScratch), "statistics scratch lives in wcnt");
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = blockIdx.x;
   const int L = E / R, LW = L / W;
   const int ep = 1 << elog;        // E rounded up to a power of two
   const int64_t rows = cap < 0 ? npicks : (int64_t)E * cap;  // rows of the send buffer
-  const int nslice = kB >> elog;   // row slices of the hist matrix
+  const int nslice = NT >> elog;   // row slices of the hist matrix
   // This block's shard: hist rows [h0, h1), rows from base, outputs at slice src.
   int src;
   int64_t p0, p1;
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
 
   if (tid < E) {
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) wcnt[q][tid] = 0;
+    for (int q = 0; q < NW; ++q) wcnt[q][tid] = 0;
   }
 
   // 1. Picks of each expert in the shard's earlier chunks and in all its
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kB) void place_kernel(
     }
   }
   __syncthreads();
-  const int nrow = ep < kWave ? kWaves : nslice;  // partial rows
+  const int nrow = ep < kWave ? NW : nslice;  // partial rows
   // The statistics: an extra block past the placing ones computes them and
   // leaves, or (when the placing blocks already fill the chip) placing block
   // sblock computes them after its own placement.
@@ -180,20 +183,21 @@ __global__ __launch_bounds__(kB) void place_kernel(
   //    every bucket is cap rows long) and this block's first free row of each
   //    bucket, one bucket per thread. The shard's first block publishes its
   //    counts and offsets.
-  const int total = bucket_scan(ppre, pall, nrow, ep, E, R, W, cap, base, cnt, off, run, part);
+  const int total =
+      bucket_scan<NT>(ppre, pall, nrow, ep, E, R, W, cap, base, cnt, off, run, part);
   if (b == h0)
-    publish_index(cnt, off, total, E, R, W, cap, base, expert_counts + (int64_t)src * E,
+    publish_index<NT>(cnt, off, total, E, R, W, cap, base, expert_counts + (int64_t)src * E,
                   expert_offsets + (int64_t)src * E, rank_counts + (int64_t)src * W * R,
                   rank_offsets + (int64_t)src * W * R, wave_offsets + (int64_t)src * (W + 1));
 
-  // 3. Stable ranks inside the chunk, 1024 picks per batch.
+  // 3. Stable ranks inside the chunk, NT picks per batch.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-  for (int64_t base_p = p0; base_p < p1; base_p += kB) {
+  for (int64_t base_p = p0; base_p < p1; base_p += NT) {
     const int64_t p = base_p + tid;
     const int e = e_next;
-    e_next = (p + kB < p1) ? idx[p + kB] : -1;  // prefetch the next batch
+    e_next = (p + NT < p1) ? idx[p + NT] : -1;  // prefetch the next batch
     const bool valid = (p < p1) && ((unsigned)e < (unsigned)E);
-    const int rel = batch_rank(e, valid, nbits, wcnt, run, base_p + kB >= p1);
+    const int rel = batch_rank(e, valid, nbits, wcnt, run, base_p + NT >= p1);
     if (valid) {
       const int P = cap < 0 ? rel : (rel < cap ? off[e] + rel : -1);
       pos[p] = P;
@@ -266,6 +270,32 @@ __global__ __launch_bounds__(kCopyBlock) void pad_kernel(int E, int R, int W, in
   for (int64_t q = first; q < n; q += step) send[r0 * nvec + q] = v4u{0u, 0u, 0u, 0u};
 }
 
+// Threads of a placing block: 1024, or fewer (a power of two from 256) when
+// that still holds one bucket per thread, the whole chunk in one batch and the
+// block's read of the nb x E histogram in one round of four loads a thread,
+// and (with statistics) leaves at least eight threads per value for the pair
+// sums; the block's barriers then span fewer waves (local layer index 7.4-7.7
+// -> 6.7-6.8 us). Measured no better or slower otherwise: zipf (larger
+// histogram), dirichlet_waves (19.2 -> 26.0 us: more load rounds a block),
+// decode_hot (statistics block with four threads per value, 6.4 -> 6.8 us).
+int place_threads(int E, int64_t chunk, int64_t nb, bool stats) {
+  const int64_t ep = pow2_at_least(E);
+  int nt = 256;
+  while (nt < kIndexBlock &&
+         (nt < ep || nt < chunk || nb * ep > 4 * nt || (stats && nt < 8 * ep)))
+    nt <<= 1;
+  return nt;
+}
+
+template <typename... A>
+hipError_t launch_place_kernel(int nt, unsigned grid, hipStream_t s, A... a) {
+  switch (nt) {
+    case 256: return launch(place_kernel<256>, dim3(grid), dim3(256), 0, s, a...);
+    case 512: return launch(place_kernel<512>, dim3(grid), dim3(512), 0, s, a...);
+    default: return launch(place_kernel<kIndexBlock>, dim3(grid), dim3(kIndexBlock), 0, s, a...);
+  }
+}
+
 int ilog2_ceil(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -298,9 +328,10 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
   const bool in_place = stats != nullptr && nplace >= kPlaceResident;
   const int sblock = in_place ? nplace - 1 : nplace;
   const unsigned grid = (unsigned)nplace + (stats != nullptr && !in_place ? 1u : 0u);
-  return launch(place_kernel, dim3(grid), dim3(kB), 0, s, idx, npicks, 1, nb, npicks, chunk, k,
-                E, ilog2_ceil(E), R, W, hist, expert_counts, expert_offsets, rank_counts,
-                rank_offsets, wave_offsets, pos, row_token, stats, sblock, cap);
+  const int nt = place_threads(E, chunk, nplace, stats != nullptr);
+  return launch_place_kernel(nt, grid, s, idx, npicks, 1, nb, npicks, chunk, k, E, ilog2_ceil(E),
+                             R, W, hist, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                             wave_offsets, pos, row_token, stats, sblock, cap);
 }
 
 hipError_t launch_place(const int32_t* idx, int64_t npicks, int k, int E, int R, int W,
@@ -379,7 +410,7 @@ hipError_t launch_place_sources(const int32_t* idx, int nsrc, int64_t src_picks,
   int64_t chunk;
   int spc;
   source_chunks(src_picks, E, chunk, spc);
-  return launch(place_kernel, dim3((unsigned)(nsrc * spc)), dim3(kB), 0, s, idx,
+  return launch_place_kernel(kIndexBlock, (unsigned)(nsrc * spc), s, idx,
                 (int64_t)nsrc * src_picks, nsrc, spc, src_picks, chunk, k, E, ilog2_ceil(E), R, W,
                 hist, expert_counts, expert_offsets, rank_counts, rank_offsets, wave_offsets, pos,
                 (int32_t*)nullptr, (moe_stats_t*)nullptr, -1, -1);

@@ -1,5 +1,5 @@
 // index_tables.h -- block-level pieces of the placing kernel's index stage
-// (1024-thread blocks, E <= 1024, so thread j owns bucket j and expert j): the
+// (blocks of NT <= 1024 threads, E <= NT, so thread j owns bucket j and expert j): the
 // bucket scan, the published tables, the stable in-batch rank.
 //
 // The send buffer holds one bucket per expert in (wave, rank, slot) order
@@ -13,7 +13,6 @@
 
 namespace moe {
 
-constexpr int kIndexWaves = kIndexBlock / kWave;
 constexpr int kIndexMaxE = 1024;
 
 // Inclusive prefix sum over the 64 lanes of a wave by DPP (the whole wave must
@@ -38,8 +37,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // bucket, relative) and run[e] (next free row: picks before this block, plus
 // base + off[e] without a capacity; with one the rank inside the bucket
 // decides between a row and a drop, so it stays relative). Returns the total.
-// Called by every thread of the block; part holds kIndexWaves ints of LDS.
-// Two barriers, the last at the end.
+// Called by every thread of the NT-thread block (E <= NT); part holds NT / 64
+// ints of LDS. Two barriers, the last at the end.
+template <int NT>
 __device__ __forceinline__ int bucket_scan(const int32_t* ppre, const int32_t* pall, int nrow,
                                            int ep, int E, int R, int W, int cap, int64_t base,
                                            int32_t* cnt, int32_t* off, int32_t* run,
@@ -60,7 +60,7 @@ __device__ __forceinline__ int bucket_scan(const int32_t* ppre, const int32_t* p
   __syncthreads();
   int excl = incl - cj, total = 0;
 #pragma unroll
-  for (int q = 0; q < kIndexWaves; ++q) {
+  for (int q = 0; q < NT / kWave; ++q) {
     excl += (q < wid) ? part[q] : 0;
     total += part[q];
   }
@@ -75,7 +75,9 @@ __device__ __forceinline__ int bucket_scan(const int32_t* ppre, const int32_t* p
 
 // Counts and offsets of one dispatch (rows from `base`): expert_counts (kept
 // rows: min(c, cap) with a capacity), expert_offsets, per-(wave, rank)
-// rank_counts / rank_offsets (whole buckets) and wave_offsets[W+1].
+// rank_counts / rank_offsets (whole buckets) and wave_offsets[W+1], written by
+// the NT threads of one block (E <= NT).
+template <int NT>
 __device__ __forceinline__ void publish_index(const int32_t* cnt, const int32_t* off, int total,
                                               int E, int R, int W, int cap, int64_t base,
                                               int32_t* ec, int32_t* eo, int32_t* rc, int32_t* ro,
@@ -86,13 +88,13 @@ __device__ __forceinline__ void publish_index(const int32_t* cnt, const int32_t*
     ec[tid] = (cap >= 0 && cnt[tid] > cap) ? cap : cnt[tid];
     eo[tid] = (int32_t)(base + off[tid]);
   }
-  for (int q = tid; q < W * R; q += kIndexBlock) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
+  for (int q = tid; q < W * R; q += NT) {  // q = w * R + r: buckets q*LW .. q*LW+LW-1
     int s = 0;
     for (int j = q * LW; j < q * LW + LW; ++j) s += cap >= 0 ? cap : cnt[bucket_expert(j, R, L, LW)];
     rc[q] = s;
     ro[q] = (int32_t)(base + off[bucket_expert(q * LW, R, L, LW)]);
   }
-  for (int w = tid; w <= W; w += kIndexBlock)
+  for (int w = tid; w <= W; w += NT)
     wo[w] = (int32_t)(base + ((w < W) ? off[bucket_expert(w * R * LW, R, L, LW)] : total));
 }
 

@@ -171,6 +171,10 @@ EDGES = {
     "copy_two_rows64": _edge(9001, 512, 32, 4, 4, 2),
     # expert rows beyond the cache-reuse budget: the streamed combine, ragged
     "combine_streamed": _edge(70001, 1024, 16, 1, 4, 1),
+    # small chunks and histograms: the fused index stage's 256- and 512-thread
+    # placing blocks (E = 64; E = 24 with its lane-folded partial sums)
+    "place256_E64": _edge(500, 16, 64, 4, 8, 2),
+    "place256_E24": _edge(700, 16, 24, 2, 4, 2),
 }
 
 

@@ -85,13 +85,15 @@ def test_route_index_full_size(name):
 
 
 def test_route_index_without_stats_and_empty():
-    wl = PARITY["zipf"]
-    logits = synth.logits(wl)
-    _, _, ref = _oracle_index(wl, logits)
-    idx, w, out, raw = _fused(wl, dev(logits), stats=False)
-    torch.cuda.synchronize()
-    assert raw is None
-    check_index(out, ref)
+    # zipf: 1024-thread placing blocks; decode_hot without statistics: 256
+    for name in ("zipf", "decode_hot"):
+        wl = PARITY[name]
+        logits = synth.logits(wl)
+        _, _, ref = _oracle_index(wl, logits)
+        idx, w, out, raw = _fused(wl, dev(logits), stats=False)
+        torch.cuda.synchronize()
+        assert raw is None
+        check_index(out, ref)
 
     empty = synth.Workload("edge", T=0, H=16, dtype="bf16", E=8, k=2, R=4, W=2, routing="iid",
                            seed=1)
