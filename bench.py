@@ -56,12 +56,17 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
         if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def ms(self, a, b) -> float:
         out = ctypes.c_float()
@@ -342,12 +347,12 @@ def path_default(c, args):
         c.keep = (gu, dn, ws)
         a = (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
              P(gu), P(dn), P(expert_out), P(ws), ws.numel(), s)
-        # two GEMMs, each with its tail launch (the last partial round as
-        # half-width tiles) where the tile shape has one
-        names = (["ffn_gemm_kernel<gate_up>", "ffn_gemm_kernel<gate_up,tail>",
-                  "ffn_gemm_kernel<down>", "ffn_gemm_kernel<down,tail>"]
-                 if launches_of(c, L.moe_expert_swiglu, a) == 4 else
-                 ["ffn_gemm_kernel<gate_up>", "ffn_gemm_kernel<down>"])
+        # the two GEMMs of each chain of experts (the chains run on streams of
+        # their own, so the stage is timed as the span of its kernels)
+        nl = launches_of(c, L.moe_expert_swiglu, a)
+        if nl < 2 or nl % 2:
+            raise RuntimeError(f"moe_expert_swiglu launched {nl} kernels")
+        names = ["ffn_gemm_kernel<gate_up>", "ffn_gemm_kernel<down>"] * (nl // 2)
         expert = (L.moe_expert_swiglu, a, [("expert", n) for n in names])
     else:
         expert = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
@@ -514,10 +519,13 @@ class StepRunner:
     """Runs the calls of one step; with event arrays, every kernel a call
     launches records start/stop events through the library's timing hook."""
 
-    NPAIR = 4  # event pairs per call (a call launches at most 4 kernels)
+    NPAIR = 8  # event pairs per call (a call launches at most 8 kernels)
 
-    def __init__(self, c, calls):
-        self.c, self.calls = c, calls
+    def __init__(self, c, calls, span_stages=()):
+        """span_stages: stages whose call runs its kernels on several streams at
+        once; such a call is timed from its first kernel's start to its last
+        kernel's end instead of by the sum of its kernels."""
+        self.c, self.calls, self.span_stages = c, calls, set(span_stages)
         self.hipev = HipEvents()
         self.stages = [st for st in STAGES if any(st == g for cl in calls for g, _ in cl[2])]
         self.kernel_of = {st: "+".join(dict.fromkeys(kn for cl in calls for g, kn in cl[2]
@@ -526,13 +534,24 @@ class StepRunner:
                             for st in self.stages}
         self.kernel_ms = {}
 
+    def span_stage(self, i):
+        """The stage of call i when it is timed as a span, else None."""
+        sts = {st for st, _ in self.calls[i][2]}
+        return next(iter(sts)) if len(sts) == 1 and sts <= self.span_stages else None
+
     def step(self, evs=None):
-        """One pass of the path; evs[i] = (starts, stops) event arrays of call i."""
+        """One pass of the path; evs[i] = (starts, stops, span) event arrays of
+        call i (span: two events recorded on the call's stream around it)."""
         L = self.c.L
         for i, (fn, a, kernels) in enumerate(self.calls):
+            span = evs is not None and self.span_stage(i) is not None
             if evs is not None:
                 L.moe_set_timing_events(evs[i][0], evs[i][1], self.NPAIR)
+            if span:
+                self.hipev.record(evs[i][2][0], self.c.stream)
             st = fn(*a)
+            if span:
+                self.hipev.record(evs[i][2][1], self.c.stream)
             if evs is not None:
                 n = L.moe_timed_launches()
                 L.moe_set_timing_events(None, None, 0)
@@ -544,7 +563,8 @@ class StepRunner:
     def new_events(self, n):
         def arr():
             return (ctypes.c_void_p * self.NPAIR)(*[self.hipev.create() for _ in range(self.NPAIR)])
-        return [[(arr(), arr()) for _ in self.calls] for _ in range(n)]
+        return [[(arr(), arr(), (self.hipev.create(), self.hipev.create())) for _ in self.calls]
+                for _ in range(n)]
 
     def stage_means(self, evs):
         """Per stage: summed execution time of its kernels, averaged over steps
@@ -555,12 +575,18 @@ class StepRunner:
         for e in evs:
             one = {st: 0.0 for st in self.stages}
             for i, (_, _, kernels) in enumerate(self.calls):
+                span = self.span_stage(i)
                 for j, (st, kn) in enumerate(kernels):
                     t = self.hipev.ms(e[i][0][j], e[i][1][j])
-                    tot[st] += t
-                    one[st] += t
+                    if span is None:
+                        tot[st] += t
+                        one[st] += t
                     per[kn] = per.get(kn, 0.0) + t
                     n[kn] = n.get(kn, 0) + 1
+                if span is not None:
+                    t = self.hipev.ms(e[i][2][0], e[i][2][1])
+                    tot[span] += t
+                    one[span] += t
             self.step_stage_ms.append(one)
         self.kernel_ms = {kn: per[kn] / n[kn] for kn in per}
         return {st: v / len(evs) for st, v in tot.items()}
@@ -686,7 +712,7 @@ def main() -> int:
         path = path_vsrc(c, args)
     else:
         path = path_default(c, args)
-    run = StepRunner(c, path.calls)
+    run = StepRunner(c, path.calls, span_stages=("expert",) if swiglu else ())
     T, K = wl.T, args.steps
 
     for _ in range(args.warmup):

@@ -244,6 +244,11 @@ size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I);
  * w_gate_up [E][2I][H] bf16 (rows 0..I-1 gate, I..2I-1 up), w_down [E][H][I]
  * bf16, send_buf and expert_out [T*k][H], all 16-byte aligned. workspace:
  * moe_expert_swiglu_workspace_bytes(shape, I) bytes, clobbered.
+ * Ordering: as one call on `stream`. Inside, the odd-id experts run on a side
+ * stream the library keeps per host thread and device (default priority),
+ * forked from `stream` by an event after the work already queued there and
+ * joined back by an event that `stream` waits on; so the device current at
+ * the call must be the stream's, and the call can be captured in a HIP graph.
  * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
  *         MOE_ERR_DEVICE. */
 int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,

@@ -144,3 +144,31 @@ def test_graph_replay_exchange_and_regroup():
     outputs = [idx, w, vb["recv_counts"], vb["recv_offsets"], vb["send_buf"][:n],
                vb["recv_buf"][:n], vb["grouped"][:n], veo[:n], back[:n], y]
     _replays_match(step, outputs, noise)
+
+
+def test_graph_replay_swiglu_chains():
+    """The SwiGLU FFN forks its odd-id experts onto the library's side stream
+    and joins them back: captured, the fork and join become graph edges."""
+    wl = synth.Workload("ffn", T=1000, H=256, dtype="bf16", E=16, k=2, R=1, W=1,
+                        routing="zipf0.5", expert="swiglu", I=192, seed=3)
+    print(f"[graph] swiglu: T={wl.T} H={wl.H} E={wl.E} I={wl.I} k={wl.k}", flush=True)
+    shape = shape_of(wl)
+    x = dev(synth.hidden(wl))
+    gu, dn = (dev(a) for a in synth.swiglu_weights(wl, std=0.1))
+    idx, _ = moe.route(dev(synth.logits(wl)), wl.k)
+    out = moe.dispatch(x, idx, wl.E, wl.R, wl.W)
+    eo = torch.empty_like(out["send_buf"])
+    ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
+                     device=DEV)
+    eo2, ws2 = torch.empty_like(eo), torch.empty_like(ws)
+
+    def step():
+        moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                          gu, dn, expert_out=eo, workspace=ws)
+
+    def noise():  # the same FFN eagerly, through the same side stream
+        moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                          gu, dn, expert_out=eo2, workspace=ws2)
+
+    _replays_match(step, [eo], noise)
+    assert torch.equal(eo2.view(torch.uint8), eo.view(torch.uint8))
