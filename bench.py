@@ -348,7 +348,12 @@ def path_default(c, args):
         a = (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
              P(gu), P(dn), P(expert_out), P(ws), ws.numel(), s)
         # the two GEMMs of each chain of experts (the chains run on streams of
-        # their own, so the stage is timed as the span of its kernels)
+        # their own, so the stage is timed as the span of its kernels). The
+        # count probe runs before any index stage has filled the tables: empty
+        # buckets keep it from touching rows (the launch count does not
+        # depend on them).
+        buf["expert_counts"].zero_()
+        buf["expert_offsets"].zero_()
         nl = launches_of(c, L.moe_expert_swiglu, a)
         if nl < 2 or nl % 2:
             raise RuntimeError(f"moe_expert_swiglu launched {nl} kernels")
