@@ -145,3 +145,46 @@ def test_local_layer_full_size_sampled():
     yg = oracle.bf16_to_f64(host(y[torch.from_numpy(toks).to(DEV)]))
     err = np.abs(yg - y_ref)
     assert (err <= bound + 2.0**-8 * np.abs(y_ref)).all(), f"max combine err {err.max()}"
+
+
+def test_swiglu_chains_follow_caller_stream():
+    """On a stream of the caller's own, with no synchronisation between calls:
+    the side-stream chain must start after the dispatch queued before it and
+    the combine queued after it must see both chains' rows."""
+    wl = synth.Workload("ffn", T=2048, H=256, dtype="bf16", E=16, k=2, R=1, W=1,
+                        routing="zipf0.5", expert="swiglu", I=192, seed=5)
+    print(f"[ffn] caller stream: T={wl.T} E={wl.E} H={wl.H} I={wl.I}", flush=True)
+    logits, x, gu, dn, idx_o, w_o, ec, eo, pos, rt = _ffn_setup(wl, std=0.1)
+    shape = moe.Shape(wl.T, wl.H, wl.E, wl.k, wl.R, wl.W, torch.bfloat16)
+    xd, gud, dnd, ld = dev(x), dev(gu), dev(dn), dev(logits)
+    torch.cuda.synchronize()
+    ref = None
+    for attempt in range(2):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            idx, w = moe.route(ld, wl.k)
+            out = moe.alloc_dispatch(shape, DEV)
+            out["send_buf"].view(torch.uint8).fill_(0xA5)  # stale rows would show
+            moe.dispatch_index(idx, shape, out)
+            moe.dispatch_copy(xd, out["pos"], shape, out["send_buf"])
+            eo_gpu = torch.empty_like(out["send_buf"])
+            eo_gpu.view(torch.uint8).fill_(0x5A)
+            moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                              gud, dnd, expert_out=eo_gpu)
+            y = moe.combine(eo_gpu, w, out["pos"], shape)
+            got = (eo_gpu.clone(), y.clone())
+        s.synchronize()
+        # the combine queued behind the FFN on the caller's stream must equal
+        # one run after everything has finished
+        y_after = moe.combine(got[0], w, out["pos"], shape)
+        torch.cuda.synchronize()
+        assert torch.equal(got[1].view(torch.uint8), y_after.view(torch.uint8))
+        if ref is None:
+            ref = got
+            nrows = int(ec.sum())
+            rows = np.arange(nrows)
+            o64, _ = oracle.expert_swiglu_rows(x[rt[rows]], _row_expert(ec, eo, rows), gu, dn)
+            _check_rows(host(got[0]), o64, atol=2e-3)
+        else:  # a second stream, same results bit for bit
+            assert torch.equal(got[0].view(torch.uint8), ref[0].view(torch.uint8))
+            assert torch.equal(got[1].view(torch.uint8), ref[1].view(torch.uint8))
