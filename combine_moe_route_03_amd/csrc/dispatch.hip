@@ -42,7 +42,8 @@ namespace {
 
 constexpr int kB = kIndexBlock;  // counting block: 1024 threads, 16 waves
 constexpr int kMaxE = kIndexMaxE;
-// placing blocks resident at once: one per compute unit (1024 threads, ~86 KiB LDS)
+// placing blocks resident at once: one per compute unit (1024 threads, ~86 KiB
+// LDS; smaller blocks are chosen only for grids far below this)
 constexpr int kPlaceResident = 256;
 
 // Picks [p0, p1) of block b: chunk b - src*spc of shard src.
