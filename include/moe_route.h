@@ -310,11 +310,15 @@ int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_o
  * moe_expert_swiglu. copy_stream first waits for the work already queued on
  * compute_stream; when this call returns, compute_stream carries every wave's
  * FFN (follow with moe_combine there). copy_stream == compute_stream runs the
- * same launches serialised. The library keeps W+1 reusable events per host
- * thread and device (created on first use, on the device current at the call,
- * which must be the device of both streams). Arguments as moe_expert_swiglu, plus x
- * [T][H], row_token [T*k], wave_offsets [W+1] (DEVICE). 3W launches: W
- * gathers and 2W FFN kernels.
+ * same launches serialised. When a wave's experts split into even and odd
+ * slots as one stride-2 run of ids each (R == 1, or W == 1) and a wave holds
+ * at least eight experts, the odd ones run on a side stream forked from
+ * compute_stream after the wave's event and joined back into it (as in
+ * moe_expert_swiglu). The library keeps 3W+1 reusable events and that side
+ * stream per host thread and device (created on first use, on the device
+ * current at the call, which must be the device of both streams). Arguments as
+ * moe_expert_swiglu, plus x [T][H], row_token [T*k], wave_offsets [W+1]
+ * (DEVICE). W gathers and 2W FFN kernels, or 4W with the two chains.
  * Errors: as moe_expert_swiglu; MOE_ERR_ARG also for null x / row_token /
  *         wave_offsets. */
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,

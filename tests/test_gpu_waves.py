@@ -49,8 +49,11 @@ def _waves(wl, x, gu, dn, idx, w, two_streams):
     return out, eo, y
 
 
+# two chains of experts a wave: R1_W1, R1_W2 (one rank), R4_W1 (one wave); the
+# others one chain (fewer than eight experts a wave, or a split that is not a
+# stride-2 run of expert ids)
 CASES = [("R1_W1", 1, 1), ("R1_W2", 1, 2), ("R1_W4", 1, 4), ("R1_W16", 1, 16), ("R2_W2", 2, 2),
-         ("R4_W4", 4, 4)]
+         ("R4_W4", 4, 4), ("R4_W1", 4, 1)]
 
 
 @pytest.mark.parametrize("name,R,W", CASES)
