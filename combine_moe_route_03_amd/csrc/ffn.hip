@@ -45,9 +45,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXCD = 8;
-// m-tiles per rasterisation patch: on the local layer 1 measured 701 us against
-// 714 for 4 (an even split of rows favours 4-16 by ~3%; the layer is skewed)
-constexpr int kGroupM = 1;
+// m-tiles per rasterisation patch. With one chain of experts the local layer
+// measured 701 us for 1 against 714 for 4; with two chains sharing each XCD's
+// L2, 4 and 8 are faster than 1 (step 723-726 against 733 us, same box).
+constexpr int kGroupM = 4;
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
 
