@@ -67,7 +67,8 @@ SIGNATURES = {
                                ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_swiglu_waves": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                          ctypes.c_size_t, _vp, _vp], ctypes.c_int),
+                          ctypes.c_size_t, _vp, _vp, _vp, _vp, _i32], ctypes.c_int),
+    "moe_swiglu_waves_events": ([_i32], ctypes.c_int32),
     "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
     "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp], ctypes.c_int),
@@ -77,8 +78,8 @@ SIGNATURES = {
     "moe_vsrc_regroup": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                          ctypes.c_int),
     "moe_expert_swiglu_workspace_bytes": ([_shp, _i32], ctypes.c_size_t),
-    "moe_expert_swiglu": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
-                          ctypes.c_int),
+    "moe_expert_swiglu": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                           _vp, _vp, _vp], ctypes.c_int),
     "moe_combine": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_stats": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "moe_dirichlet_alpha": ([_vp, _i32, _vp, _vp], ctypes.c_int),
@@ -153,6 +154,36 @@ class Shape:
 
 def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
+
+
+class Chains:
+    """Caller-owned stream resources of the FFN entry points: a side stream for
+    the second chain of experts (None: one chain) and n_events events (torch
+    objects; the library keeps none of them). Create it before capturing a
+    graph that uses it: the event handles are materialised here by one record
+    on the side stream (or the current stream)."""
+
+    def __init__(self, n_events: int = 2, side: bool = True, device=None):
+        self.stream = torch.cuda.Stream(device=device) if side else None
+        self.events = [torch.cuda.Event() for _ in range(n_events)]
+        where = self.stream if self.stream is not None else torch.cuda.current_stream(device)
+        for e in self.events:
+            e.record(where)
+        self._handles = (ctypes.c_void_p * max(n_events, 1))(
+            *[ctypes.c_void_p(e.cuda_event) for e in self.events])
+
+    def side_ptr(self) -> ctypes.c_void_p | None:
+        return None if self.stream is None else ctypes.c_void_p(self.stream.cuda_stream)
+
+    def event_ptr(self, i: int) -> ctypes.c_void_p:
+        return ctypes.c_void_p(self.events[i].cuda_event)
+
+    def event_array(self):
+        return self._handles
+
+
+def swiglu_waves_events(W: int) -> int:
+    return int(lib().moe_swiglu_waves_events(W))
 
 
 # ----------------------------------------------------------------------- route
@@ -407,30 +438,39 @@ def expert_swiglu_workspace_bytes(shape: Shape, I: int) -> int:
 def expert_swiglu(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
                   expert_counts: torch.Tensor, shape: Shape, w_gate_up: torch.Tensor,
                   w_down: torch.Tensor, expert_out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """SwiGLU expert FFN on MFMA; w_gate_up [E,2I,H], w_down [E,H,I] bf16."""
+                  workspace: torch.Tensor | None = None,
+                  chains: Chains | None = None) -> torch.Tensor:
+    """SwiGLU expert FFN on MFMA; w_gate_up [E,2I,H], w_down [E,H,I] bf16. With
+    `chains` (a side stream and two events) the odd-id experts run on the side
+    stream; without, one chain on the current stream."""
     I = w_down.shape[2]
     expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
     if workspace is None:
         workspace = _empty((max(expert_swiglu_workspace_bytes(shape, I), 1),), torch.uint8,
                            send_buf.device)
+    side, fork, join = None, None, None
+    if chains is not None and chains.stream is not None:
+        side, fork, join = chains.side_ptr(), chains.event_ptr(0), chains.event_ptr(1)
     sh = shape.c()
     _check(lib().moe_expert_swiglu(ctypes.byref(sh), I, _ptr(send_buf), _ptr(expert_offsets),
                                    _ptr(expert_counts), _ptr(w_gate_up), _ptr(w_down),
                                    _ptr(expert_out), _ptr(workspace), workspace.numel(),
-                                   _stream()), "moe_expert_swiglu")
+                                   _stream(), side, fork, join), "moe_expert_swiglu")
     return expert_out
 
 
 def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tensor,
                  w_down: torch.Tensor, expert_out: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None,
-                 copy_stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+                 copy_stream: torch.cuda.Stream | None = None,
+                 chains: Chains | None = None) -> torch.Tensor:
     """Wave-pipelined dispatch + SwiGLU FFN: per wave a gather of its rows into
     out["send_buf"] on `copy_stream`, then the FFN of its experts on the
     current stream after an event. `out` holds a dispatch index of `shape`
     (row_token, wave_offsets, expert offsets/counts). No copy stream: the same
-    launches on the current stream."""
+    launches on the current stream. `chains` supplies the events (at least
+    swiglu_waves_events(W) of them when a copy stream or a side stream is used)
+    and, when it has one, the side stream of the second chain of experts."""
     I = w_down.shape[2]
     send_buf = out["send_buf"]
     expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
@@ -439,12 +479,19 @@ def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tens
                            send_buf.device)
     compute = _stream()
     copy = compute if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    side = chains.side_ptr() if chains is not None else None
+    if (copy_stream is not None or side is not None) and (
+            chains is None or len(chains.events) < swiglu_waves_events(shape.W)):
+        raise ValueError(f"swiglu_waves with a copy or side stream needs a Chains with at least "
+                         f"{swiglu_waves_events(shape.W)} events")
+    events = chains.event_array() if chains is not None else None
+    n_events = len(chains.events) if chains is not None else 0
     sh = shape.c()
     _check(lib().moe_swiglu_waves(
         ctypes.byref(sh), I, _ptr(x), _ptr(out["row_token"]), _ptr(out["wave_offsets"]),
         _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(w_gate_up), _ptr(w_down),
-        _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), compute, copy),
-        "moe_swiglu_waves")
+        _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), compute, copy,
+        side, events, n_events), "moe_swiglu_waves")
     return expert_out
 
 

@@ -294,32 +294,44 @@ extern "C" {
 int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
                       const int32_t* expert_offsets, const int32_t* expert_counts,
                       const void* w_gate_up, const void* w_down, void* expert_out,
-                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream) {
+                      void* workspace, size_t workspace_bytes_given, moe_stream_t stream,
+                      moe_stream_t side_stream, void* fork_event, void* join_event) {
   const int st = check_swiglu_args(shape, I, send_buf, expert_offsets, expert_counts, w_gate_up,
                                    w_down, expert_out, workspace, workspace_bytes_given);
   if (st != MOE_OK) return st;
+  if (side_stream && (!fork_event || !join_event)) return MOE_ERR_ARG;
   const int64_t rows = int64_t(shape->T) * shape->k;
-  return status_of(moe::launch_expert_swiglu(send_buf, rows, shape->H, I, shape->E,
-                                             expert_offsets, expert_counts, w_gate_up, w_down,
-                                             workspace, expert_out, as_stream(stream)));
+  return status_of(moe::launch_expert_swiglu(
+      send_buf, rows, shape->H, I, shape->E, expert_offsets, expert_counts, w_gate_up, w_down,
+      workspace, expert_out, as_stream(stream), as_stream(side_stream),
+      static_cast<hipEvent_t>(fork_event), static_cast<hipEvent_t>(join_event)));
 }
+
+int32_t moe_swiglu_waves_events(int32_t W) { return W < 1 || W > (1 << 20) ? -1 : 1 + 3 * W; }
 
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
                      const int32_t* wave_offsets, const int32_t* expert_offsets,
                      const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
                      void* send_buf, void* expert_out, void* workspace,
                      size_t workspace_bytes_given, moe_stream_t compute_stream,
-                     moe_stream_t copy_stream) {
+                     moe_stream_t copy_stream, moe_stream_t side_stream, void* const* events,
+                     int32_t n_events) {
   int st = check_swiglu_args(shape, I, send_buf, expert_offsets, expert_counts, w_gate_up,
                              w_down, expert_out, workspace, workspace_bytes_given);
   if (st != MOE_OK) return st;
   if (!wave_offsets) return MOE_ERR_ARG;
   if (shape->T > 0 && (!x || !row_token)) return MOE_ERR_ARG;
   if (!aligned(x, 16) || !aligned(row_token, 4) || !aligned(wave_offsets, 4)) return MOE_ERR_ALIGN;
+  if (copy_stream != compute_stream || side_stream) {
+    if (!events || n_events < moe_swiglu_waves_events(shape->W)) return MOE_ERR_ARG;
+    for (int32_t i = 0; i < 1 + 3 * shape->W; ++i)
+      if (!events[i]) return MOE_ERR_ARG;
+  }
   return status_of(moe::launch_swiglu_waves(
       x, shape->T, shape->k, shape->H, I, shape->E, shape->R, shape->W, row_token, wave_offsets,
       expert_offsets, expert_counts, w_gate_up, w_down, send_buf, workspace, expert_out,
-      as_stream(compute_stream), as_stream(copy_stream)));
+      as_stream(compute_stream), as_stream(copy_stream), as_stream(side_stream),
+      reinterpret_cast<const hipEvent_t*>(events)));
 }
 
 int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_out,

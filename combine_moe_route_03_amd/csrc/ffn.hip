@@ -414,64 +414,33 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
                                      w_gate_up, w_down, hbuf, out, s);
 }
 
-namespace {
-
-// A side stream with its fork and join events, created once per host thread
-// and device (a stream belongs to the device current at its creation) and
-// reused: a wait takes the event's most recent record at the time it is
-// enqueued.
-constexpr int kMaxDevices = 64;
-struct SideChain {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-hipError_t side_chain(SideChain*& out) {
-  thread_local SideChain pool[kMaxDevices];
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideChain& c = pool[dev];
-  if (!c.stream) {
-    SideChain n;
-    if ((err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess) return err;
-    if ((err = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) return err;
-    if ((err = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return err;
-    c = n;
-  }
-  out = &c;
-  return hipSuccess;
-}
-
-}  // namespace
-
 // The experts run as two chains, even and odd expert ids, each its gate/up
-// GEMM then its down GEMM: the first on the caller's stream, the second on a
-// side stream forked from it and joined back into it. While one chain's last,
-// partial round of tiles runs, the other chain's tiles fill the idle compute
-// units (local layer step 772 -> 733 us; halves by id 753, three or four
-// chains 797 and 830 us). Per-element arithmetic is that of one launch.
+// GEMM then its down GEMM: the first on the caller's stream, the second on the
+// caller's side stream, forked from the first by one caller event and joined
+// back into it by another. While one chain's last, partial round of tiles
+// runs, the other chain's tiles fill the idle compute units (local layer step
+// 772 -> 733 us; halves by id 753, three or four chains 797 and 830 us).
+// Per-element arithmetic is that of one launch. Without a side stream, one
+// chain of all experts on the caller's stream.
 hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, int E,
                                 const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
-                                const void* w_down, void* hbuf, void* out, hipStream_t s) {
+                                const void* w_down, void* hbuf, void* out, hipStream_t s,
+                                hipStream_t side, hipEvent_t fork, hipEvent_t join) {
   if (rows == 0 || E == 0) return hipSuccess;
-  if (E < 2)
+  if (E < 2 || side == nullptr)
     return launch_expert_swiglu_subset(send, rows, H, I, E, E, 0, 0, offs, cnts, w_gate_up,
                                        w_down, hbuf, out, s);
-  SideChain* sc = nullptr;
-  hipError_t err = side_chain(sc);
-  if (err != hipSuccess) return err;
-  if ((err = hipEventRecord(sc->fork, s)) != hipSuccess) return err;
-  if ((err = hipStreamWaitEvent(sc->stream, sc->fork, 0)) != hipSuccess) return err;
+  hipError_t err;
+  if ((err = hipEventRecord(fork, s)) != hipSuccess) return err;
+  if ((err = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return err;
   for (int c = 0; c < 2; ++c) {
     // chain c: experts 2i + c
     err = launch_expert_swiglu_subset(send, rows, H, I, (E - c + 1) / 2, 1, 2, c, offs, cnts,
-                                      w_gate_up, w_down, hbuf, out, c ? sc->stream : s);
+                                      w_gate_up, w_down, hbuf, out, c ? side : s);
     if (err != hipSuccess) return err;
   }
-  if ((err = hipEventRecord(sc->join, sc->stream)) != hipSuccess) return err;
-  return hipStreamWaitEvent(s, sc->join, 0);
+  if ((err = hipEventRecord(join, side)) != hipSuccess) return err;
+  return hipStreamWaitEvent(s, join, 0);
 }
 
 }  // namespace moe

@@ -163,9 +163,12 @@ hipError_t launch_dirichlet_alpha(const int32_t* counts, int E, double* out, hip
 // Grouped SwiGLU FFN (bf16): gate/up GEMM with fused SiLU*up into hbuf
 // [rows][I], then the down GEMM into out [rows][H]. Needs I % 64 == 0 and
 // H % 128 == 0.
+// With a side stream the odd-id experts run there, forked from s by the event
+// `fork` and joined back by `join` (both caller-owned); without, one chain.
 hipError_t launch_expert_swiglu(const void* send, int64_t rows, int H, int I, int E,
                                 const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
-                                const void* w_down, void* hbuf, void* out, hipStream_t s);
+                                const void* w_down, void* hbuf, void* out, hipStream_t s,
+                                hipStream_t side, hipEvent_t fork, hipEvent_t join);
 
 // The FFN on a subset of n experts: the i-th is expert (i / sg) * sstride +
 // sbase + i % sg (all E experts: n = sg = E, sstride = sbase = 0).
@@ -176,7 +179,9 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
 
 // Wave-pipelined local layer: per wave, gather dispatch of its rows on `copy`,
 // then the FFN of its experts on `compute` after an event (copy == compute:
-// the same work, serialised).
+// the same work, serialised). `events` holds at least 1 + 3W caller-owned
+// events when copy != compute or side is non-null; `side` (may be null)
+// carries the second chain of a wave's experts.
 hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int32_t* wave_offsets,
                               int w, int T, int64_t rows_max, int64_t row_bytes, void* send,
                               hipStream_t s);
@@ -184,7 +189,8 @@ hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                const void* w_down, void* send, void* hbuf, void* out,
-                               hipStream_t compute, hipStream_t copy);
+                               hipStream_t compute, hipStream_t copy, hipStream_t side,
+                               const hipEvent_t* events);
 
 // Expert id of the j-th bucket when buckets run in (wave, rank, slot) order:
 // L = E / R slots per rank, LW = L / W slots per wave.

@@ -9,12 +9,11 @@
 // a copy stream, an event, and the SwiGLU FFN of that wave's experts on the
 // compute stream once the event has fired; so the gather of wave w+1 (HBM
 // bound) runs under the FFN of wave w (MFMA bound). Where the wave's experts
-// split into even and odd slots, the odd ones run on a side stream forked
-// from the compute stream and joined back, as the unpipelined FFN does. The
+// split into even and odd slots, the odd ones run on the caller's side stream
+// forked from the compute stream and joined back, as the unpipelined FFN does;
+// every stream and event is the caller's (the library keeps none). The
 // combine runs once, after the last wave, with the same arithmetic as the
 // unpipelined path.
-#include <vector>
-
 #include "device.h"
 #include "launch.h"
 
@@ -59,45 +58,6 @@ __global__ __launch_bounds__(kBlock) void gather_wave_kernel(
   }
 }
 
-// Events of the pipeline, created once per host thread and device (an event
-// belongs to the device current when it was created) and reused by later calls
-// (a wait takes the event's most recent record at the time it is enqueued).
-constexpr int kMaxDevices = 64;
-
-// A side stream for the second chain of a wave's experts, one per host thread
-// and device like the events.
-hipError_t side_stream(hipStream_t& out) {
-  thread_local hipStream_t pool[kMaxDevices] = {};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (!pool[dev]) {
-    hipStream_t st = nullptr;
-    if ((err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return err;
-    pool[dev] = st;
-  }
-  out = pool[dev];
-  return hipSuccess;
-}
-
-hipError_t wave_events(int n, std::vector<hipEvent_t>*& out) {
-  thread_local std::vector<hipEvent_t> pool[kMaxDevices];
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::vector<hipEvent_t>& p = pool[dev];
-  while ((int)p.size() < n) {
-    hipEvent_t e;
-    err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-    if (err != hipSuccess) return err;
-    p.push_back(e);
-  }
-  out = &p;
-  return hipSuccess;
-}
-
 }  // namespace
 
 hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int32_t* wave_offsets,
@@ -114,37 +74,35 @@ hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                const void* w_down, void* send, void* hbuf, void* out,
-                               hipStream_t compute, hipStream_t copy) {
+                               hipStream_t compute, hipStream_t copy, hipStream_t side,
+                               const hipEvent_t* events) {
   const int64_t rows = (int64_t)T * k;
   if (rows == 0) return hipSuccess;
   const int L = E / R, LW = L / W;
   const int64_t row_bytes = (int64_t)H * 2;
   const bool two = copy != compute;
-  // A wave's experts run as two chains (even and odd slots, the second on a
-  // side stream) when that split is one stride-2 run of expert ids (one rank,
-  // or one wave: all experts) and the wave has at least eight experts. Local
-  // layer, one stream: W = 1 776 -> 741 us, W = 2 867 -> 842; with chains of
-  // one or two experts W = 4 1011 -> 1019, W = 8 1446 -> 1632 (the fork and
-  // join cost more than the overlap gives). Otherwise one chain.
-  const bool chains = R * LW >= 8 && (R == 1 || W == 1);
-  std::vector<hipEvent_t>* ev = nullptr;
-  hipStream_t side = nullptr;
+  // A wave's experts run as two chains (even and odd slots, the second on the
+  // side stream) when the caller gives one, that split is one stride-2 run of
+  // expert ids (one rank, or one wave: all experts) and the wave has at least
+  // eight experts. Local layer, one stream: W = 1 776 -> 741 us, W = 2 867 ->
+  // 842; with chains of one or two experts W = 4 1011 -> 1019, W = 8 1446 ->
+  // 1632 (the fork and join cost more than the overlap gives). Otherwise one
+  // chain.
+  const bool chains = side != nullptr && R * LW >= 8 && (R == 1 || W == 1);
   hipError_t e = hipSuccess;
   // events: [0] copy start, [1..W] gathers, then a fork and a join per wave
-  if ((e = wave_events(1 + W + (chains ? 2 * W : 0), ev)) != hipSuccess) return e;
-  if (chains && (e = side_stream(side)) != hipSuccess) return e;
   if (two) {
     // the copy stream starts after everything already queued on the compute
     // stream (the index stage that wrote row_token and wave_offsets)
-    if ((e = hipEventRecord((*ev)[0], compute)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(copy, (*ev)[0], 0)) != hipSuccess) return e;
+    if ((e = hipEventRecord(events[0], compute)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(copy, events[0], 0)) != hipSuccess) return e;
   }
   for (int w = 0; w < W; ++w) {
     e = launch_gather_wave(x, row_token, wave_offsets, w, T, rows, row_bytes, send, copy);
     if (e != hipSuccess) return e;
     if (two) {
-      if ((e = hipEventRecord((*ev)[w + 1], copy)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(compute, (*ev)[w + 1], 0)) != hipSuccess) return e;
+      if ((e = hipEventRecord(events[w + 1], copy)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(compute, events[w + 1], 0)) != hipSuccess) return e;
     }
     if (!chains) {
       // the R*LW experts of wave w: slots w*LW .. w*LW+LW-1 of every rank
@@ -155,7 +113,7 @@ hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E,
     }
     // the wave's experts w*LW + 2i + c (R == 1), or 2i + c (W == 1), as two
     // chains: c = 0 on the compute stream, c = 1 on the side stream
-    hipEvent_t fork = (*ev)[1 + W + 2 * w], join = (*ev)[2 + W + 2 * w];
+    hipEvent_t fork = events[1 + W + 2 * w], join = events[2 + W + 2 * w];
     if ((e = hipEventRecord(fork, compute)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
     const int n = R * LW;

@@ -14,8 +14,10 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers unless stated otherwise. The
- *     caller owns every buffer; the library never allocates, frees or keeps
- *     pointers past the call, and holds no mutable global state.
+ *     caller owns every buffer, stream and event; the library never allocates,
+ *     frees, creates or keeps them past the call. The one piece of mutable
+ *     library state is the benchmark timing hook (moe_set_timing_events): per
+ *     host thread, inert unless armed, and not part of the path.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream). Results are ready when the stream reaches that point.
  *   - Arguments are validated on the host before anything is launched. On any
@@ -244,17 +246,24 @@ size_t moe_expert_swiglu_workspace_bytes(const moe_shape* shape, int32_t I);
  * w_gate_up [E][2I][H] bf16 (rows 0..I-1 gate, I..2I-1 up), w_down [E][H][I]
  * bf16, send_buf and expert_out [T*k][H], all 16-byte aligned. workspace:
  * moe_expert_swiglu_workspace_bytes(shape, I) bytes, clobbered.
- * Ordering: as one call on `stream`. Inside, the odd-id experts run on a side
- * stream the library keeps per host thread and device (default priority),
- * forked from `stream` by an event after the work already queued there and
- * joined back by an event that `stream` waits on; so the device current at
- * the call must be the stream's, and the call can be captured in a HIP graph.
- * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
- *         MOE_ERR_DEVICE. */
+ * Two chains: with side_stream non-NULL the odd-id experts run there (their
+ * gate/up then down GEMM) while the even-id experts run on `stream`, so one
+ * chain's partial last round of tiles is filled by the other's. side_stream
+ * is forked from `stream` by recording fork_event on `stream` (after the work
+ * already queued there) and joined back by recording join_event on
+ * side_stream, which `stream` then waits on: ordering is as one call on
+ * `stream`. All three are the caller's (hipStream_t, hipEvent_t handles, on
+ * the device of `stream`, default priority); a caller running several FFN
+ * calls at once gives each its own side stream and events. side_stream NULL:
+ * one chain of all experts on `stream` (the events are then ignored). The
+ * call can be captured in a HIP graph (record and wait become graph edges).
+ * Errors: MOE_ERR_ARG (also side_stream without both events), MOE_ERR_ALIGN,
+ *         MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
                       const int32_t* expert_offsets, const int32_t* expert_counts,
                       const void* w_gate_up, const void* w_down, void* expert_out,
-                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream,
+                      moe_stream_t side_stream, void* fork_event, void* join_event);
 
 /* Combine, MoE systems survey section 1.1 eq. (1) and EP flow step 4 (restore
  * the original token order, weight each expert output by its gate value):
@@ -310,22 +319,30 @@ int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_o
  * moe_expert_swiglu. copy_stream first waits for the work already queued on
  * compute_stream; when this call returns, compute_stream carries every wave's
  * FFN (follow with moe_combine there). copy_stream == compute_stream runs the
- * same launches serialised. When a wave's experts split into even and odd
- * slots as one stride-2 run of ids each (R == 1, or W == 1) and a wave holds
- * at least eight experts, the odd ones run on a side stream forked from
- * compute_stream after the wave's event and joined back into it (as in
- * moe_expert_swiglu). The library keeps 3W+1 reusable events and that side
- * stream per host thread and device (created on first use, on the device
- * current at the call, which must be the device of both streams). Arguments as
+ * same launches serialised. With side_stream non-NULL, a wave whose experts
+ * split into even and odd slots as one stride-2 run of ids each (R == 1, or
+ * W == 1) and that holds at least eight experts runs the odd ones on
+ * side_stream, forked from compute_stream after the wave's event and joined
+ * back into it (as in moe_expert_swiglu).
+ * events: n_events caller-owned hipEvent_t handles, at least
+ * moe_swiglu_waves_events(W) = 1 + 3W of them whenever copy_stream !=
+ * compute_stream or side_stream is non-NULL (one to start the copy stream, one
+ * per gather, a fork and a join per wave); unused otherwise. Streams and
+ * events are the caller's, on one device. Arguments otherwise as
  * moe_expert_swiglu, plus x [T][H], row_token [T*k], wave_offsets [W+1]
  * (DEVICE). W gathers and 2W FFN kernels, or 4W with the two chains.
  * Errors: as moe_expert_swiglu; MOE_ERR_ARG also for null x / row_token /
- *         wave_offsets. */
+ *         wave_offsets, and for too few (or null) events when they are used. */
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
                      const int32_t* wave_offsets, const int32_t* expert_offsets,
                      const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
                      void* send_buf, void* expert_out, void* workspace, size_t workspace_bytes,
-                     moe_stream_t compute_stream, moe_stream_t copy_stream);
+                     moe_stream_t compute_stream, moe_stream_t copy_stream,
+                     moe_stream_t side_stream, void* const* events, int32_t n_events);
+
+/* Events moe_swiglu_waves needs for W waves: 1 + 3W (-1 for W outside
+ * [1, 2^20]). Host-only, pure. */
+int32_t moe_swiglu_waves_events(int32_t W);
 
 /* ---------------------------------------------------------------------------
  * Virtual-source exchange: the expert-parallel exchange of R ranks emulated on

@@ -92,7 +92,8 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_int64, _f64p, _vp]
         _u16p = ctypes.POINTER(ctypes.c_uint16)
         L.oracle_expert_swiglu_rows.argtypes = [_u16p, _i32p, ctypes.c_int64, ctypes.c_int64,
-                                                ctypes.c_int64, _u16p, _u16p, _f64p, _u16p]
+                                                ctypes.c_int64, _u16p, _u16p, _f64p, _u16p,
+                                                _f64p]
         L.oracle_stats.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Stats)]
         _d = ctypes.c_double
         L.oracle_wave_time.argtypes = [_d, _d, _d, _d]
@@ -278,8 +279,9 @@ def scaled_tokens(x: np.ndarray, idx: np.ndarray, w: np.ndarray, E: int, tokens,
 
 
 def expert_swiglu_rows(rows: np.ndarray, row_expert, w_gate_up: np.ndarray,
-                       w_down: np.ndarray):
-    """SwiGLU FFN of the given bf16 rows: (out_f64 [n,H], out_bf16 bits [n,H])."""
+                       w_down: np.ndarray, want_gu: bool = False):
+    """SwiGLU FFN of the given bf16 rows: (out_f64 [n,H], out_bf16 bits [n,H]),
+    plus the pre-activation sums gu [n, 2I] (g then u) with want_gu."""
     rows = np.ascontiguousarray(rows, dtype=np.uint16)
     n, H = rows.shape
     I = w_down.shape[2]
@@ -290,9 +292,11 @@ def expert_swiglu_rows(rows: np.ndarray, row_expert, w_gate_up: np.ndarray,
     o64 = np.empty((n, H), np.float64)
     o16 = np.empty((n, H), np.uint16)
     u16 = ctypes.POINTER(ctypes.c_uint16)
+    gus = np.empty((n, 2 * I), np.float64) if want_gu else None
     lib().oracle_expert_swiglu_rows(_p(rows, u16), _p(re, _i32p), n, H, I, _p(gu, u16),
-                                    _p(dn, u16), _p(o64, _f64p), _p(o16, u16))
-    return o64, o16
+                                    _p(dn, u16), _p(o64, _f64p), _p(o16, u16),
+                                    _p(gus, _f64p) if want_gu else None)
+    return (o64, o16, gus) if want_gu else (o64, o16)
 
 
 def stats(expert_counts: np.ndarray, R: int) -> dict:

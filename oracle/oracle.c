@@ -242,7 +242,7 @@ void oracle_expert_swiglu_rows(const uint16_t* rows, const int32_t* row_expert,
                                int64_t n, int64_t H, int64_t I,
                                const uint16_t* w_gate_up,
                                const uint16_t* w_down, double* out_f64,
-                               uint16_t* out_bf16) {
+                               uint16_t* out_bf16, double* gu_out) {
   double* hmid = (double*)malloc(sizeof(double) * (size_t)I);
   for (int64_t r = 0; r < n; ++r) {
     const uint16_t* s = rows + r * H;
@@ -256,6 +256,10 @@ void oracle_expert_swiglu_rows(const uint16_t* rows, const int32_t* row_expert,
         double sv = load_elem_bits_bf16(s[h]);
         g += load_elem_bits_bf16(wg[j * H + h]) * sv;
         u += load_elem_bits_bf16(wu[j * H + h]) * sv;
+      }
+      if (gu_out) {
+        gu_out[r * 2 * I + j] = g;
+        gu_out[r * 2 * I + I + j] = u;
       }
       double silu = g / (1.0 + exp(-g));
       hmid[j] = load_elem_bits_bf16(oracle_round_bf16(silu * u));

@@ -119,10 +119,17 @@ def test_swiglu_size_limits():
     L = moe.lib()
     sh = _shape(T=8, H=4096, E=16, k=2, R=1)
     # one expert's gate/up weights past the 31-bit byte range of the kernels' descriptors
-    assert L.moe_expert_swiglu(ctypes.byref(sh), 1 << 17, *[FAKE] * 7, 1 << 40, None) == ARG
-    assert L.moe_expert_swiglu(ctypes.byref(sh), 1408 + 32, *[FAKE] * 7, 1 << 40, None) == ARG
+    one = (None, None, None, None)  # stream; no side stream, no events
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1 << 17, *[FAKE] * 7, 1 << 40, *one) == ARG
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1408 + 32, *[FAKE] * 7, 1 << 40, *one) == ARG
     sh32 = _shape(T=8, H=4096, E=16, k=2, R=1, dtype=moe.MOE_F32)
-    assert L.moe_expert_swiglu(ctypes.byref(sh32), 1408, *[FAKE] * 7, 1 << 40, None) == UNSUPPORTED
+    assert L.moe_expert_swiglu(ctypes.byref(sh32), 1408, *[FAKE] * 7, 1 << 40, *one) == UNSUPPORTED
+    # a side stream needs both of its events
+    ws = L.moe_expert_swiglu_workspace_bytes(ctypes.byref(sh), 1408)
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1408, *[FAKE] * 7, ws, None, FAKE, None,
+                               FAKE) == ARG
+    assert L.moe_expert_swiglu(ctypes.byref(sh), 1408, *[FAKE] * 7, ws, None, FAKE, FAKE,
+                               None) == ARG
 
 
 def test_route_index_validation():
@@ -240,10 +247,20 @@ def test_swiglu_waves_validation():
     # x, row_token, wave_offsets, offsets, counts, w_gate_up, w_down, send, out, workspace
     a = [FAKE] * 10
     ok = lambda *v: L.moe_swiglu_waves(ctypes.byref(v[0]), v[1], *v[2], ws if len(v) < 4 else v[3],  # noqa: E731
-                                       None, None)
+                                       None, None, None, None, 0)
     assert ok(sh, 100, a) == ARG                              # I % 64 != 0
     assert ok(_shape(T=64, H=256, E=8, k=2, R=1, W=2, dtype=moe.MOE_F32), 128, a) == UNSUPPORTED
     assert ok(sh, 128, [FAKE, FAKE, None] + a[3:]) == ARG     # no wave_offsets
     assert ok(sh, 128, [None] + a[1:]) == ARG                 # no x
     assert ok(sh, 128, [ctypes.c_void_p((1 << 20) + 4)] + a[1:]) == ALIGN
     assert ok(sh, 128, a, ws - 1) == WORKSPACE
+    # a copy or side stream needs 1 + 3W caller events, none of them null
+    assert L.moe_swiglu_waves_events(2) == 7
+    assert L.moe_swiglu_waves_events(0) == -1
+    evs = (ctypes.c_void_p * 7)(*[FAKE] * 7)
+    waves = lambda copy, side, ev, n: L.moe_swiglu_waves(  # noqa: E731
+        ctypes.byref(sh), 128, *a, ws, None, copy, side, ev, n)
+    assert waves(FAKE, None, None, 0) == ARG
+    assert waves(None, FAKE, evs, 6) == ARG
+    holes = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
+    assert waves(FAKE, None, holes, 7) == ARG

@@ -147,8 +147,8 @@ def test_graph_replay_exchange_and_regroup():
 
 
 def test_graph_replay_swiglu_chains():
-    """The SwiGLU FFN forks its odd-id experts onto the library's side stream
-    and joins them back: captured, the fork and join become graph edges."""
+    """The SwiGLU FFN forks its odd-id experts onto the caller's side stream and
+    joins them back: captured, the fork and join become graph edges."""
     wl = synth.Workload("ffn", T=1000, H=256, dtype="bf16", E=16, k=2, R=1, W=1,
                         routing="zipf0.5", expert="swiglu", I=192, seed=3)
     print(f"[graph] swiglu: T={wl.T} H={wl.H} E={wl.E} I={wl.I} k={wl.k}", flush=True)
@@ -161,14 +161,54 @@ def test_graph_replay_swiglu_chains():
     ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
                      device=DEV)
     eo2, ws2 = torch.empty_like(eo), torch.empty_like(ws)
+    chains, chains2 = moe.Chains(), moe.Chains()
 
     def step():
         moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
-                          gu, dn, expert_out=eo, workspace=ws)
+                          gu, dn, expert_out=eo, workspace=ws, chains=chains)
 
-    def noise():  # the same FFN eagerly, through the same side stream
+    def noise():  # the same FFN eagerly, through another side stream
         moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
-                          gu, dn, expert_out=eo2, workspace=ws2)
+                          gu, dn, expert_out=eo2, workspace=ws2, chains=chains2)
 
     _replays_match(step, [eo], noise)
     assert torch.equal(eo2.view(torch.uint8), eo.view(torch.uint8))
+
+
+def test_graph_swiglu_first_call_captured():
+    """The very first call with a fresh side stream and events is made inside
+    a capture (nothing in the library is set up on first use): the replays
+    equal an eager run made afterwards, bit for bit."""
+    wl = synth.Workload("ffn", T=700, H=256, dtype="bf16", E=8, k=2, R=1, W=1,
+                        routing="zipf0.5", expert="swiglu", I=128, seed=9)
+    print(f"[graph] swiglu first call: T={wl.T} H={wl.H} E={wl.E} I={wl.I}", flush=True)
+    shape = shape_of(wl)
+    x = dev(synth.hidden(wl))
+    gu, dn = (dev(a) for a in synth.swiglu_weights(wl, std=0.1))
+    idx, _ = moe.route(dev(synth.logits(wl)), wl.k)
+    out = moe.dispatch(x, idx, wl.E, wl.R, wl.W)
+    eo = torch.empty_like(out["send_buf"])
+    ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
+                     device=DEV)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        chains = moe.Chains()  # created outside the capture, used first inside it
+    cap.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"],
+                              shape, gu, dn, expert_out=eo, workspace=ws, chains=chains)
+    torch.cuda.synchronize()
+    ref = moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                            gu, dn, chains=moe.Chains())
+    torch.cuda.synchronize()
+    n = int(out["expert_counts"].sum().item())
+    for rep in range(3):
+        eo.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(eo[:n].view(torch.uint8), ref[:n].view(torch.uint8)), rep

@@ -33,13 +33,18 @@ def test_matches_torch_float64():
     gu, dn = _weights(E, H, I, 1)
     rows = _rows(n, H, 2)
     re = np.arange(n) % E
-    o64, o16 = oracle.expert_swiglu_rows(rows, re, gu, dn)
+    o64, o16, gus = oracle.expert_swiglu_rows(rows, re, gu, dn, want_gu=True)
+    o64b, o16b = oracle.expert_swiglu_rows(rows, re, gu, dn)
+    assert np.array_equal(o64, o64b) and np.array_equal(o16, o16b)
     for r in range(n):
         e = re[r]
         s = torch.from_numpy(f64(rows[r]))
         Wg = torch.from_numpy(f64(gu[e, :I]))
         Wu = torch.from_numpy(f64(gu[e, I:]))
         Wd = torch.from_numpy(f64(dn[e]))
+        # the pre-activation sums the oracle reports are the two projections
+        np.testing.assert_allclose(gus[r, :I], (Wg @ s).numpy(), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(gus[r, I:], (Wu @ s).numpy(), rtol=1e-13, atol=1e-13)
         h = torch.nn.functional.silu(Wg @ s) * (Wu @ s)
         h = h.to(torch.float32).to(torch.bfloat16).to(torch.float64)  # bf16 intermediate
         ref = (Wd @ h).numpy()
