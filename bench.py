@@ -2,24 +2,29 @@
 """Benchmark of the one-GPU MoE routing path on an MI355X.
 
 One step = the whole path on one batch of synthetic input, inputs already in
-HBM: route (top-k gating) -> dispatch index (counts, offsets, positions) ->
-dispatch copy (permute into the send buffer) -> experts (identity-scaled, or
-the SwiGLU FFN on MFMA for the local-layer workload) -> combine -> skew
-statistics of S. By default route, index and statistics go through the fused
-entry point moe_route_index (the counting pass inside the routing kernel, the
-statistics from one extra block of the placing kernel: 5 kernels a step);
---unfused calls moe_route, moe_dispatch_index and moe_stats instead (7
-kernels). Every step runs in the library's HIP kernels on torch's current
-stream; torch only provides memory and the stream.
+HBM: route (top-k gating) -> dispatch index (counting pass, offsets,
+positions) -> dispatch copy (permute into the send buffer) -> experts
+(identity-scaled, or the SwiGLU FFN on MFMA for the local-layer workload) ->
+combine -> skew statistics of S (moe_route, moe_dispatch_index,
+moe_dispatch_copy, the expert call, moe_combine, moe_stats: 7 kernels). With
+--fused, route, index and statistics go through moe_route_index instead (the
+counting pass inside the routing kernel, the statistics from one extra block of
+the placing kernel: 5 kernels); the counting pass then sits outside the
+dispatch+combine region. Every step runs in the library's HIP kernels on
+torch's current stream; torch only provides memory and the stream.
 
-Prints ONE JSON line. `value` is whole-step tokens/s over K timed steps (wall
-clock, bracketed by synchronisations, no instrumentation). A second K-step
-loop, right after it, times every stage on the GPU itself: the library's timing
-hook launches the stage's kernels with start/stop events (extended launches on
-the launch stream), so a stage's time is its kernels' execution time. The
-dominant kernel's algorithmic bytes (or flops) over its average duration is
-`roofline`. A third loop repeats the instrumented steps after evicting the
-256 MB Infinity Cache (a 512 MiB scratch write) for cold-cache stage times.
+Prints ONE JSON line. `value` is the metric: dispatch+combine tokens/s, i.e. T
+over the median (over steps) of the summed execution times of the dispatch
+kernels (count, place, copy) and the combine kernel. Those come from an
+instrumented K-step loop: the library's timing hook launches every kernel with
+start/stop events (extended launches on the launch stream), so a stage's time
+is its kernels' execution time. `ms_per_step` is the wall clock of K
+uninstrumented whole steps (bracketed by synchronisations); a third loop runs
+only the dispatch and combine calls K times for their wall clock. The dominant
+dispatch/combine kernel's algorithmic bytes over its average duration is
+`roofline` (the expert stage, outside the metric, has its own record). A
+further loop repeats the instrumented steps after evicting the 256 MB Infinity
+Cache (a 512 MiB scratch write) for cold-cache stage times.
 
 --vsrc runs the exchange of R ranks emulated on the one device instead: every
 source shard's dispatch and the count exchange, the block-transpose all-to-all,
@@ -46,6 +51,9 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 STAGES = ("route", "dispatch_index", "dispatch_copy", "exchange", "regroup", "expert", "combine",
           "stats")
+# The metric's region: counts, offsets, positions, the permute copy (and, for
+# the emulated exchange, the exchange and regroup copies), and the combine.
+DC_STAGES = ("dispatch_index", "dispatch_copy", "exchange", "regroup", "combine")
 
 
 class HipEvents:
@@ -82,14 +90,15 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="zipf")
+    ap.add_argument("--workload", default="dirichlet_waves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-evicted loop")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--graph", action="store_true",
                     help="also time K steps replayed from one captured HIP graph")
-    ap.add_argument("--unfused", action="store_true",
-                    help="separate route / dispatch_index / stats calls (7 kernels a step)")
+    ap.add_argument("--fused", action="store_true",
+                    help="route, index and statistics through moe_route_index (5 kernels a "
+                         "step; the counting pass then runs inside the routing kernel)")
     ap.add_argument("--wave-sweep", action="store_true",
                     help="local layer: wave-pipelined dispatch + FFN for every W dividing L, "
                          "two streams vs one; T(W) and the fitted wave model")
@@ -177,12 +186,32 @@ def ffn_flops(wl) -> int:
     return 6 * wl.T * wl.k * wl.H * wl.I  # gate/up (2*2I*H) + down (2*H*I) per row
 
 
+def host_description() -> dict:
+    """CPU model and the core counts of the host the oracle runs on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) -> dict:
-    """The oracle, as it stands, timed on the host (single thread)."""
+    """The oracle, as it stands, timed on the host (single thread), in the
+    metric's unit where the path allows it: dispatch + combine tokens/s."""
     import numpy as np
 
     import oracle
 
+    host = host_description()
     if vsrc:
         passes, t_used = 0, 0.0
         while passes < 2 or t_used < seconds:
@@ -197,19 +226,26 @@ def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) ->
                   f"(C steps, numpy block moves): route, per-source dispatch, exchange, regroup, "
                   f"expert, ungroup, exchange back, combine, stats")
     elif ffn_weights is None:
+        # routing and the expert rows once, untimed (outside the metric); then
+        # whole passes of the oracle's dispatch (counts, offsets, positions,
+        # row copy) and combine over all T tokens
+        idx, w = oracle.route(logits, wl.k)
+        d = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
+        out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
+        del d
         passes, t_used = 0, 0.0
         while passes < 2 or t_used < seconds:
             t0 = time.perf_counter()
-            idx, w = oracle.route(logits, wl.k)
             d = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
-            out = oracle.expert_scale(d["send_buf"], d["expert_offsets"], d["expert_counts"])
             oracle.combine_f64(out, w, d["pos"], wl.T)
-            oracle.stats(d["expert_counts"], wl.R)
             t_used += time.perf_counter() - t0
             passes += 1
+            del d
         tokens = wl.T * passes
-        sample = (f"{passes} full passes of the {wl.name} workload (T={wl.T}) through the "
-                  f"single-threaded C oracle: route, dispatch, expert, combine (fp64), stats")
+        sample = (f"{passes} whole passes of the {wl.name} workload (T={wl.T}) through the "
+                  f"single-threaded C oracle's dispatch (counts, offsets, positions, row copy) "
+                  f"and combine (fp64); routing and expert rows computed once beforehand, "
+                  f"untimed")
     else:
         gu, dn = ffn_weights
         tokens, t_used = 0, 0.0
@@ -226,7 +262,8 @@ def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) ->
         sample = (f"{tokens} tokens of the {wl.name} workload one at a time through the "
                   f"single-threaded C oracle: route, SwiGLU FFN of the k picks (fp64), combine")
     return {"value": round(tokens / t_used, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}; {t_used:.1f} s on {platform.processor() or platform.machine()}"}
+            "sample": f"{sample}; {t_used:.1f} s on one thread of {host['cpu_model']} "
+                      f"({host['nproc']} usable cores)", "host": host}
 
 
 def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
@@ -254,10 +291,12 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
         ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
                          device=dev)
 
+        chains = moe.Chains(n_events=moe.swiglu_waves_events(W))
+
         def step(two):
             moe.route_index(logits, shape, buf, idx, wt)
             moe.swiglu_waves(x, buf, shape, gu, dn, expert_out=eo, workspace=ws,
-                             copy_stream=side if two else None)
+                             copy_stream=side if two else None, chains=chains)
             moe.combine(eo, wt, buf["pos"], shape, y=y)
 
         row = []
@@ -332,8 +371,8 @@ def make_context(wl, moe, torch, np):
 # the counts the Dirichlet fit reads, the step's description and extra config.
 
 def path_default(c, args):
-    """route + index (+ stats) + copy + experts + combine: moe_route_index (5
-    kernels a step) or, with --unfused, separate calls (7)."""
+    """route + index + copy + experts + combine + stats: separate calls (7
+    kernels a step) or, with --fused, moe_route_index (5)."""
     moe, L, P, shp, s = c.moe, c.L, c.P, c.shp, c.stream
     buf = moe.alloc_dispatch(c.shape, c.dev)
     expert_out = torch_empty_like(c, buf["send_buf"])
@@ -344,9 +383,11 @@ def path_default(c, args):
         gu, dn = c.to_dev(c.ffn_np[0]), c.to_dev(c.ffn_np[1])
         ws = c.torch.empty((moe.expert_swiglu_workspace_bytes(c.shape, c.wl.I),),
                            dtype=c.torch.uint8, device=c.dev)
-        c.keep = (gu, dn, ws)
+        chains = moe.Chains()  # the second chain of experts: a side stream and two events
+        c.keep = (gu, dn, ws, chains)
         a = (shp, c.wl.I, P(buf["send_buf"]), P(buf["expert_offsets"]), P(buf["expert_counts"]),
-             P(gu), P(dn), P(expert_out), P(ws), ws.numel(), s)
+             P(gu), P(dn), P(expert_out), P(ws), ws.numel(), s, chains.side_ptr(),
+             chains.event_ptr(0), chains.event_ptr(1))
         # the two GEMMs of each chain of experts (the chains run on streams of
         # their own, so the stage is timed as the span of its kernels). The
         # count probe runs before any index stage has filled the tables: empty
@@ -363,7 +404,7 @@ def path_default(c, args):
         expert = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
                                        P(buf["expert_counts"]), P(expert_out), s),
                   [("expert", "expert_scale_kernel")])
-    if args.unfused:
+    if not args.fused:
         calls = [
             (L.moe_route, (P(c.logits), c.T, c.E, c.k, P(c.topk_idx), P(c.topk_w), s),
              [("route", "route_kernel")]),
@@ -371,7 +412,7 @@ def path_default(c, args):
                                     buf["workspace"].numel(), s),
              [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel")]),
         ]
-        desc = "route+dispatch_index+stats (separate calls)+dispatch_copy+expert+combine"
+        desc = "route+dispatch_index(count,place)+dispatch_copy+expert+combine+stats"
     else:
         calls = [
             (L.moe_route_index, (shp, P(c.logits), P(c.topk_idx), P(c.topk_w), *index_args,
@@ -386,7 +427,7 @@ def path_default(c, args):
         (L.moe_combine, (shp, P(expert_out), P(c.topk_w), P(buf["pos"]), P(c.y), s),
          [("combine", "combine_kernel")]),
     ]
-    if args.unfused:
+    if not args.fused:
         calls.append((L.moe_stats, (P(buf["expert_counts"]), c.E, c.R, P(c.stats_raw), s),
                       [("stats", "stats_kernel")]))
     return SimpleNamespace(calls=calls, nbytes=lambda: algorithmic_bytes(c.wl),
@@ -631,9 +672,11 @@ class StepRunner:
         return time.perf_counter() - t0
 
 
-def plain_copy_gbs(torch, dev) -> float:
-    """The HIP runtime's own copy of 1 GiB (beyond the Infinity Cache): a
-    reference streaming rate on this machine, read + write."""
+def plain_rates(torch, dev) -> dict:
+    """Reference streaming rates on this machine, with buffers beyond the Infinity
+    Cache: the HIP runtime's own 1 GiB device copy (read + write) and torch's
+    sum over 1 GiB of fp32 (read-only; its counters also check the scale of the
+    read-byte counter on a second kernel of known bytes)."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -643,7 +686,18 @@ def plain_copy_gbs(torch, dev) -> float:
         dst.copy_(src)
     cb.record()
     torch.cuda.synchronize()
-    return 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    copy_gbs = 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    del dst
+    f = src.view(torch.float32)
+    acc = f.sum()
+    ca.record()
+    for _ in range(5):
+        acc = f.sum()
+    cb.record()
+    torch.cuda.synchronize()
+    read_gbs = (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    del acc
+    return {"plain_copy_GBs": round(copy_gbs, 1), "plain_read_GBs": round(read_gbs, 1)}
 
 
 def dirichlet_fit(moe, torch, counts, dev) -> dict:
@@ -745,8 +799,23 @@ def main() -> int:
     kernel_us = {kn: round(v * 1e3, 2) for kn, v in run.kernel_ms.items()}
     nbytes = path.nbytes()
 
+    # ---- timed region 3: only the calls whose kernels all belong to dispatch
+    # or combine, K times -> their wall clock (launch gaps included)
+    dc_calls = [cl for cl in path.calls if cl[2] and all(st in DC_STAGES for st, _ in cl[2])]
+    dc_wall = None
+    if dc_calls:
+        dc_run = StepRunner(c, dc_calls)
+        for _ in range(max(1, args.warmup // 2)):
+            dc_run.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            dc_run.step()
+        torch.cuda.synchronize()
+        dc_wall = time.perf_counter() - t0
+
     graph_wall = run.graph_wall(K) if args.graph else None
-    copy_gbs = plain_copy_gbs(torch, c.dev)
+    rates = plain_rates(torch, c.dev)
 
     cold_ms = None
     if not args.no_cold:
@@ -780,35 +849,42 @@ def main() -> int:
             rep["expert"]["frac_mfma_bf16_peak"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
         return rep
 
-    # Dominant single-kernel stage (HBM-bound kernels; the FFN is reported as MFMA-bound).
-    single = [n for n in ("route", "dispatch_copy", "exchange", "regroup", "expert", "combine",
-                          "stats")
-              if n in stages and not (swiglu and n == "expert")]
-    dom = max(single, key=lambda n: stage_ms[n])
-    # per launch: a stage may launch its kernel more than once a step (the
-    # exchange and the regroup run forward and back), bytes and time both scale
-    nl = launches_of[dom]
-    roofline = {"bound": "hbm", "kernel": kernel_of[dom],
-                "achieved": round(gbs(dom, stage_ms[dom]), 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs(dom, stage_ms[dom]) / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(wl.name, kernel_of[dom]),
-                "bytes_per_launch": nbytes[dom] // nl, "launches_per_step": nl,
-                "avg_us": round(stage_ms[dom] * 1e3 / nl, 2)}
-    if swiglu and stage_ms["expert"] > stage_ms[dom]:
-        tf = ffn_flops(wl) / (stage_ms["expert"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": kernel_of["expert"], "achieved": round(tf, 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": stored_traffic(wl.name, kernel_of["expert"]),
-                    "flops_per_launch": ffn_flops(wl), "avg_us": round(stage_ms["expert"] * 1e3, 2)}
-
-    dc_keys = tuple(n for n in ("dispatch_index", "dispatch_copy", "exchange", "regroup",
-                                "combine") if n in stage_ms)
+    dc_keys = tuple(n for n in DC_STAGES if n in stage_ms)
     dc_ms = sum(stage_ms[n] for n in dc_keys)
+    dc_med = StepRunner.median_of(warm_steps, dc_keys)
     dc_bytes = sum(nbytes[n] for n in dc_keys)
+
+    def roofline_hbm(n, ms):
+        # per launch: a stage may launch its kernel more than once a step (the
+        # exchange and the regroup run forward and back), bytes and time both scale
+        nl = launches_of[n]
+        return {"bound": "hbm", "kernel": kernel_of[n], "achieved": round(gbs(n, ms[n]), 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs(n, ms[n]) / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic(wl.name, kernel_of[n]),
+                "bytes_per_launch": nbytes[n] // nl, "launches_per_step": nl,
+                "avg_us": round(ms[n] * 1e3 / nl, 2)}
+
+    # The dominant single-kernel stage of the metric's region (the row copies;
+    # the index stage is a few small kernels): the headline roofline.
+    single = [n for n in ("dispatch_copy", "exchange", "regroup", "combine") if n in stages]
+    dom = max(single, key=lambda n: stage_ms[n])
+    roofline = roofline_hbm(dom, stage_ms)
+    # The expert stage sits between dispatch and combine but outside the metric.
+    if swiglu:
+        tf = ffn_flops(wl) / (stage_ms["expert"] * 1e-3) / 1e12
+        expert_roofline = {"bound": "mfma", "kernel": kernel_of["expert"],
+                           "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "traffic": stored_traffic(wl.name, kernel_of["expert"]),
+                           "flops_per_call": ffn_flops(wl),
+                           "avg_us": round(stage_ms["expert"] * 1e3, 2)}
+    else:
+        expert_roofline = roofline_hbm("expert", stage_ms)
+
     result = {
         "metric": METRIC,
-        "value": round(T * K / wall, 1),
+        "value": round(T / (dc_med * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -825,34 +901,42 @@ def main() -> int:
                    "expert": wl.expert, "step": path.desc,
                    "kernels_per_step": sum(len(cl[2]) for cl in path.calls),
                    **({"I": wl.I} if swiglu else {}), **path.config()},
+        "step_tokens_per_s": round(T * K / wall, 1),
         "dispatch_combine": {
-            "us": round(dc_ms * 1e3, 2),
-            "median_us": round(StepRunner.median_of(warm_steps, dc_keys) * 1e3, 2),
-            "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
-            "GB/s": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "median_us": round(dc_med * 1e3, 2),
+            "mean_us": round(dc_ms * 1e3, 2),
+            "tokens_per_s": round(T / (dc_med * 1e-3), 1),
+            "GB/s": round(dc_bytes / (dc_med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(dc_bytes / (dc_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes": dc_bytes,
             "kernels": "+".join(kernel_of[n] for n in dc_keys),
+            "timing": "median over the instrumented steps of the summed kernel execution times",
+            **({"wall_us": round(dc_wall * 1e6 / K, 2),
+                "wall_calls": "+".join(cl[0].__name__ for cl in dc_calls),
+                "wall_frac_hbm_peak": round(
+                    sum(nbytes[st] for st in {g for cl in dc_calls for g, _ in cl[2]})
+                    / (dc_wall / K) / 1e9 / HBM_PEAK_GBS, 4)}
+               if dc_wall is not None else {}),
         },
         "roofline": roofline,
+        "expert_roofline": expert_roofline,
         "stages": stage_report(stage_ms),
         "kernel_us_per_launch": kernel_us,
         "stage_timing": "sum of the execution times of each stage's kernels, from start/stop "
                         "events recorded by the library's extended launches (instrumented loop "
                         f"of {K} steps, {wall_instr * 1e3 / K:.4f} ms/step wall)",
-        "plain_copy_GBs": round(copy_gbs, 1),
+        **rates,
         "dirichlet_alpha": alpha_fit,
     }
     if graph_wall is not None:
         result["graph_replay"] = {"ms_per_step": round(graph_wall * 1e3 / K, 4),
                                   "tokens_per_s": round(T * K / graph_wall, 1)}
     if cold_ms is not None:
-        cdc = sum(cold_ms[n] for n in dc_keys)
+        cdc = StepRunner.median_of(cold_steps, dc_keys)
         result["cold_cache"] = {
             "stages": stage_report(cold_ms),
-            "dispatch_combine": {"us": round(cdc * 1e3, 2),
-                                 "median_us": round(StepRunner.median_of(cold_steps, dc_keys) * 1e3,
-                                                    2),
+            "dispatch_combine": {"median_us": round(cdc * 1e3, 2),
+                                 "mean_us": round(sum(cold_ms[n] for n in dc_keys) * 1e3, 2),
                                  "tokens_per_s": round(T / (cdc * 1e-3), 1),
                                  "GB/s": round(dc_bytes / (cdc * 1e-3) / 1e9, 1),
                                  "frac_hbm_peak": round(dc_bytes / (cdc * 1e-3) / 1e9
