@@ -56,6 +56,9 @@ SIGNATURES = {
     "moe_dispatch_copy": ([_shp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_dispatch_noalloc": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+                             ctypes.c_int),
+    "moe_noalloc_scratch_bytes": ([], ctypes.c_size_t),
     "moe_expert_scale": ([_shp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_scale_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_expert_capacity": ([_i32, ctypes.c_double, _i32, _i32], ctypes.c_int32),
@@ -270,6 +273,24 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, W: int,
         _ptr(out["row_token"]), _ptr(out["workspace"]), out["workspace"].numel(), _stream()),
         "moe_dispatch")
     return out
+
+
+def dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, shape: Shape, out: dict) -> dict:
+    """moe_dispatch without a workspace: the library's static per-device array
+    holds the index stage's histograms. `out` holds the output buffers (its
+    "workspace" entry, if any, is not used). Calls overlapping on one device
+    race on that array."""
+    sh = shape.c()
+    _check(lib().moe_dispatch_noalloc(
+        ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(out["send_buf"]),
+        _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
+        _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]), _ptr(out["pos"]),
+        _ptr(out["row_token"]), _stream()), "moe_dispatch_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().moe_noalloc_scratch_bytes())
 
 
 # ------------------------------------------------------- capacity-factor path

@@ -5,6 +5,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -51,18 +52,29 @@ size_t workspace_bytes(const moe_shape* sh) {
   return size_t((bytes + 255) / 256 * 256);
 }
 
+// The index outputs (everything but the workspace).
+int check_index_ptrs(const moe_shape* sh, const int32_t* topk_idx, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                     int32_t* wave_offsets, int32_t* pos, int32_t* row_token) {
+  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets || !wave_offsets)
+    return MOE_ERR_ARG;
+  if (sh->T > 0 && (!topk_idx || !pos || !row_token)) return MOE_ERR_ARG;
+  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        wave_offsets, pos, row_token};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
 int check_index_args(const moe_shape* sh, const int32_t* topk_idx, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
                      int32_t* wave_offsets, int32_t* pos, int32_t* row_token, void* workspace,
                      size_t workspace_bytes_given) {
-  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets || !wave_offsets ||
-      !workspace)
-    return MOE_ERR_ARG;
-  if (sh->T > 0 && (!topk_idx || !pos || !row_token)) return MOE_ERR_ARG;
-  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
-                        wave_offsets, pos, row_token, workspace};
-  for (const void* p : ptrs)
-    if (!aligned(p, 4)) return MOE_ERR_ALIGN;
+  const int st = check_index_ptrs(sh, topk_idx, expert_counts, expert_offsets, rank_counts,
+                                  rank_offsets, wave_offsets, pos, row_token);
+  if (st != MOE_OK) return st;
+  if (!workspace) return MOE_ERR_ARG;
+  if (!aligned(workspace, 4)) return MOE_ERR_ALIGN;
   if (workspace_bytes_given < workspace_bytes(sh)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
@@ -547,6 +559,72 @@ int moe_vsrc_regroup(const moe_shape* shape, int32_t direction, const void* in, 
       in, out, row_bytes, int64_t(shape->T) * shape->k, shape->E, shape->R, shape->W, src_counts,
       recv_offsets, expert_offsets, static_cast<int32_t*>(workspace), direction == 1,
       as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free dispatch
+// moe_dispatch_noalloc keeps the index stage's histogram rows in a file-scope
+// device array instead of a caller workspace, for callers that cannot
+// allocate. In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device (with that device
+// current) and only that address is handed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(256) << 10;  // the index workspace's largest size
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of this device's copy of `scratch` (looked up on the
+// first call made with the device current), or null on failure.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int moe_dispatch_noalloc(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                         void* send_buf, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
+                         int32_t* pos, int32_t* row_token, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  st = check_index_ptrs(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                        rank_offsets, wave_offsets, pos, row_token);
+  if (st != MOE_OK) return st;
+  st = check_copy_args(shape, x, pos, send_buf);
+  if (st != MOE_OK) return st;
+  // the count pass writes every row of its histogram, so nothing needs clearing
+  const int64_t npicks = int64_t(shape->T) * shape->k;
+  const int64_t need = moe::num_chunks(npicks, shape->E) * int64_t(shape->E) * 4;
+  if (need > int64_t(kScratchBytes)) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_DEVICE;
+  hipStream_t s = as_stream(stream);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  st = status_of(moe::launch_count(topk_idx, npicks, shape->E, hist, s));
+  if (st != MOE_OK) return st;
+  st = status_of(moe::launch_place(topk_idx, npicks, shape->k, shape->E, shape->R, shape->W,
+                                   hist, expert_counts, expert_offsets, rank_counts,
+                                   rank_offsets, wave_offsets, pos, row_token, s));
+  if (st != MOE_OK) return st;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, npicks, send_buf, s));
 }
 
 }  // extern "C"

@@ -157,6 +157,29 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                  int32_t* row_token, void* workspace, size_t workspace_bytes,
                  moe_stream_t stream);
 
+/* moe_dispatch without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The index stage's per-chunk histograms live in a
+ * static device array of moe_noalloc_scratch_bytes() = 256 KiB that the
+ * library holds on each device it runs on until the process ends (its device
+ * address is looked up on the first call made with that device current).
+ * Same arguments, results and launches as moe_dispatch; nothing is allocated
+ * or freed. Every call on one device shares that device's array: calls that
+ * overlap on one device (concurrent streams, or several host threads) race
+ * and must be serialised by the caller. The array's contents need no
+ * initialisation (each call writes every histogram row it reads).
+ * Errors: as moe_dispatch; MOE_ERR_WORKSPACE when the shape's histogram
+ * (chunks x E int32) exceeds the array (no valid shape does: at most
+ * 65536 / pow2(E) chunks of E counts); MOE_ERR_DEVICE when the array's device
+ * address cannot be found or a launch fails. */
+int moe_dispatch_noalloc(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                         void* send_buf, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* wave_offsets,
+                         int32_t* pos, int32_t* row_token, moe_stream_t stream);
+
+/* Bytes of the static device array moe_dispatch_noalloc uses (host-only). */
+size_t moe_noalloc_scratch_bytes(void);
+
 /* Expert capacity (MoE systems survey section 1.2 item 2, eq. (3)): rows per
  * expert for capacity factor f, ceil(k * f * T / E) evaluated in double in
  * that order. Host-only, pure; -1 for k < 1, T < 0, E < 1, f < 0 (or NaN) or a

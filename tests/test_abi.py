@@ -264,3 +264,19 @@ def test_swiglu_waves_validation():
     assert waves(None, FAKE, evs, 6) == ARG
     holes = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
     assert waves(FAKE, None, holes, 7) == ARG
+
+
+def test_noalloc_dispatch_validation():
+    L = moe.lib()
+    assert L.moe_noalloc_scratch_bytes() == 256 << 10
+    sh = _shape()
+    args = [FAKE] * 10  # x, topk_idx, send_buf, 7 index outputs (a valid call is never made)
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert L.moe_dispatch_noalloc(ctypes.byref(sh), *a, None) == ARG, i
+    a = list(args)
+    a[0] = ctypes.c_void_p((1 << 20) + 4)  # x not 16-byte aligned
+    assert L.moe_dispatch_noalloc(ctypes.byref(sh), *a, None) == ALIGN
+    assert L.moe_dispatch_noalloc(ctypes.byref(_shape(E=9)), *args, None) == ARG
+    assert L.moe_dispatch_noalloc(None, *args, None) == ARG
