@@ -20,7 +20,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
+# MOE_ROUTE_LIB names another build of the same library (the host-sanitized
+# build the CPU sanitizer run loads); there is no fallback when it is missing.
+LIB_PATH = os.environ.get("MOE_ROUTE_LIB") or os.path.join(_HERE, "libmoe_route.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}

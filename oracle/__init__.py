@@ -18,7 +18,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c (the sanitizer run's); build()
+# always writes the default one.
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB = os.environ.get("ORACLE_LIB") or _DEFAULT_LIB
 
 F32, BF16 = 0, 1
 
@@ -46,15 +49,21 @@ class Stats(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (plain C11, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C11, no FMA
+    contraction); with sanitize, an AddressSanitizer + UBSan build (-O1 -g,
+    aborting on the first report) at `out` instead."""
+    target = out or (_DEFAULT_LIB if not sanitize else _DEFAULT_LIB.replace(".so", "_san.so"))
+    if force or not os.path.exists(target):
+        tmp = target + ".tmp"
+        flags = ["-O2"] if not sanitize else [
+            "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=all"]
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+            ["gcc", *flags, "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
              _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 _lib_handle = None
@@ -64,6 +73,8 @@ def lib() -> ctypes.CDLL:
     global _lib_handle
     if _lib_handle is None:
         if not os.path.exists(_LIB):
+            if _LIB != _DEFAULT_LIB:
+                raise RuntimeError(f"ORACLE_LIB={_LIB} does not exist")
             build(force=True)
         L = ctypes.CDLL(_LIB)
         L.oracle_route.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i32p, _f64p]

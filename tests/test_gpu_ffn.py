@@ -111,8 +111,8 @@ def test_swiglu_validation():
 
 def test_local_layer_full_size_sampled():
     """The local-layer workload at full size (T=8192, E=16, H=4096, I=1408,
-    weights N(0, 0.02^2)): FFN rows sampled across every expert, and combined
-    tokens end to end."""
+    weights N(0, 0.02^2)): FFN rows at both edges of every m-tile of every
+    expert plus a random sample, and combined tokens end to end."""
     wl = synth.WORKLOADS["local_layer"]
     print(f"[ffn] local_layer full T={wl.T} H={wl.H} E={wl.E} I={wl.I}", flush=True)
     logits, x, gu, dn, idx_o, w_o, ec, eo, pos, rt = _ffn_setup(wl, std=0.02)
@@ -127,9 +127,14 @@ def test_local_layer_full_size_sampled():
     np.testing.assert_array_equal(host(out["pos"]), pos)
 
     g = np.random.default_rng(7)
-    firsts = eo[ec > 0]
-    lasts = (eo + ec - 1)[ec > 0]
-    rows = np.unique(np.concatenate([firsts, lasts, g.integers(0, int(ec.sum()), 24)]))
+    # the first and last row of every 256-row m-tile of every expert (the
+    # kernel's tile edges, partial last tiles included) and a random sample
+    edges = []
+    for e in np.nonzero(ec > 0)[0]:
+        starts = np.arange(eo[e], eo[e] + ec[e], 256)
+        edges += [starts, np.minimum(starts + 255, eo[e] + ec[e] - 1)]
+    rows = np.unique(np.concatenate(edges + [g.integers(0, int(ec.sum()), 24)]))
+    print(f"[ffn] local_layer full: {len(rows)} rows checked", flush=True)
     got = host(eo_gpu[torch.from_numpy(rows).to(DEV)])
     _check_rows(got, x[rt[rows]], _row_expert(ec, eo, rows), gu, dn, tight_atol=1e-3)
 

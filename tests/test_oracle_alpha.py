@@ -10,6 +10,7 @@ import pytest
 from scipy.special import digamma, gammaln
 
 import oracle
+import synth
 
 
 def _counts(seed, E, N, alpha):
@@ -66,3 +67,28 @@ def test_permutation_invariant():
     a = oracle.dirichlet_alpha(c)
     b = oracle.dirichlet_alpha(c[g.permutation(32)])
     assert abs(a - b) <= 1e-12 * a
+
+
+def test_generator_alpha_and_routing_sharpening():
+    """The dirichlet_waves generator draws p ~ Dirichlet(0.3) over E = 256: counts
+    drawn straight from Multinomial(T k, p) fit alpha close to 0.3 (mean over six
+    seeds within 15%). The workload's routed counts (top-8 of N(0,1) + ln p) fit
+    a much smaller alpha (about 0.09): an expert whose ln p lies far below the
+    8th largest is almost never lifted into the top 8 by unit noise, and the
+    largest ones are picked by almost every token, so fewer experts receive
+    picks and the counts are more uneven than p itself."""
+    wl = synth.WORKLOADS["dirichlet_waves"]
+    mult, routed = [], []
+    for seed in range(6):
+        p = np.exp(synth._dirichlet_log_bias(wl.E, 0.3, seed).astype(np.float64))
+        p /= p.sum()
+        c = np.random.default_rng(100 + seed).multinomial(wl.T * wl.k, p).astype(np.int32)
+        idx, _ = oracle.route(synth.logits(wl.with_(seed=seed)), wl.k)
+        ec, _ = oracle.counts(idx, wl.E, wl.R, wl.W)
+        a_m, a_r = oracle.dirichlet_alpha(c), oracle.dirichlet_alpha(ec)
+        mult.append(a_m)
+        routed.append(a_r)
+        assert a_r < 0.5 * a_m
+        assert (ec > 0).sum() < (c > 0).sum()
+    assert abs(np.mean(mult) - 0.3) < 0.15 * 0.3
+    assert 0.05 < np.mean(routed) < 0.15
