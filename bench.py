@@ -5,13 +5,15 @@ One step = the whole path on one batch of synthetic input, inputs already in
 HBM: route (top-k gating) -> dispatch index (counting pass, offsets,
 positions) -> dispatch copy (permute into the send buffer) -> experts
 (identity-scaled, or the SwiGLU FFN on MFMA for the local-layer workload) ->
-combine -> skew statistics of S (moe_route, moe_dispatch_index,
-moe_dispatch_copy, the expert call, moe_combine, moe_stats: 7 kernels). With
---fused, route, index and statistics go through moe_route_index instead (the
-counting pass inside the routing kernel, the statistics from one extra block of
-the placing kernel: 5 kernels); the counting pass then sits outside the
-dispatch+combine region. Every step runs in the library's HIP kernels on
-torch's current stream; torch only provides memory and the stream.
+combine -> skew statistics of S (moe_route, moe_dispatch, the expert call,
+moe_combine, moe_stats: 7 kernels a step, or 5 when all T*k picks fit one
+1024-pick batch, the decode regime, where moe_dispatch is one launch). With
+--fused, routing, index, statistics and the dispatch copy go through
+moe_route_dispatch instead (2 launches in the decode regime, else the routing
+kernel with the counting pass, the placing kernel with the statistics block
+and the copy; the counting pass then sits outside the dispatch+combine
+region). Every step runs in the library's HIP kernels on torch's current
+stream; torch only provides memory and the stream.
 
 Prints ONE JSON line. `value` is the metric: dispatch+combine tokens/s, i.e. T
 over the median (over steps) of the summed execution times of the dispatch
@@ -49,11 +51,12 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine tokens/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-STAGES = ("route", "dispatch_index", "dispatch_copy", "exchange", "regroup", "expert", "combine",
-          "stats")
+STAGES = ("route", "dispatch", "dispatch_index", "dispatch_copy", "exchange", "regroup", "expert",
+          "combine", "stats")
 # The metric's region: counts, offsets, positions, the permute copy (and, for
 # the emulated exchange, the exchange and regroup copies), and the combine.
-DC_STAGES = ("dispatch_index", "dispatch_copy", "exchange", "regroup", "combine")
+# "dispatch" is the one-launch form of index + copy (T*k <= 1024).
+DC_STAGES = ("dispatch", "dispatch_index", "dispatch_copy", "exchange", "regroup", "combine")
 
 
 class HipEvents:
@@ -97,8 +100,9 @@ def parse_args():
     ap.add_argument("--graph", action="store_true",
                     help="also time K steps replayed from one captured HIP graph")
     ap.add_argument("--fused", action="store_true",
-                    help="route, index and statistics through moe_route_index (5 kernels a "
-                         "step; the counting pass then runs inside the routing kernel)")
+                    help="route, index, statistics and the dispatch copy through "
+                         "moe_route_dispatch (two launches when T*k <= 1024, else three; the "
+                         "counting pass then runs inside the routing kernel)")
     ap.add_argument("--wave-sweep", action="store_true",
                     help="local layer: wave-pipelined dispatch + FFN for every W dividing L, "
                          "two streams vs one; T(W) and the fitted wave model")
@@ -125,6 +129,7 @@ def algorithmic_bytes(wl) -> dict:
         "expert": 2 * T * k * H * b,                             # rows in, rows out
         "combine": T * k * H * b + 8 * T * k + T * H * b,        # k rows, w + pos in; y out
     }
+    out["dispatch"] = out["dispatch_index"] + out["dispatch_copy"]
     if wl.expert == "swiglu":  # + the expert weights, read once
         out["expert"] += 3 * wl.E * wl.H * wl.I * 2
     return out
@@ -371,8 +376,9 @@ def make_context(wl, moe, torch, np):
 # the counts the Dirichlet fit reads, the step's description and extra config.
 
 def path_default(c, args):
-    """route + index + copy + experts + combine + stats: separate calls (7
-    kernels a step) or, with --fused, moe_route_index (5)."""
+    """route + dispatch (index + copy) + experts + combine + stats: separate
+    calls (7 kernels a step, 5 when T*k <= 1024) or, with --fused,
+    moe_route_dispatch (4 kernels a step when T*k <= 1024, else 5)."""
     moe, L, P, shp, s = c.moe, c.L, c.P, c.shp, c.stream
     buf = moe.alloc_dispatch(c.shape, c.dev)
     expert_out = torch_empty_like(c, buf["send_buf"])
@@ -404,25 +410,33 @@ def path_default(c, args):
         expert = (L.moe_expert_scale, (shp, P(buf["send_buf"]), P(buf["expert_offsets"]),
                                        P(buf["expert_counts"]), P(expert_out), s),
                   [("expert", "expert_scale_kernel")])
+    # index + copy: one launch when all picks fit one 1024-pick batch (decode)
+    one = 0 < c.T * c.k <= 1024 and c.E <= 1024
     if not args.fused:
         calls = [
             (L.moe_route, (P(c.logits), c.T, c.E, c.k, P(c.topk_idx), P(c.topk_w), s),
              [("route", "route_kernel")]),
-            (L.moe_dispatch_index, (shp, P(c.topk_idx), *index_args, P(buf["workspace"]),
-                                    buf["workspace"].numel(), s),
-             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel")]),
+            (L.moe_dispatch, (shp, P(c.x), P(c.topk_idx), P(buf["send_buf"]), *index_args,
+                              P(buf["workspace"]), buf["workspace"].numel(), s),
+             [("dispatch", "dispatch_small_kernel")] if one else
+             [("dispatch_index", "count_kernel"), ("dispatch_index", "place_kernel"),
+              ("dispatch_copy", "copy_kernel")]),
         ]
-        desc = "route+dispatch_index(count,place)+dispatch_copy+expert+combine+stats"
+        desc = ("route+dispatch(" + ("one launch" if one else "count,place,copy")
+                + ")+expert+combine+stats")
     else:
+        kernels = ([("route", "route_kernel"), ("dispatch", "dispatch_small_kernel(+stats block)")]
+                   if one else
+                   [("route", "route_count_kernel"), ("dispatch_index", "place_kernel(+stats block)"),
+                    ("dispatch_copy", "copy_kernel")])
         calls = [
-            (L.moe_route_index, (shp, P(c.logits), P(c.topk_idx), P(c.topk_w), *index_args,
-                                 P(c.stats_raw), P(buf["workspace"]), buf["workspace"].numel(), s),
-             [("route", "route_count_kernel"), ("dispatch_index", "place_kernel(+stats block)")]),
+            (L.moe_route_dispatch, (shp, P(c.logits), P(c.x), P(c.topk_idx), P(c.topk_w),
+                                    P(buf["send_buf"]), *index_args, P(c.stats_raw),
+                                    P(buf["workspace"]), buf["workspace"].numel(), s), kernels),
         ]
-        desc = "route+dispatch_index+stats (moe_route_index)+dispatch_copy+expert+combine"
+        desc = ("route+dispatch+stats (moe_route_dispatch: "
+                + ("two launches" if one else "three launches") + ")+expert+combine")
     calls += [
-        (L.moe_dispatch_copy, (shp, P(c.x), P(buf["pos"]), P(buf["send_buf"]), s),
-         [("dispatch_copy", "copy_kernel")]),
         expert,
         (L.moe_combine, (shp, P(expert_out), P(c.topk_w), P(buf["pos"]), P(c.y), s),
          [("combine", "combine_kernel")]),
@@ -867,7 +881,8 @@ def main() -> int:
 
     # The dominant single-kernel stage of the metric's region (the row copies;
     # the index stage is a few small kernels): the headline roofline.
-    single = [n for n in ("dispatch_copy", "exchange", "regroup", "combine") if n in stages]
+    single = [n for n in ("dispatch", "dispatch_copy", "exchange", "regroup", "combine")
+              if n in stages]
     dom = max(single, key=lambda n: stage_ms[n])
     roofline = roofline_hbm(dom, stage_ms)
     # The expert stage sits between dispatch and combine but outside the metric.

@@ -56,6 +56,8 @@ SIGNATURES = {
     "moe_route_index": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_dispatch_copy": ([_shp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_route_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_dispatch_noalloc": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -250,6 +252,21 @@ def route_index(logits: torch.Tensor, shape: Shape, out: dict, topk_idx: torch.T
         _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
         _ptr(out["wave_offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(stats_out),
         _ptr(out["workspace"]), out["workspace"].numel(), _stream()), "moe_route_index")
+    return out
+
+
+def route_dispatch(logits: torch.Tensor, x: torch.Tensor, shape: Shape, out: dict,
+                   topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                   stats: torch.Tensor | None = None) -> dict:
+    """Routing, index stage, optional statistics and the dispatch copy (one
+    launch when T*k <= 1024) into topk_idx / topk_w and the buffers of `out`."""
+    sh = shape.c()
+    _check(lib().moe_route_dispatch(
+        ctypes.byref(sh), _ptr(logits), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(out["send_buf"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["wave_offsets"]),
+        _ptr(out["pos"]), _ptr(out["row_token"]), _ptr(stats), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream()), "moe_route_dispatch")
     return out
 
 

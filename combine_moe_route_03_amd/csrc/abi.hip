@@ -212,6 +212,40 @@ int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_i
       wave_offsets, pos, row_token, stats, -1, s));
 }
 
+int moe_route_dispatch(const moe_shape* shape, const float* logits, const void* x,
+                       int32_t* topk_idx, float* topk_w, void* send_buf, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
+                       moe_stats_t* stats, void* workspace, size_t workspace_bytes_given,
+                       moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (int64_t(shape->T) * shape->E >= (int64_t(1) << 40)) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!logits || !topk_w)) return MOE_ERR_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_w, 4) || !aligned(stats, 8)) return MOE_ERR_ALIGN;
+  st = check_index_args(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
+                        rank_offsets, wave_offsets, pos, row_token, workspace,
+                        workspace_bytes_given);
+  if (st != MOE_OK) return st;
+  st = check_copy_args(shape, x, pos, send_buf);
+  if (st != MOE_OK) return st;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  if (moe::dispatch_one_launch(int64_t(shape->T) * shape->k, shape->E)) {
+    hipStream_t s = as_stream(stream);
+    st = status_of(moe::launch_route(logits, shape->T, shape->E, shape->k, topk_idx, topk_w, s));
+    if (st != MOE_OK) return st;
+    return status_of(moe::launch_dispatch_small(
+        topk_idx, shape->T, shape->E, shape->k, shape->R, shape->W, x, row_bytes, expert_counts,
+        expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, stats, send_buf,
+        s));
+  }
+  st = moe_route_index(shape, logits, topk_idx, topk_w, expert_counts, expert_offsets,
+                       rank_counts, rank_offsets, wave_offsets, pos, row_token, stats, workspace,
+                       workspace_bytes_given, stream);
+  if (st != MOE_OK) return st;
+  return moe_dispatch_copy(shape, x, pos, send_buf, stream);
+}
+
 int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos, void* send_buf,
                       moe_stream_t stream) {
   int st = check_shape(shape);
@@ -236,6 +270,11 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
   if (st != MOE_OK) return st;
   st = check_copy_args(shape, x, pos, send_buf);
   if (st != MOE_OK) return st;
+  if (moe::dispatch_one_launch(int64_t(shape->T) * shape->k, shape->E))
+    return status_of(moe::launch_dispatch_small(
+        topk_idx, shape->T, shape->E, shape->k, shape->R, shape->W, x,
+        int64_t(shape->H) * elem_bytes(shape->dtype), expert_counts, expert_offsets, rank_counts,
+        rank_offsets, wave_offsets, pos, row_token, nullptr, send_buf, as_stream(stream)));
   st = moe_dispatch_index(shape, topk_idx, expert_counts, expert_offsets, rank_counts,
                           rank_offsets, wave_offsets, pos, row_token, workspace,
                           workspace_bytes_given, stream);
@@ -609,8 +648,14 @@ int moe_dispatch_noalloc(const moe_shape* shape, const void* x, const int32_t* t
   if (st != MOE_OK) return st;
   st = check_copy_args(shape, x, pos, send_buf);
   if (st != MOE_OK) return st;
-  // the count pass writes every row of its histogram, so nothing needs clearing
   const int64_t npicks = int64_t(shape->T) * shape->k;
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  if (moe::dispatch_one_launch(npicks, shape->E))  // one launch, no histogram workspace
+    return status_of(moe::launch_dispatch_small(
+        topk_idx, shape->T, shape->E, shape->k, shape->R, shape->W, x, row_bytes, expert_counts,
+        expert_offsets, rank_counts, rank_offsets, wave_offsets, pos, row_token, nullptr,
+        send_buf, as_stream(stream)));
+  // the count pass writes every row of its histogram, so nothing needs clearing
   const int64_t need = moe::num_chunks(npicks, shape->E) * int64_t(shape->E) * 4;
   if (need > int64_t(kScratchBytes)) return MOE_ERR_WORKSPACE;
   void* ws = scratch_on_current_device();
@@ -623,7 +668,6 @@ int moe_dispatch_noalloc(const moe_shape* shape, const void* x, const int32_t* t
                                    hist, expert_counts, expert_offsets, rank_counts,
                                    rank_offsets, wave_offsets, pos, row_token, s));
   if (st != MOE_OK) return st;
-  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
   return status_of(moe::launch_copy(x, pos, shape->T, shape->k, row_bytes, npicks, send_buf, s));
 }
 

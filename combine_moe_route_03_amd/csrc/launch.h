@@ -105,6 +105,17 @@ hipError_t launch_place_chunks(const int32_t* idx, int64_t npicks, int64_t chunk
                                int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
                                int32_t* row_token, moe_stats_t* stats, int cap, hipStream_t s);
 
+// Counts, offsets, positions, the statistics (stats may be null) and the
+// dispatch copy in one launch; only for dispatch_one_launch(T*k, E) (all picks
+// in one 1024-pick batch). Ids outside [0, E) are dropped picks.
+bool dispatch_one_launch(int64_t npicks, int E);
+hipError_t launch_dispatch_small(const int32_t* topk_idx, int T, int E, int k, int R, int W,
+                                 const void* x, int64_t row_bytes, int32_t* expert_counts,
+                                 int32_t* expert_offsets, int32_t* rank_counts,
+                                 int32_t* rank_offsets, int32_t* wave_offsets, int32_t* pos,
+                                 int32_t* row_token, moe_stats_t* stats, void* send,
+                                 hipStream_t s);
+
 // Row copies; row_bytes is a multiple of 16.
 hipError_t launch_copy(const void* x, const int32_t* pos, int T, int k, int64_t row_bytes,
                        int64_t send_rows, void* send, hipStream_t s);

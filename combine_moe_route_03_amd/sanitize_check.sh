@@ -16,7 +16,7 @@ SRC=combine_moe_route_03_amd/csrc
   -Xarch_host -fno-sanitize-recover=undefined -shared-libsan \
   -I include -I $SRC \
   $SRC/abi.hip $SRC/route.hip $SRC/dispatch.hip $SRC/combine.hip $SRC/expert.hip $SRC/ffn.hip \
-  $SRC/stats.hip $SRC/alpha.hip $SRC/exchange.hip $SRC/waves.hip \
+  $SRC/stats.hip $SRC/alpha.hip $SRC/exchange.hip $SRC/waves.hip $SRC/dispatch_small.hip \
   -o "$OUT/libmoe_route_san.so"
 export MOE_ROUTE_LIB=$OUT/libmoe_route_san.so
 export LD_PRELOAD=$(ls /opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so | head -1)

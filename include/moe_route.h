@@ -141,6 +141,23 @@ int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_i
                     int32_t* pos, int32_t* row_token, moe_stats_t* stats, void* workspace,
                     size_t workspace_bytes, moe_stream_t stream);
 
+/* moe_route_index followed by moe_dispatch_copy (routing, counts, offsets,
+ * positions, the optional statistics and the permute copy) with identical
+ * results. When all T * k picks fit one 1024-pick batch (the decode regime)
+ * it is TWO launches: the routing kernel, then the one-launch dispatch of
+ * moe_dispatch with one extra block for the statistics. Otherwise the three
+ * launches of the two calls (routing with the counting pass, placing with the
+ * statistics block, copy). Arguments as those two calls (logits [T][E] fp32,
+ * x [T][H], send_buf [T*k][H]; stats NULL or one device moe_stats_t;
+ * workspace of moe_dispatch_workspace_bytes(shape) bytes, unused by the
+ * one-launch dispatch). Errors: as moe_route_index and moe_dispatch_copy. */
+int moe_route_dispatch(const moe_shape* shape, const float* logits, const void* x,
+                       int32_t* topk_idx, float* topk_w, void* send_buf, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                       int32_t* wave_offsets, int32_t* pos, int32_t* row_token,
+                       moe_stats_t* stats, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream);
+
 /* The permute copy (explainer section 3 item 5: rows are reordered by
  * destination and packed before sending): send_buf[pos[t][i]][:] = x[t][:],
  * a bit copy. Each x row is read once and written k times; picks with
@@ -149,7 +166,12 @@ int moe_route_index(const moe_shape* shape, const float* logits, int32_t* topk_i
 int moe_dispatch_copy(const moe_shape* shape, const void* x, const int32_t* pos,
                       void* send_buf, moe_stream_t stream);
 
-/* moe_dispatch_index followed by moe_dispatch_copy on the same stream. */
+/* moe_dispatch_index followed by moe_dispatch_copy on the same stream, with
+ * identical results. When all T * k picks fit one 1024-pick batch (T * k <=
+ * 1024, E <= 1024: the decode regime) it is ONE launch: every block reads all
+ * expert ids and places all picks itself (no device-wide ordering point is
+ * needed), then copies its share of the rows; block 0 writes the index tables
+ * (the workspace is then unused). Otherwise count, place and copy launches. */
 int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                  void* send_buf, int32_t* expert_counts,
                  int32_t* expert_offsets, int32_t* rank_counts,
@@ -163,8 +185,8 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  * static device array of moe_noalloc_scratch_bytes() = 256 KiB that the
  * library holds on each device it runs on until the process ends (its device
  * address is looked up on the first call made with that device current).
- * Same arguments, results and launches as moe_dispatch; nothing is allocated
- * or freed. Every call on one device shares that device's array: calls that
+ * Same arguments, results and launches as moe_dispatch (whose one-launch form
+ * for T * k <= 1024 needs no histogram at all); nothing is allocated or freed. Every call on one device shares that device's array: calls that
  * overlap on one device (concurrent streams, or several host threads) race
  * and must be serialised by the caller. The array's contents need no
  * initialisation (each call writes every histogram row it reads).

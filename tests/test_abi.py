@@ -280,3 +280,25 @@ def test_noalloc_dispatch_validation():
     assert L.moe_dispatch_noalloc(ctypes.byref(sh), *a, None) == ALIGN
     assert L.moe_dispatch_noalloc(ctypes.byref(_shape(E=9)), *args, None) == ARG
     assert L.moe_dispatch_noalloc(None, *args, None) == ARG
+
+
+def test_route_dispatch_validation():
+    L = moe.lib()
+    sh = _shape()
+    ws = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
+    # logits, x, topk_idx, topk_w, send_buf, 7 index outputs, stats, workspace
+    args = [FAKE] * 14
+    call = lambda a, n=ws: L.moe_route_dispatch(ctypes.byref(sh), *a, n, None)  # noqa: E731
+    for i in range(14):
+        if i == 12:  # stats may be NULL
+            continue
+        a = list(args)
+        a[i] = None
+        assert call(a) == ARG, i
+    a = list(args)
+    a[12] = ctypes.c_void_p((1 << 20) + 4)  # stats not 8-byte aligned
+    assert call(a) == ALIGN
+    a = list(args)
+    a[1] = ctypes.c_void_p((1 << 20) + 8)  # x not 16-byte aligned
+    assert call(a) == ALIGN
+    assert call(args, ws - 1) == WORKSPACE
