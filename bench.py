@@ -272,58 +272,79 @@ def cpu_baseline(wl, logits, x, seconds: float, ffn_weights=None, vsrc=False) ->
 
 
 def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
-    """T(W) of the wave-pipelined local layer: per W dividing L, K steps of
-    route+index (fused) -> per-wave gather dispatch on a copy stream overlapped
-    with the per-wave FFN on the compute stream -> combine; and the same
-    launches on one stream. Fits T(W) = a*W + b + m/W (the page's
-    W*alpha + M/beta + M/(W*beta) plus the stages outside the pipeline)."""
+    """T(W) of the wave-pipelined layer: per W dividing L, K steps of
+    route+index (fused) -> per wave, a gather dispatch on a copy stream
+    overlapped with that wave's experts (the SwiGLU FFN, or the identity-scaled
+    experts) on the compute stream -> combine; and the same launches on one
+    stream; and, for reference, the unpipelined copy + expert stage with the
+    same W. Fits T(W) = a*W + b + m/W (the page's W*alpha + M/beta +
+    M/(W*beta) plus the stages outside the pipeline)."""
     dev = torch.device("cuda:0")
     T, H, E, k, R = wl.T, wl.H, wl.E, wl.k, wl.R
     L = E // R
+    swiglu = wl.expert == "swiglu"
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     logits, x = to_dev(logits_np), to_dev(x_np)
     import synth
-    gu_np, dn_np = synth.swiglu_weights(wl)
-    gu, dn = to_dev(gu_np), to_dev(dn_np)
+    if swiglu:
+        gu_np, dn_np = synth.swiglu_weights(wl)
+        gu, dn = to_dev(gu_np), to_dev(dn_np)
     side = torch.cuda.Stream()
-    res = {"W": [], "ms_two_streams": [], "ms_one_stream": []}
+    res = {"W": [], "ms_two_streams": [], "ms_one_stream": [], "ms_unpipelined": []}
     for W in [d for d in range(1, L + 1) if L % d == 0]:
-        shape = moe.Shape(T, H, E, k, R, W, torch.bfloat16)
+        shape = moe.Shape(T, H, E, k, R, W, tdt)
         buf = moe.alloc_dispatch(shape, dev)
         idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         wt = torch.empty((T, k), dtype=torch.float32, device=dev)
         eo = torch.empty_like(buf["send_buf"])
-        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
-                         device=dev)
+        y = torch.empty((T, H), dtype=tdt, device=dev)
+        if swiglu:
+            ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),),
+                             dtype=torch.uint8, device=dev)
+            chains = moe.Chains(n_events=moe.swiglu_waves_events(W))
+        else:
+            chains = moe.Chains(n_events=1 + W, side=False)
 
-        chains = moe.Chains(n_events=moe.swiglu_waves_events(W))
-
-        def step(two):
+        def step(mode):
             moe.route_index(logits, shape, buf, idx, wt)
-            moe.swiglu_waves(x, buf, shape, gu, dn, expert_out=eo, workspace=ws,
-                             copy_stream=side if two else None, chains=chains)
+            copy = side if mode == "two" else None
+            if mode == "plain":
+                moe.dispatch_copy(x, buf["pos"], shape, buf["send_buf"])
+                if swiglu:
+                    moe.expert_swiglu(buf["send_buf"], buf["expert_offsets"],
+                                      buf["expert_counts"], shape, gu, dn, expert_out=eo,
+                                      workspace=ws, chains=chains)
+                else:
+                    moe.expert_scale(buf["send_buf"], buf["expert_offsets"],
+                                     buf["expert_counts"], shape, expert_out=eo)
+            elif swiglu:
+                moe.swiglu_waves(x, buf, shape, gu, dn, expert_out=eo, workspace=ws,
+                                 copy_stream=copy, chains=chains)
+            else:
+                moe.scale_waves(x, buf, shape, expert_out=eo, copy_stream=copy, chains=chains)
             moe.combine(eo, wt, buf["pos"], shape, y=y)
 
         row = []
-        for two in (True, False):
+        for mode in ("two", "one", "plain"):
             for _ in range(args.warmup):
-                step(two)
+                step(mode)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(args.steps):
-                step(two)
+                step(mode)
             torch.cuda.synchronize()
             row.append((time.perf_counter() - t0) * 1e3 / args.steps)
         res["W"].append(W)
         res["ms_two_streams"].append(round(row[0], 4))
         res["ms_one_stream"].append(round(row[1], 4))
-        print(f"[bench] W={W}: {row[0]:.4f} ms (two streams), {row[1]:.4f} ms (one)",
-              file=sys.stderr, flush=True)
+        res["ms_unpipelined"].append(round(row[2], 4))
+        print(f"[bench] W={W}: {row[0]:.4f} ms (two streams), {row[1]:.4f} ms (one), "
+              f"{row[2]:.4f} ms (unpipelined)", file=sys.stderr, flush=True)
     Ws = np.array(res["W"], float)
     t = np.array(res["ms_two_streams"]) * 1e-3
     A = np.stack([Ws, np.ones_like(Ws), 1.0 / Ws], axis=1)
     (a, b, m), *_ = np.linalg.lstsq(A, t, rcond=None)
-    M = T * k * H * 2  # bytes dispatched per step (the gathered rows)
+    M = T * k * H * wl.elem_bytes  # bytes dispatched per step (the gathered rows)
     fit = {"alpha_us": round(a * 1e6, 3), "const_us": round(b * 1e6, 2), "m_us": round(m * 1e6, 2)}
     if a > 0 and m > 0:
         beta = M / m
@@ -733,16 +754,19 @@ def wave_sweep_result(args, wl, moe, torch, np, c) -> dict:
     ws_res = wave_sweep(args, wl, moe, torch, np, c.to_dev, c.logits_np, c.x_np)
     best = ws_res["W"].index(ws_res["W_best_measured"])
     ms = ws_res["ms_two_streams"][best]
+    swiglu = wl.expert == "swiglu"
     return {
         "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic (seeded logits and hidden states; random-init SwiGLU expert weights)",
+        "data": "synthetic (seeded logits and hidden states"
+                + ("; random-init SwiGLU expert weights)" if swiglu else "; identity-scaled experts)"),
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k,
-                   "virtual_ranks": wl.R, "waves": ws_res["W_best_measured"], "I": wl.I,
-                   "expert": wl.expert,
+                   "virtual_ranks": wl.R, "waves": ws_res["W_best_measured"],
+                   **({"I": wl.I} if swiglu else {}), "expert": wl.expert,
                    "step": "route+index (moe_route_index) + per wave: gather dispatch (copy "
-                           "stream) -> FFN (compute stream) + combine"},
+                           "stream) -> experts (compute stream) + combine; value = whole-step "
+                           "tokens/s at the best W"},
         "wave_sweep": ws_res,
     }
 
@@ -764,9 +788,6 @@ def main() -> int:
 
     wl = synth.WORKLOADS[args.workload]
     swiglu = wl.expert == "swiglu"
-    if args.wave_sweep and not swiglu:
-        print("--wave-sweep runs the SwiGLU local layer (--workload local_layer)", file=sys.stderr)
-        return 2
     if (args.capacity_factor is not None or args.vsrc) and swiglu:
         print("--capacity-factor and --vsrc run the identity-scaled experts", file=sys.stderr)
         return 2

@@ -76,6 +76,8 @@ SIGNATURES = {
     "moe_swiglu_waves": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           ctypes.c_size_t, _vp, _vp, _vp, _vp, _i32], ctypes.c_int),
     "moe_swiglu_waves_events": ([_i32], ctypes.c_int32),
+    "moe_scale_waves": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32],
+                        ctypes.c_int),
     "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
     "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp], ctypes.c_int),
@@ -532,6 +534,30 @@ def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tens
         _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(w_gate_up), _ptr(w_down),
         _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), compute, copy,
         side, events, n_events), "moe_swiglu_waves")
+    return expert_out
+
+
+def scale_waves(x: torch.Tensor, out: dict, shape: Shape, expert_out: torch.Tensor | None = None,
+                copy_stream: torch.cuda.Stream | None = None,
+                chains: Chains | None = None) -> torch.Tensor:
+    """Wave-pipelined dispatch + identity-scaled experts: per wave a gather of its
+    rows into out["send_buf"] on `copy_stream`, then the (e+1) scaling of those
+    rows on the current stream after an event. `out` holds a dispatch index of
+    `shape`; with a copy stream, `chains` supplies at least 1 + W events."""
+    send_buf = out["send_buf"]
+    expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
+    compute = _stream()
+    copy = compute if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    if copy_stream is not None and (chains is None or len(chains.events) < 1 + shape.W):
+        raise ValueError(f"scale_waves with a copy stream needs a Chains with at least "
+                         f"{1 + shape.W} events")
+    events = chains.event_array() if chains is not None else None
+    n_events = len(chains.events) if chains is not None else 0
+    sh = shape.c()
+    _check(lib().moe_scale_waves(
+        ctypes.byref(sh), _ptr(x), _ptr(out["row_token"]), _ptr(out["wave_offsets"]),
+        _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(send_buf),
+        _ptr(expert_out), compute, copy, events, n_events), "moe_scale_waves")
     return expert_out
 
 

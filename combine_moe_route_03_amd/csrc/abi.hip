@@ -358,6 +358,32 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
       static_cast<hipEvent_t>(fork_event), static_cast<hipEvent_t>(join_event)));
 }
 
+int moe_scale_waves(const moe_shape* shape, const void* x, const int32_t* row_token,
+                    const int32_t* wave_offsets, const int32_t* expert_offsets,
+                    const int32_t* expert_counts, void* send_buf, void* expert_out,
+                    moe_stream_t compute_stream, moe_stream_t copy_stream, void* const* events,
+                    int32_t n_events) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!wave_offsets || !expert_offsets || !expert_counts) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!x || !row_token || !send_buf || !expert_out)) return MOE_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(send_buf, 16) || !aligned(expert_out, 16) ||
+      !aligned(row_token, 4) || !aligned(wave_offsets, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(expert_counts, 4))
+    return MOE_ERR_ALIGN;
+  if (copy_stream != compute_stream) {
+    if (!events || n_events < 1 + shape->W) return MOE_ERR_ARG;
+    for (int32_t i = 0; i < 1 + shape->W; ++i)
+      if (!events[i]) return MOE_ERR_ARG;
+  }
+  const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  return status_of(moe::launch_scale_waves(
+      x, shape->T, shape->k, row_bytes, shape->dtype, shape->H, shape->E, shape->R, shape->W,
+      row_token, wave_offsets, expert_offsets, expert_counts, send_buf, expert_out,
+      as_stream(compute_stream), as_stream(copy_stream),
+      reinterpret_cast<const hipEvent_t*>(events)));
+}
+
 int32_t moe_swiglu_waves_events(int32_t W) { return W < 1 || W > (1 << 20) ? -1 : 1 + 3 * W; }
 
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,

@@ -127,6 +127,13 @@ hipError_t launch_expert_scale(const void* in, int dtype, int64_t rows, int64_t 
                                int W, const int32_t* expert_offsets,
                                const int32_t* expert_counts, void* out, hipStream_t s);
 
+// The identity-scaled experts on the rows of one expert wave w (bounds read
+// from wave_offsets on the device).
+hipError_t launch_expert_scale_wave(const void* in, int dtype, int64_t rows_max, int64_t H, int E,
+                                    int R, int W, const int32_t* expert_offsets,
+                                    const int32_t* expert_counts, const int32_t* wave_offsets,
+                                    int w, void* out, hipStream_t s);
+
 // expert_out has eo_rows rows; picks with pos outside [0, eo_rows) are skipped.
 hipError_t launch_combine(const void* expert_out, int dtype, const float* w, const int32_t* pos,
                           int T, int k, int64_t H, int64_t eo_rows, void* y, hipStream_t s);
@@ -196,6 +203,14 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
 hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int32_t* wave_offsets,
                               int w, int T, int64_t rows_max, int64_t row_bytes, void* send,
                               hipStream_t s);
+// Wave-pipelined identity-scaled experts: per wave, gather dispatch of its rows
+// on `copy`, then the experts of the wave on `compute` after an event; events
+// holds at least 1 + W caller-owned events when copy != compute.
+hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, int dtype, int64_t H,
+                              int E, int R, int W, const int32_t* row_token,
+                              const int32_t* wave_offsets, const int32_t* offs,
+                              const int32_t* cnts, void* send, void* out, hipStream_t compute,
+                              hipStream_t copy, const hipEvent_t* events);
 hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,

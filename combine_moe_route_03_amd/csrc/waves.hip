@@ -70,6 +70,37 @@ hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int
                 row_token, wave_offsets, w, T, rows_max, nvec, static_cast<v4u*>(send));
 }
 
+// The identity-scaled experts of the synthetic workloads in the same
+// schedule: per wave its gather dispatch on the copy stream, an event, and
+// the wave's experts on the compute stream (bit-identical to the one-pass copy
+// and expert stage: both are bit copies and the same per-element product).
+hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, int dtype, int64_t H,
+                              int E, int R, int W, const int32_t* row_token,
+                              const int32_t* wave_offsets, const int32_t* offs,
+                              const int32_t* cnts, void* send, void* out, hipStream_t compute,
+                              hipStream_t copy, const hipEvent_t* events) {
+  const int64_t rows = (int64_t)T * k;
+  if (rows == 0) return hipSuccess;
+  const bool two = copy != compute;
+  hipError_t e = hipSuccess;
+  if (two) {
+    if ((e = hipEventRecord(events[0], compute)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(copy, events[0], 0)) != hipSuccess) return e;
+  }
+  for (int w = 0; w < W; ++w) {
+    e = launch_gather_wave(x, row_token, wave_offsets, w, T, rows, row_bytes, send, copy);
+    if (e != hipSuccess) return e;
+    if (two) {
+      if ((e = hipEventRecord(events[w + 1], copy)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(compute, events[w + 1], 0)) != hipSuccess) return e;
+    }
+    e = launch_expert_scale_wave(send, dtype, rows, H, E, R, W, offs, cnts, wave_offsets, w, out,
+                                 compute);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,

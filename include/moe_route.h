@@ -385,6 +385,25 @@ int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int
                      moe_stream_t compute_stream, moe_stream_t copy_stream,
                      moe_stream_t side_stream, void* const* events, int32_t n_events);
 
+/* The same wave schedule with the identity-scaled experts of moe_expert_scale
+ * (the experts of the synthetic workloads): for each wave w, on copy_stream
+ * the gather dispatch send_buf[r] = x[row_token[r]] of rows [wave_offsets[w],
+ * wave_offsets[w+1]), an event, and on compute_stream the (e+1) scaling of
+ * those rows into expert_out. Results are bit-identical to moe_dispatch_copy +
+ * moe_expert_scale (follow with moe_combine on compute_stream). copy_stream
+ * first waits for the work already queued on compute_stream; copy_stream ==
+ * compute_stream runs the same launches serialised. events: at least 1 + W
+ * caller-owned hipEvent_t handles when the streams differ (unused otherwise).
+ * 2W launches. row_token, wave_offsets, expert_offsets, expert_counts as
+ * written by a dispatch-index call with the same shape (DEVICE).
+ * Errors: MOE_ERR_ARG (null pointers, too few or null events), MOE_ERR_ALIGN,
+ *         MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
+int moe_scale_waves(const moe_shape* shape, const void* x, const int32_t* row_token,
+                    const int32_t* wave_offsets, const int32_t* expert_offsets,
+                    const int32_t* expert_counts, void* send_buf, void* expert_out,
+                    moe_stream_t compute_stream, moe_stream_t copy_stream, void* const* events,
+                    int32_t n_events);
+
 /* Events moe_swiglu_waves needs for W waves: 1 + 3W (-1 for W outside
  * [1, 2^20]). Host-only, pure. */
 int32_t moe_swiglu_waves_events(int32_t W);

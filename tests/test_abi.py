@@ -302,3 +302,22 @@ def test_route_dispatch_validation():
     a[1] = ctypes.c_void_p((1 << 20) + 8)  # x not 16-byte aligned
     assert call(a) == ALIGN
     assert call(args, ws - 1) == WORKSPACE
+
+
+def test_scale_waves_validation():
+    L = moe.lib()
+    sh = _shape(T=64, H=256, E=8, k=2, R=1, W=2)
+    a = [FAKE] * 7  # x, row_token, wave_offsets, expert_offsets, expert_counts, send, out
+    evs = (ctypes.c_void_p * 3)(*[FAKE] * 3)
+    go = lambda a, copy, ev, n: L.moe_scale_waves(ctypes.byref(sh), *a, None, copy, ev, n)  # noqa: E731
+    for i in range(7):
+        b = list(a)
+        b[i] = None
+        assert go(b, None, None, 0) == ARG, i
+    assert go(a, FAKE, None, 0) == ARG          # a copy stream needs 1 + W events
+    assert go(a, FAKE, evs, 2) == ARG
+    holes = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert go(a, FAKE, holes, 3) == ARG
+    b = list(a)
+    b[0] = ctypes.c_void_p((1 << 20) + 4)
+    assert go(b, None, None, 0) == ALIGN

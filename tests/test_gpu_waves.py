@@ -104,3 +104,51 @@ def test_wave_pipeline_full_size_repeat():
         assert torch.equal(out["send_buf"][:n], plain["send_buf"][:n]), rep
         assert torch.equal(eo[:n], eo_p[:n]), rep
         assert torch.equal(y, y_p), rep
+
+
+# ------------------------------------------- identity-scaled experts in waves
+
+SCALE_CASES = [("dirichlet_shape_W8", 32, 8, 1024, 256), ("dirichlet_shape_W1", 32, 1, 1024, 256),
+               ("R4_W2_f32", 4, 2, 700, 64), ("R1_W4_ragged", 1, 4, 333, 128)]
+
+
+@pytest.mark.parametrize("name,R,W,T,H", SCALE_CASES)
+@pytest.mark.parametrize("two_streams", [True, False])
+def test_scale_waves_match_plain(name, R, W, T, H, two_streams):
+    """moe_scale_waves (per wave: gather dispatch on a copy stream, the wave's
+    identity-scaled experts on the compute stream) against moe_dispatch_copy +
+    moe_expert_scale and the oracle: send rows, expert rows and the combine
+    after it, bit for bit."""
+    base = synth.WORKLOADS["dirichlet_waves"] if R == 32 else synth.WORKLOADS["zipf"]
+    dt = "f32" if name.endswith("f32") else "bf16"
+    E = 256 if R == 32 else 64
+    wl = base.with_(T=T, H=H, E=E, R=R, W=W, dtype=dt, seed=7)
+    print(f"[scale waves] {name} two_streams={two_streams}: T={T} H={H} E={E} k={wl.k} R={R} "
+          f"W={W} {dt}", flush=True)
+    logits, x = synth.logits(wl), synth.hidden(wl)
+    idx, w = oracle.route(logits, wl.k)
+    ref = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
+    out_o = oracle.expert_scale(ref["send_buf"], ref["expert_offsets"], ref["expert_counts"])
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    shape = moe.Shape(T, H, E, wl.k, R, W, tdt)
+    xd, idd, wd = dev(x), dev(idx), dev(w.astype(np.float32))
+    plain = moe.dispatch(xd, idd, E, R, W)
+    eo_p = moe.expert_scale(plain["send_buf"], plain["expert_offsets"], plain["expert_counts"],
+                            shape)
+    y_p = moe.combine(eo_p, wd, plain["pos"], shape)
+    out = moe.alloc_dispatch(shape, DEV)
+    moe.dispatch_index(idd, shape, out)
+    out["send_buf"].view(torch.uint8).fill_(0xA5)
+    eo = torch.empty_like(out["send_buf"])
+    eo.view(torch.uint8).fill_(0x5A)
+    copy = torch.cuda.Stream() if two_streams else None
+    chains = moe.Chains(n_events=1 + W, side=False) if two_streams else None
+    moe.scale_waves(xd, out, shape, expert_out=eo, copy_stream=copy, chains=chains)
+    y = moe.combine(eo, wd, out["pos"], shape)
+    torch.cuda.synchronize()
+    n = ref["nrows"]
+    np.testing.assert_array_equal(host(out["send_buf"])[:n], ref["send_buf"])
+    np.testing.assert_array_equal(host(eo)[:n], out_o)
+    bits = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(eo[:n].view(bits), eo_p[:n].view(bits))
+    assert torch.equal(y.view(bits), y_p.view(bits))
