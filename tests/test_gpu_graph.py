@@ -74,6 +74,53 @@ def test_graph_replay_default_step():
     _replays_match(step, outputs, noise)
 
 
+def test_graph_replay_decode_step():
+    """The decode step as the benchmark's --fused path runs it: routing, the
+    one-launch dispatch with its statistics block, experts, combine; and the
+    wave-pipelined identity-scaled experts on two streams (dirichlet_waves
+    layout, W = 8) in the same graph."""
+    wl = synth.WORKLOADS["decode_hot"]
+    print(f"[graph] decode step: T={wl.T} H={wl.H} E={wl.E} k={wl.k}", flush=True)
+    shape = shape_of(wl)
+    logits, x = dev(synth.logits(wl)), dev(synth.hidden(wl))
+    out = moe.alloc_dispatch(shape, DEV)
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=DEV)
+    raw = torch.empty((moe.STATS_BYTES,), dtype=torch.uint8, device=DEV)
+    eo = torch.empty_like(out["send_buf"])
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    wv = synth.WORKLOADS["dirichlet_waves"].with_(T=256, H=512)
+    shape_w = shape_of(wv)
+    logits_w, x_w = dev(synth.logits(wv)), dev(synth.hidden(wv))
+    out_w = moe.alloc_dispatch(shape_w, DEV)
+    idx_w = torch.empty((wv.T, wv.k), dtype=torch.int32, device=DEV)
+    w_w = torch.empty((wv.T, wv.k), dtype=torch.float32, device=DEV)
+    eo_w = torch.empty_like(out_w["send_buf"])
+    y_w = torch.empty((wv.T, wv.H), dtype=torch.bfloat16, device=DEV)
+    copy = torch.cuda.Stream()
+    chains = moe.Chains(n_events=1 + wv.W, side=False)
+    out2 = moe.alloc_dispatch(shape, DEV)
+    idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
+
+    def step():
+        moe.route_dispatch(logits, x, shape, out, idx, w, stats=raw)
+        moe.expert_scale(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                         expert_out=eo)
+        moe.combine(eo, w, out["pos"], shape, y=y)
+        moe.route_index(logits_w, shape_w, out_w, idx_w, w_w)
+        moe.scale_waves(x_w, out_w, shape_w, expert_out=eo_w, copy_stream=copy, chains=chains)
+        moe.combine(eo_w, w_w, out_w["pos"], shape_w, y=y_w)
+
+    def noise():
+        moe.route_dispatch(logits, x, shape, out2, idx2, w2)
+
+    n, nw = wl.T * wl.k, wv.T * wv.k
+    outputs = [idx, w, raw, out["expert_counts"], out["expert_offsets"], out["rank_counts"],
+               out["rank_offsets"], out["wave_offsets"], out["pos"], out["row_token"][:n],
+               out["send_buf"], eo, y, out_w["send_buf"][:nw], eo_w[:nw], y_w]
+    _replays_match(step, outputs, noise)
+
+
 def test_graph_replay_capacity_and_direct_exchange():
     wl = PARITY["zipf"]
     print(f"[graph] capacity + direct exchange: T={wl.T} H={wl.H} E={wl.E}", flush=True)
