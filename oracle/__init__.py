@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_scaled_tokens.argtypes = [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, _i32p, _f64p, _f32p, _i64p,
                                            ctypes.c_int64, _f64p, _vp]
+        L.oracle_combine_order.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]
         _u16p = ctypes.POINTER(ctypes.c_uint16)
         L.oracle_expert_swiglu_rows.argtypes = [_u16p, _i32p, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_int64, _u16p, _u16p, _f64p, _u16p,
@@ -201,6 +203,16 @@ def dispatch(x: np.ndarray, idx: np.ndarray, E: int, R: int, W: int):
     send = dispatch_copy(x, row_token, nrows)
     return dict(expert_counts=ec, rank_counts=rc, expert_offsets=eo, rank_offsets=ro,
                 wave_offsets=wo, pos=pos, row_token=row_token, send_buf=send, nrows=nrows)
+
+
+def combine_order(idx: np.ndarray, E: int, R: int, W: int):
+    """Per-wave combine order: (token_wave_offsets int32 [W+1], token_order int32 [T])."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    two = np.empty(W + 1, np.int32)
+    order = np.empty(max(T, 1), np.int32)
+    lib().oracle_combine_order(_p(idx, _i32p), T, k, E, R, W, _p(two, _i32p), _p(order, _i32p))
+    return two, order[:T]
 
 
 def expert_capacity(k: int, f: float, T: int, E: int) -> int:

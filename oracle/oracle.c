@@ -332,6 +332,46 @@ void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
   }
 }
 
+/* ------------------------------------------------------- per-wave combine */
+
+/* The wave after which token t's combine can run: its picks' experts sit in
+ * waves wave_of(e) (irregular AllToAll page, "Wave-Scheduled pipelining": W
+ * waves of E / W experts, each wave running dispatch -> compute -> combine),
+ * and the token's weighted sum needs every one of them, so it is complete
+ * after the last of those waves. A token without a kept pick is complete
+ * before any wave: wave 0. Tokens are listed wave by wave, in token order
+ * within a wave; token_wave_offsets[w] is the first entry of wave w and
+ * token_wave_offsets[W] = T. */
+void oracle_combine_order(const int32_t* idx, int64_t T, int32_t k, int32_t E,
+                          int32_t R, int32_t W, int32_t* token_wave_offsets,
+                          int32_t* token_order) {
+  int32_t L = E / R;
+  int32_t* done = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t last = 0;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t e = idx[t * k + i];
+      if (e < 0 || e >= E) continue; /* dropped pick */
+      int32_t w = wave_of(e, L, W);
+      if (w > last) last = w;
+    }
+    done[t] = last;
+  }
+  /* first entry of each wave: tokens of the waves before it */
+  for (int32_t w = 0; w <= W; ++w) {
+    int32_t before = 0;
+    for (int64_t t = 0; t < T; ++t)
+      if (done[t] < w) ++before;
+    token_wave_offsets[w] = before;
+  }
+  for (int32_t w = 0; w < W; ++w) {
+    int32_t n = token_wave_offsets[w];
+    for (int64_t t = 0; t < T; ++t)
+      if (done[t] == w) token_order[n++] = (int32_t)t;
+  }
+  free(done);
+}
+
 /* ------------------------------------------------------------------- stats */
 
 double oracle_gini_i64(const int64_t* v, int32_t n) {

@@ -120,6 +120,16 @@ void oracle_scaled_tokens(const void* x, int32_t dtype, int64_t H, int32_t E,
                           const float* w32, const int64_t* tokens, int64_t n,
                           double* y_f64, void* y_q);
 
+/* Completion-wave order of the tokens for a per-wave combine (irregular
+ * AllToAll page, "Wave-Scheduled pipelining": each wave's dispatch -> compute
+ * -> combine). Token t is complete after wave max_i wave_of(idx[t][i]) over
+ * its kept picks (0 when it has none). token_wave_offsets [W+1]: first entry
+ * of each wave's tokens (last = T); token_order [T]: tokens wave by wave,
+ * ascending within a wave. */
+void oracle_combine_order(const int32_t* idx, int64_t T, int32_t k, int32_t E,
+                          int32_t R, int32_t W, int32_t* token_wave_offsets,
+                          int32_t* token_order);
+
 /* SwiGLU expert FFN of the local-layer workload, on selected send-buffer rows
  * (the pages name only an FFN; the workload fixes SwiGLU, intermediate size I,
  * bf16 weights). For row n of expert e = row_expert[n], in double:
