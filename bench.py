@@ -104,8 +104,11 @@ def parse_args():
                          "moe_route_dispatch (two launches when T*k <= 1024, else three; the "
                          "counting pass then runs inside the routing kernel)")
     ap.add_argument("--wave-sweep", action="store_true",
-                    help="local layer: wave-pipelined dispatch + FFN for every W dividing L, "
-                         "two streams vs one; T(W) and the fitted wave model")
+                    help="wave-pipelined dispatch + experts for every W dividing L, two streams "
+                         "vs one, with and without the per-wave combine; T(W) and the fitted "
+                         "wave model")
+    ap.add_argument("--waves", type=int, default=None,
+                    help="with --wave-sweep: only this W (for a profiled run)")
     ap.add_argument("--vsrc", action="store_true",
                     help="the expert-parallel exchange of R virtual source ranks on one device")
     ap.add_argument("--direct", action="store_true",
@@ -276,9 +279,12 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
     route+index (fused) -> per wave, a gather dispatch on a copy stream
     overlapped with that wave's experts (the SwiGLU FFN, or the identity-scaled
     experts) on the compute stream -> combine; and the same launches on one
-    stream; and, for reference, the unpipelined copy + expert stage with the
-    same W. Fits T(W) = a*W + b + m/W (the page's W*alpha + M/beta +
-    M/(W*beta) plus the stages outside the pipeline)."""
+    stream; the two-stream schedule with each wave's completed tokens combined
+    in the pipeline (on a third stream, as soon as the wave's experts are
+    done); and,
+    for reference, the unpipelined copy + expert stage with the same W. Fits
+    T(W) = a*W + b + m/W (the page's W*alpha + M/beta + M/(W*beta) plus the
+    stages outside the pipeline) to the two-stream times."""
     dev = torch.device("cuda:0")
     T, H, E, k, R = wl.T, wl.H, wl.E, wl.k, wl.R
     L = E // R
@@ -289,25 +295,39 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
     if swiglu:
         gu_np, dn_np = synth.swiglu_weights(wl)
         gu, dn = to_dev(gu_np), to_dev(dn_np)
-    side = torch.cuda.Stream()
-    res = {"W": [], "ms_two_streams": [], "ms_one_stream": [], "ms_unpipelined": []}
-    for W in [d for d in range(1, L + 1) if L % d == 0]:
+    side, cstream = torch.cuda.Stream(), torch.cuda.Stream()
+    res = {"W": [], "ms_two_streams": [], "ms_one_stream": [], "ms_unpipelined": [],
+           "ms_two_streams_wave_combine": []}
+    for W in [d for d in range(1, L + 1) if L % d == 0 and args.waves in (None, d)]:
         shape = moe.Shape(T, H, E, k, R, W, tdt)
         buf = moe.alloc_dispatch(shape, dev)
         idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         wt = torch.empty((T, k), dtype=torch.float32, device=dev)
         eo = torch.empty_like(buf["send_buf"])
         y = torch.empty((T, H), dtype=tdt, device=dev)
+        two = torch.empty((W + 1,), dtype=torch.int32, device=dev)
+        order = torch.empty((T,), dtype=torch.int32, device=dev)
+        wc = dict(topk_w=wt, pos=buf["pos"], token_order=order, token_wave_offsets=two, y=y,
+                  stream=cstream)
         if swiglu:
             ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),),
                              dtype=torch.uint8, device=dev)
             chains = moe.Chains(n_events=moe.swiglu_waves_events(W))
         else:
-            chains = moe.Chains(n_events=1 + W, side=False)
+            chains = moe.Chains(n_events=moe.scale_waves_events(W), side=False)
 
         def step(mode):
             moe.route_index(logits, shape, buf, idx, wt)
-            copy = side if mode == "two" else None
+            copy = side if mode in ("two", "two_wc") else None
+            if mode == "two_wc":
+                moe.combine_order(buf["pos"], buf["wave_offsets"], shape, two, order)
+                if swiglu:
+                    moe.swiglu_waves(x, buf, shape, gu, dn, expert_out=eo, workspace=ws,
+                                     copy_stream=copy, chains=chains, combine=wc)
+                else:
+                    moe.scale_waves(x, buf, shape, expert_out=eo, copy_stream=copy,
+                                    chains=chains, combine=wc)
+                return
             if mode == "plain":
                 moe.dispatch_copy(x, buf["pos"], shape, buf["send_buf"])
                 if swiglu:
@@ -325,7 +345,7 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
             moe.combine(eo, wt, buf["pos"], shape, y=y)
 
         row = []
-        for mode in ("two", "one", "plain"):
+        for mode in ("two", "one", "plain", "two_wc"):
             for _ in range(args.warmup):
                 step(mode)
             torch.cuda.synchronize()
@@ -338,19 +358,52 @@ def wave_sweep(args, wl, moe, torch, np, to_dev, logits_np, x_np) -> dict:
         res["ms_two_streams"].append(round(row[0], 4))
         res["ms_one_stream"].append(round(row[1], 4))
         res["ms_unpipelined"].append(round(row[2], 4))
+        res["ms_two_streams_wave_combine"].append(round(row[3], 4))
         print(f"[bench] W={W}: {row[0]:.4f} ms (two streams), {row[1]:.4f} ms (one), "
-              f"{row[2]:.4f} ms (unpipelined)", file=sys.stderr, flush=True)
+              f"{row[2]:.4f} ms (unpipelined), {row[3]:.4f} ms (two streams, per-wave combine)",
+              file=sys.stderr, flush=True)
+        # the combine forms alone, on the last step's buffers (events on the
+        # current stream, median over the steps)
+        moe.combine_order(buf["pos"], buf["wave_offsets"], shape, two, order)
+
+        def each():
+            for q in range(W):
+                moe.combine_waves(eo, wt, buf["pos"], order, two, shape, q, q + 1, y=y)
+        alone = {
+            "combine": lambda: moe.combine(eo, wt, buf["pos"], shape, y=y),
+            "combine_waves_all": lambda: moe.combine_waves(eo, wt, buf["pos"], order, two,
+                                                           shape, 0, W, y=y),
+            "combine_waves_each": each,
+            "combine_order": lambda: moe.combine_order(buf["pos"], buf["wave_offsets"], shape,
+                                                       two, order),
+        }
+        for key, fn in alone.items():
+            ts = []
+            for i in range(args.warmup + args.steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                if i >= args.warmup:
+                    ts.append(a.elapsed_time(b) * 1e3)
+            res.setdefault(f"us_{key}", []).append(round(float(np.median(ts)), 1))
+        res.setdefault("tokens_per_completion_wave", []).append(
+            np.diff(two.cpu().numpy()).tolist())
     Ws = np.array(res["W"], float)
     t = np.array(res["ms_two_streams"]) * 1e-3
-    A = np.stack([Ws, np.ones_like(Ws), 1.0 / Ws], axis=1)
-    (a, b, m), *_ = np.linalg.lstsq(A, t, rcond=None)
     M = T * k * H * wl.elem_bytes  # bytes dispatched per step (the gathered rows)
-    fit = {"alpha_us": round(a * 1e6, 3), "const_us": round(b * 1e6, 2), "m_us": round(m * 1e6, 2)}
-    if a > 0 and m > 0:
-        beta = M / m
-        w_plan, _ = moe.plan_waves(M, a, beta, L)
-        fit.update(beta_GBs=round(beta / 1e9, 1), W_star=round(float(np.sqrt(m / a)), 2),
-                   W_plan=w_plan)
+    fit = None
+    if len(Ws) >= 3:  # three parameters
+        A = np.stack([Ws, np.ones_like(Ws), 1.0 / Ws], axis=1)
+        (a, b, m), *_ = np.linalg.lstsq(A, t, rcond=None)
+        fit = {"alpha_us": round(a * 1e6, 3), "const_us": round(b * 1e6, 2),
+               "m_us": round(m * 1e6, 2)}
+        if a > 0 and m > 0:
+            beta = M / m
+            w_plan, _ = moe.plan_waves(M, a, beta, L)
+            fit.update(beta_GBs=round(beta / 1e9, 1), W_star=round(float(np.sqrt(m / a)), 2),
+                       W_plan=w_plan)
     res["fit"] = fit
     res["W_best_measured"] = int(Ws[int(np.argmin(t))])
     res["message_bytes"] = M

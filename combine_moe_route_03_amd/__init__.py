@@ -74,10 +74,15 @@ SIGNATURES = {
                                ctypes.c_size_t, _vp], ctypes.c_int),
     "moe_combine_rows": ([_shp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe_swiglu_waves": ([_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                          ctypes.c_size_t, _vp, _vp, _vp, _vp, _i32], ctypes.c_int),
+                          ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _i32], ctypes.c_int),
     "moe_swiglu_waves_events": ([_i32], ctypes.c_int32),
-    "moe_scale_waves": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32],
-                        ctypes.c_int),
+    "moe_scale_waves": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _vp, _vp, _vp, _i32], ctypes.c_int),
+    "moe_scale_waves_events": ([_i32], ctypes.c_int32),
+    "moe_combine_order": ([_shp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "moe_combine_order_workspace_bytes": ([_shp], ctypes.c_size_t),
+    "moe_combine_waves": ([_shp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "moe_vsrc_workspace_bytes": ([_shp], ctypes.c_size_t),
     "moe_vsrc_dispatch": ([_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp], ctypes.c_int),
@@ -193,6 +198,10 @@ class Chains:
 
 def swiglu_waves_events(W: int) -> int:
     return int(lib().moe_swiglu_waves_events(W))
+
+
+def scale_waves_events(W: int) -> int:
+    return int(lib().moe_scale_waves_events(W))
 
 
 # ----------------------------------------------------------------------- route
@@ -501,18 +510,39 @@ def expert_swiglu(send_buf: torch.Tensor, expert_offsets: torch.Tensor,
     return expert_out
 
 
+def _wave_combine_args(combine: dict | None, shape: Shape, device):
+    """(topk_w, pos, token_order, token_wave_offsets, y) pointers of a
+    per-wave combine, or five NULLs; the combine stream (NULL: the copy
+    stream); y. `combine` holds topk_w, pos, the order tables of
+    combine_order(), optionally y (allocated when missing) and optionally
+    "stream", a torch stream of the combines' own."""
+    if combine is None:
+        return (None,) * 5, None, None
+    y = combine.get("y")
+    if y is None:
+        y = _empty((shape.T, shape.H), shape.dtype, device)
+    cs = combine.get("stream")
+    return ((_ptr(combine["topk_w"]), _ptr(combine["pos"]), _ptr(combine["token_order"]),
+             _ptr(combine["token_wave_offsets"]), _ptr(y)),
+            None if cs is None else ctypes.c_void_p(cs.cuda_stream), y)
+
+
 def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tensor,
                  w_down: torch.Tensor, expert_out: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None,
                  copy_stream: torch.cuda.Stream | None = None,
-                 chains: Chains | None = None) -> torch.Tensor:
+                 chains: Chains | None = None, combine: dict | None = None):
     """Wave-pipelined dispatch + SwiGLU FFN: per wave a gather of its rows into
     out["send_buf"] on `copy_stream`, then the FFN of its experts on the
     current stream after an event. `out` holds a dispatch index of `shape`
     (row_token, wave_offsets, expert offsets/counts). No copy stream: the same
     launches on the current stream. `chains` supplies the events (at least
     swiglu_waves_events(W) of them when a copy stream or a side stream is used)
-    and, when it has one, the side stream of the second chain of experts."""
+    and, when it has one, the side stream of the second chain of experts.
+    With `combine` (topk_w, pos, token_order, token_wave_offsets, optional y
+    and "stream") each wave's completed tokens are combined in the pipeline,
+    on that stream or else on the copy stream; returns (expert_out, y) then,
+    else expert_out."""
     I = w_down.shape[2]
     send_buf = out["send_buf"]
     expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
@@ -522,43 +552,84 @@ def swiglu_waves(x: torch.Tensor, out: dict, shape: Shape, w_gate_up: torch.Tens
     compute = _stream()
     copy = compute if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
     side = chains.side_ptr() if chains is not None else None
-    if (copy_stream is not None or side is not None) and (
+    cargs, cstream, y = _wave_combine_args(combine, shape, send_buf.device)
+    if (copy_stream is not None or side is not None or cstream is not None) and (
             chains is None or len(chains.events) < swiglu_waves_events(shape.W)):
-        raise ValueError(f"swiglu_waves with a copy or side stream needs a Chains with at least "
-                         f"{swiglu_waves_events(shape.W)} events")
+        raise ValueError(f"swiglu_waves with a copy, side or combine stream needs a Chains with "
+                         f"at least {swiglu_waves_events(shape.W)} events")
     events = chains.event_array() if chains is not None else None
     n_events = len(chains.events) if chains is not None else 0
     sh = shape.c()
     _check(lib().moe_swiglu_waves(
         ctypes.byref(sh), I, _ptr(x), _ptr(out["row_token"]), _ptr(out["wave_offsets"]),
         _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(w_gate_up), _ptr(w_down),
-        _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), compute, copy,
-        side, events, n_events), "moe_swiglu_waves")
-    return expert_out
+        _ptr(send_buf), _ptr(expert_out), _ptr(workspace), workspace.numel(), *cargs, compute,
+        copy, side, cstream, events, n_events), "moe_swiglu_waves")
+    return expert_out if combine is None else (expert_out, y)
 
 
 def scale_waves(x: torch.Tensor, out: dict, shape: Shape, expert_out: torch.Tensor | None = None,
                 copy_stream: torch.cuda.Stream | None = None,
-                chains: Chains | None = None) -> torch.Tensor:
+                chains: Chains | None = None, combine: dict | None = None):
     """Wave-pipelined dispatch + identity-scaled experts: per wave a gather of its
     rows into out["send_buf"] on `copy_stream`, then the (e+1) scaling of those
     rows on the current stream after an event. `out` holds a dispatch index of
-    `shape`; with a copy stream, `chains` supplies at least 1 + W events."""
+    `shape`; with a copy stream, `chains` supplies at least scale_waves_events(W)
+    events. `combine` as in swiglu_waves."""
     send_buf = out["send_buf"]
     expert_out = torch.empty_like(send_buf) if expert_out is None else expert_out
     compute = _stream()
     copy = compute if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
-    if copy_stream is not None and (chains is None or len(chains.events) < 1 + shape.W):
-        raise ValueError(f"scale_waves with a copy stream needs a Chains with at least "
-                         f"{1 + shape.W} events")
+    need = scale_waves_events(shape.W)
+    cargs, cstream, y = _wave_combine_args(combine, shape, send_buf.device)
+    if (copy_stream is not None or cstream is not None) and (
+            chains is None or len(chains.events) < need):
+        raise ValueError(f"scale_waves with a copy or combine stream needs a Chains with at "
+                         f"least {need} events")
     events = chains.event_array() if chains is not None else None
     n_events = len(chains.events) if chains is not None else 0
     sh = shape.c()
     _check(lib().moe_scale_waves(
         ctypes.byref(sh), _ptr(x), _ptr(out["row_token"]), _ptr(out["wave_offsets"]),
         _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _ptr(send_buf),
-        _ptr(expert_out), compute, copy, events, n_events), "moe_scale_waves")
-    return expert_out
+        _ptr(expert_out), *cargs, compute, copy, cstream, events, n_events), "moe_scale_waves")
+    return expert_out if combine is None else (expert_out, y)
+
+
+def combine_order_workspace_bytes(shape: Shape) -> int:
+    sh = shape.c()
+    return int(lib().moe_combine_order_workspace_bytes(ctypes.byref(sh)))
+
+
+def combine_order(pos: torch.Tensor, wave_offsets: torch.Tensor, shape: Shape,
+                  token_wave_offsets: torch.Tensor | None = None,
+                  token_order: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """Completion-wave order of the tokens: (token_wave_offsets int32 [W+1],
+    token_order int32 [T])."""
+    dev = pos.device
+    two = _empty((shape.W + 1,), torch.int32, dev) if token_wave_offsets is None \
+        else token_wave_offsets
+    order = _empty((shape.T,), torch.int32, dev) if token_order is None else token_order
+    if workspace is None:
+        workspace = _empty((max(combine_order_workspace_bytes(shape), 1),), torch.uint8, dev)
+    sh = shape.c()
+    _check(lib().moe_combine_order(ctypes.byref(sh), _ptr(pos), _ptr(wave_offsets), _ptr(two),
+                                   _ptr(order), _ptr(workspace), workspace.numel(), _stream()),
+           "moe_combine_order")
+    return two, order
+
+
+def combine_waves(expert_out: torch.Tensor, topk_w: torch.Tensor, pos: torch.Tensor,
+                  token_order: torch.Tensor, token_wave_offsets: torch.Tensor, shape: Shape,
+                  w0: int, w1: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Combine of the tokens whose completion wave lies in [w0, w1) into y."""
+    y = _empty((shape.T, shape.H), shape.dtype, expert_out.device) if y is None else y
+    sh = shape.c()
+    _check(lib().moe_combine_waves(ctypes.byref(sh), _ptr(expert_out), _ptr(topk_w), _ptr(pos),
+                                   _ptr(token_order), _ptr(token_wave_offsets), w0, w1, _ptr(y),
+                                   _stream()), "moe_combine_waves")
+    return y
 
 
 def combine(expert_out: torch.Tensor, topk_w: torch.Tensor, pos: torch.Tensor, shape: Shape,

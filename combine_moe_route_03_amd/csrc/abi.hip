@@ -106,6 +106,33 @@ size_t vsrc_workspace_bytes(const moe_shape* sh) {
   return size_t((bytes + 255) / 256 * 256);
 }
 
+// The per-wave combine's tables and the combine inputs; y == NULL means no
+// combine (then the rest may be NULL too).
+int check_wave_combine(const moe_shape* sh, const float* topk_w, const int32_t* pos,
+                       const int32_t* token_order, const int32_t* token_wave_offsets,
+                       const void* y) {
+  if (!y) return MOE_OK;
+  if (!token_wave_offsets) return MOE_ERR_ARG;
+  if (sh->T > 0 && (!topk_w || !pos || !token_order)) return MOE_ERR_ARG;
+  if (!aligned(y, 16) || !aligned(topk_w, 4) || !aligned(pos, 4) || !aligned(token_order, 4) ||
+      !aligned(token_wave_offsets, 4))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// A per-wave combine on a stream other than the compute stream (it then
+// needs the events).
+bool own_combine_stream(const void* y, moe_stream_t combine_stream, moe_stream_t compute_stream) {
+  return y && combine_stream && combine_stream != compute_stream;
+}
+
+int check_events(void* const* events, int32_t n_events, int32_t need) {
+  if (!events || n_events < need) return MOE_ERR_ARG;
+  for (int32_t i = 0; i < need; ++i)
+    if (!events[i]) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
 int check_vsrc_move(const moe_shape* sh, int32_t direction, const void* in, const void* out) {
   if (direction != 0 && direction != 1) return MOE_ERR_ARG;
   if (sh->T > 0 && (!in || !out)) return MOE_ERR_ARG;
@@ -358,10 +385,14 @@ int moe_expert_swiglu(const moe_shape* shape, int32_t I, const void* send_buf,
       static_cast<hipEvent_t>(fork_event), static_cast<hipEvent_t>(join_event)));
 }
 
+int32_t moe_scale_waves_events(int32_t W) { return W < 1 || W > (1 << 20) ? -1 : 2 + 2 * W; }
+
 int moe_scale_waves(const moe_shape* shape, const void* x, const int32_t* row_token,
                     const int32_t* wave_offsets, const int32_t* expert_offsets,
                     const int32_t* expert_counts, void* send_buf, void* expert_out,
-                    moe_stream_t compute_stream, moe_stream_t copy_stream, void* const* events,
+                    const float* topk_w, const int32_t* pos, const int32_t* token_order,
+                    const int32_t* token_wave_offsets, void* y, moe_stream_t compute_stream,
+                    moe_stream_t copy_stream, moe_stream_t combine_stream, void* const* events,
                     int32_t n_events) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
@@ -371,27 +402,31 @@ int moe_scale_waves(const moe_shape* shape, const void* x, const int32_t* row_to
       !aligned(row_token, 4) || !aligned(wave_offsets, 4) || !aligned(expert_offsets, 4) ||
       !aligned(expert_counts, 4))
     return MOE_ERR_ALIGN;
-  if (copy_stream != compute_stream) {
-    if (!events || n_events < 1 + shape->W) return MOE_ERR_ARG;
-    for (int32_t i = 0; i < 1 + shape->W; ++i)
-      if (!events[i]) return MOE_ERR_ARG;
-  }
+  if ((st = check_wave_combine(shape, topk_w, pos, token_order, token_wave_offsets, y)) != MOE_OK)
+    return st;
+  if ((copy_stream != compute_stream || own_combine_stream(y, combine_stream, compute_stream)) &&
+      (st = check_events(events, n_events, moe_scale_waves_events(shape->W))) != MOE_OK)
+    return st;
   const int64_t row_bytes = int64_t(shape->H) * elem_bytes(shape->dtype);
+  moe::WaveCombine wc;
+  if (y) wc = {topk_w, pos, token_order, token_wave_offsets, y, as_stream(combine_stream)};
   return status_of(moe::launch_scale_waves(
       x, shape->T, shape->k, row_bytes, shape->dtype, shape->H, shape->E, shape->R, shape->W,
-      row_token, wave_offsets, expert_offsets, expert_counts, send_buf, expert_out,
+      row_token, wave_offsets, expert_offsets, expert_counts, send_buf, expert_out, wc,
       as_stream(compute_stream), as_stream(copy_stream),
       reinterpret_cast<const hipEvent_t*>(events)));
 }
 
-int32_t moe_swiglu_waves_events(int32_t W) { return W < 1 || W > (1 << 20) ? -1 : 1 + 3 * W; }
+int32_t moe_swiglu_waves_events(int32_t W) { return W < 1 || W > (1 << 20) ? -1 : 2 + 4 * W; }
 
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
                      const int32_t* wave_offsets, const int32_t* expert_offsets,
                      const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
                      void* send_buf, void* expert_out, void* workspace,
-                     size_t workspace_bytes_given, moe_stream_t compute_stream,
-                     moe_stream_t copy_stream, moe_stream_t side_stream, void* const* events,
+                     size_t workspace_bytes_given, const float* topk_w, const int32_t* pos,
+                     const int32_t* token_order, const int32_t* token_wave_offsets, void* y,
+                     moe_stream_t compute_stream, moe_stream_t copy_stream,
+                     moe_stream_t side_stream, moe_stream_t combine_stream, void* const* events,
                      int32_t n_events) {
   int st = check_swiglu_args(shape, I, send_buf, expert_offsets, expert_counts, w_gate_up,
                              w_down, expert_out, workspace, workspace_bytes_given);
@@ -399,16 +434,61 @@ int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int
   if (!wave_offsets) return MOE_ERR_ARG;
   if (shape->T > 0 && (!x || !row_token)) return MOE_ERR_ARG;
   if (!aligned(x, 16) || !aligned(row_token, 4) || !aligned(wave_offsets, 4)) return MOE_ERR_ALIGN;
-  if (copy_stream != compute_stream || side_stream) {
-    if (!events || n_events < moe_swiglu_waves_events(shape->W)) return MOE_ERR_ARG;
-    for (int32_t i = 0; i < 1 + 3 * shape->W; ++i)
-      if (!events[i]) return MOE_ERR_ARG;
-  }
+  if ((st = check_wave_combine(shape, topk_w, pos, token_order, token_wave_offsets, y)) != MOE_OK)
+    return st;
+  if ((copy_stream != compute_stream || side_stream ||
+       own_combine_stream(y, combine_stream, compute_stream)) &&
+      (st = check_events(events, n_events, moe_swiglu_waves_events(shape->W))) != MOE_OK)
+    return st;
+  moe::WaveCombine wc;
+  if (y) wc = {topk_w, pos, token_order, token_wave_offsets, y, as_stream(combine_stream)};
   return status_of(moe::launch_swiglu_waves(
       x, shape->T, shape->k, shape->H, I, shape->E, shape->R, shape->W, row_token, wave_offsets,
-      expert_offsets, expert_counts, w_gate_up, w_down, send_buf, workspace, expert_out,
+      expert_offsets, expert_counts, w_gate_up, w_down, send_buf, workspace, expert_out, wc,
       as_stream(compute_stream), as_stream(copy_stream), as_stream(side_stream),
       reinterpret_cast<const hipEvent_t*>(events)));
+}
+
+size_t moe_combine_order_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  int64_t tpb, nb;
+  moe::combine_order_blocks(shape->T, shape->W, tpb, nb);
+  const int64_t bytes = nb * int64_t(shape->W) * 4;
+  return size_t((bytes + 255) / 256 * 256);
+}
+
+int moe_combine_order(const moe_shape* shape, const int32_t* pos, const int32_t* wave_offsets,
+                      int32_t* token_wave_offsets, int32_t* token_order, void* workspace,
+                      size_t workspace_bytes_given, moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!wave_offsets || !token_wave_offsets || !workspace) return MOE_ERR_ARG;
+  if (shape->T > 0 && (!pos || !token_order)) return MOE_ERR_ARG;
+  if (!aligned(pos, 4) || !aligned(wave_offsets, 4) || !aligned(token_wave_offsets, 4) ||
+      !aligned(token_order, 4) || !aligned(workspace, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_given < moe_combine_order_workspace_bytes(shape)) return MOE_ERR_WORKSPACE;
+  return status_of(moe::launch_combine_order(pos, shape->T, shape->k, wave_offsets, shape->W,
+                                             token_wave_offsets, token_order,
+                                             static_cast<int32_t*>(workspace),
+                                             as_stream(stream)));
+}
+
+int moe_combine_waves(const moe_shape* shape, const void* expert_out, const float* topk_w,
+                      const int32_t* pos, const int32_t* token_order,
+                      const int32_t* token_wave_offsets, int32_t w0, int32_t w1, void* y,
+                      moe_stream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (w0 < 0 || w1 < w0 || w1 > shape->W) return MOE_ERR_ARG;
+  if (!y) return MOE_ERR_ARG;
+  if ((st = check_wave_combine(shape, topk_w, pos, token_order, token_wave_offsets, y)) != MOE_OK)
+    return st;
+  if (shape->T > 0 && !expert_out) return MOE_ERR_ARG;
+  if (!aligned(expert_out, 16)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_combine_waves(expert_out, shape->dtype, topk_w, pos, shape->T,
+                                             shape->k, shape->H, token_order, token_wave_offsets,
+                                             w0, w1, y, as_stream(stream)));
 }
 
 int moe_combine_rows(const moe_shape* shape, int64_t rows, const void* expert_out,

@@ -14,6 +14,7 @@
 // k positions and weights can come through the scalar cache.
 #include <type_traits>
 
+#include "combine_column.h"
 #include "device.h"
 #include "launch.h"
 
@@ -21,14 +22,6 @@ namespace moe {
 namespace {
 
 constexpr int kBlock = 256;
-// Cached rows: positions through the scalar cache (rows of 64k vectors) and
-// all k gathers in flight. Streamed rows: one gather in flight per thread and
-// positions through the vector path; on k = 8 over 14 KiB rows that measured
-// 351 us against 357 (scalar positions) and 365-368 (all eight in flight),
-// and on k = 2 the same or better.
-constexpr bool kCombineUniform = true;
-constexpr bool kStreamUniform = false;
-constexpr int kStreamGroup = 1;  // gathers in flight per thread on streamed rows
 
 template <int KMAX, bool kBF16, bool kCacheIn, bool kUniform>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__ eo,
@@ -46,56 +39,9 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__
   uint32_t t = q / nvec;
   if constexpr (kUniform) t = __builtin_amdgcn_readfirstlane(t);  // whole waves: total % 64 == 0
   const uint32_t col = q - t * nvec;
-  const int32_t* pp = pos + (size_t)t * k;
-  const float* ww = w + (size_t)t * k;
-
-  // every position and weight first (one wait), then the gathers in groups of
-  // kGroup, each group issued back to back and then accumulated (pick order is
-  // kept). A pick without a row loads row 0 (discarded) instead of branching
-  // around the load, so no gather result has to land before the next issue.
-  int32_t P[KMAX];
-  float wt[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    P[i] = (i < k) ? pp[i] : -1;
-    wt[i] = (i < k) ? ww[i] : 0.f;
-  }
-  constexpr int kGroup = kCacheIn ? KMAX : kStreamGroup;
-  constexpr int G = kGroup < KMAX ? kGroup : KMAX;
-  float a[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};  // -0: additive identity
-#pragma unroll
-  for (int g0 = 0; g0 < KMAX; g0 += G) {
-    v4u v[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int i = g0 + j;
-      if (i < k) {
-        const bool ok = (uint32_t)P[i] < nrows;
-        const v4u* src = eo + (ok ? (size_t)P[i] * nvec : 0) + col;
-        v[j] = kCacheIn ? *src : load_stream(src);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int i = g0 + j;
-      if (i < k && (uint32_t)P[i] < nrows) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if constexpr (kBF16) {
-            a[2 * c] = fmaf(wt[i], bf16_lo(v[j][c]), a[2 * c]);
-            a[2 * c + 1] = fmaf(wt[i], bf16_hi(v[j][c]), a[2 * c + 1]);
-          } else {
-            a[c] = fmaf(wt[i], __uint_as_float(v[j][c]), a[c]);
-          }
-        }
-      }
-    }
-  }
-  const v4u out = kBF16 ? v4u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                              pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])}
-                        : v4u{__float_as_uint(a[0]), __float_as_uint(a[1]),
-                              __float_as_uint(a[2]), __float_as_uint(a[3])};
-  store_stream(y + q, out);
+  store_stream(y + q, combine_column<KMAX, kBF16, kCacheIn>(eo, w + (size_t)t * k,
+                                                            pos + (size_t)t * k, k, nvec, col,
+                                                            nrows));
 }
 
 template <int KMAX>

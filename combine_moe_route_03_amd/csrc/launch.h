@@ -140,6 +140,30 @@ hipError_t launch_combine(const void* expert_out, int dtype, const float* w, con
 
 hipError_t launch_stats(const int32_t* counts, int E, int R, void* out, hipStream_t s);
 
+// The wave schedule's combine: the tokens listed by completion wave (a count
+// and a place launch of nb blocks of tpb tokens; hist: [nb][W] int32
+// workspace), then the combine of the tokens of completion waves [w0, w1)
+// (the one-pass combine's arithmetic; rows are the T*k of the plain layout).
+void combine_order_blocks(int64_t T, int W, int64_t& tpb, int64_t& nb);
+hipError_t launch_combine_order(const int32_t* pos, int T, int k, const int32_t* wave_offsets,
+                                int W, int32_t* token_wave_offsets, int32_t* token_order,
+                                int32_t* hist, hipStream_t s);
+hipError_t launch_combine_waves(const void* expert_out, int dtype, const float* w,
+                                const int32_t* pos, int T, int k, int64_t H,
+                                const int32_t* token_order, const int32_t* token_wave_offsets,
+                                int w0, int w1, void* y, hipStream_t s);
+// What the wave pipelines need to combine each wave's completed tokens (y
+// null: no combine in the pipeline), and the stream for those combines (null:
+// the copy stream).
+struct WaveCombine {
+  const float* w = nullptr;
+  const int32_t* pos = nullptr;
+  const int32_t* token_order = nullptr;
+  const int32_t* token_wave_offsets = nullptr;
+  void* y = nullptr;
+  hipStream_t stream = nullptr;
+};
+
 // Virtual source shards (the emulated exchange): nsrc shards of src_picks
 // picks; hist holds nsrc * source_chunks rows of E. Each shard's counts and
 // offsets go to its own slice ([nsrc][E], [nsrc][W*R], [nsrc][W+1]); positions
@@ -204,19 +228,22 @@ hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int
                               int w, int T, int64_t rows_max, int64_t row_bytes, void* send,
                               hipStream_t s);
 // Wave-pipelined identity-scaled experts: per wave, gather dispatch of its rows
-// on `copy`, then the experts of the wave on `compute` after an event; events
-// holds at least 1 + W caller-owned events when copy != compute.
+// on `copy`, then the experts of the wave on `compute` after an event, and
+// (with wc.y) the combine of the wave's completed tokens on wc.stream, or on
+// `copy` once the next wave's gather is queued; events holds at least 2 + 2W
+// caller-owned events when a second stream is used.
 hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, int dtype, int64_t H,
                               int E, int R, int W, const int32_t* row_token,
                               const int32_t* wave_offsets, const int32_t* offs,
-                              const int32_t* cnts, void* send, void* out, hipStream_t compute,
-                              hipStream_t copy, const hipEvent_t* events);
+                              const int32_t* cnts, void* send, void* out, const WaveCombine& wc,
+                              hipStream_t compute, hipStream_t copy, const hipEvent_t* events);
+// The same with the SwiGLU experts (2 + 4W events when used).
 hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                const void* w_down, void* send, void* hbuf, void* out,
-                               hipStream_t compute, hipStream_t copy, hipStream_t side,
-                               const hipEvent_t* events);
+                               const WaveCombine& wc, hipStream_t compute, hipStream_t copy,
+                               hipStream_t side, const hipEvent_t* events);
 
 // Expert id of the j-th bucket when buckets run in (wave, rank, slot) order:
 // L = E / R slots per rank, LW = L / W slots per wave.

@@ -11,9 +11,12 @@
 // bound) runs under the FFN of wave w (MFMA bound). Where the wave's experts
 // split into even and odd slots, the odd ones run on the caller's side stream
 // forked from the compute stream and joined back, as the unpipelined FFN does;
-// every stream and event is the caller's (the library keeps none). The
-// combine runs once, after the last wave, with the same arithmetic as the
-// unpipelined path.
+// every stream and event is the caller's (the library keeps none). With a
+// combine in the pipeline, the tokens completed by wave w (all their experts
+// in waves <= w) are combined after wave w's experts: on a combine stream of
+// their own at once, or on the copy stream behind the gather of wave w+1 (the
+// page asks that a wave's dispatch never wait behind a combine); the tokens'
+// bits equal the one-pass combine's.
 #include "device.h"
 #include "launch.h"
 
@@ -70,18 +73,76 @@ hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int
                 row_token, wave_offsets, w, T, rows_max, nvec, static_cast<v4u*>(send));
 }
 
+namespace {
+
+// The combine of the tokens completed by wave w on `cs`, once the event
+// `done` (wave w's experts, recorded on the compute stream) has fired.
+hipError_t combine_wave(const WaveCombine& wc, const void* out, int dtype, int T, int k, int64_t H,
+                        int w, bool sep, hipEvent_t done, hipStream_t cs) {
+  if (sep) {
+    const hipError_t e = hipStreamWaitEvent(cs, done, 0);
+    if (e != hipSuccess) return e;
+  }
+  return launch_combine_waves(out, dtype, wc.w, wc.pos, T, k, H, wc.token_order,
+                              wc.token_wave_offsets, w, w + 1, wc.y, cs);
+}
+
+// Wave w's experts are queued on `compute`: record `done` there. On a
+// combine stream of its own, the tokens completed by wave w are combined at
+// once; on the copy stream, the tokens completed by wave w - 1 (done_prev),
+// behind the gather of wave w already queued there, so a gather never waits
+// behind a combine of a later wave.
+hipError_t after_experts(const WaveCombine& wc, const void* out, int dtype, int T, int k,
+                         int64_t H, int w, hipEvent_t done, hipEvent_t done_prev,
+                         hipStream_t compute, hipStream_t copy) {
+  if (wc.y == nullptr) return hipSuccess;
+  const hipStream_t cs = wc.stream ? wc.stream : copy;
+  const bool sep = cs != compute;
+  if (sep) {
+    const hipError_t e = hipEventRecord(done, compute);
+    if (e != hipSuccess) return e;
+  }
+  if (cs != copy) return combine_wave(wc, out, dtype, T, k, H, w, sep, done, cs);
+  if (w == 0) return hipSuccess;
+  return combine_wave(wc, out, dtype, T, k, H, w - 1, sep, done_prev, cs);
+}
+
+// On the copy stream, the last wave's completed tokens; then the compute
+// stream joins the combine stream (everything of the call is on `compute`
+// when it returns).
+hipError_t finish_combine(const WaveCombine& wc, const void* out, int dtype, int T, int k,
+                          int64_t H, int W, hipEvent_t done_last, hipEvent_t join,
+                          hipStream_t compute, hipStream_t copy) {
+  if (wc.y == nullptr) return hipSuccess;
+  const hipStream_t cs = wc.stream ? wc.stream : copy;
+  const bool sep = cs != compute;
+  hipError_t e = hipSuccess;
+  if (cs == copy && (e = combine_wave(wc, out, dtype, T, k, H, W - 1, sep, done_last, cs)) !=
+                        hipSuccess)
+    return e;
+  if (!sep) return hipSuccess;
+  if ((e = hipEventRecord(join, cs)) != hipSuccess) return e;
+  return hipStreamWaitEvent(compute, join, 0);
+}
+
+}  // namespace
+
 // The identity-scaled experts of the synthetic workloads in the same
 // schedule: per wave its gather dispatch on the copy stream, an event, and
 // the wave's experts on the compute stream (bit-identical to the one-pass copy
 // and expert stage: both are bit copies and the same per-element product).
+// events: [0] copy start, [1..W] gathers, [1+W+w] wave w's experts done,
+// [1+2W] the final join.
 hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, int dtype, int64_t H,
                               int E, int R, int W, const int32_t* row_token,
                               const int32_t* wave_offsets, const int32_t* offs,
-                              const int32_t* cnts, void* send, void* out, hipStream_t compute,
-                              hipStream_t copy, const hipEvent_t* events) {
+                              const int32_t* cnts, void* send, void* out, const WaveCombine& wc,
+                              hipStream_t compute, hipStream_t copy, const hipEvent_t* events) {
   const int64_t rows = (int64_t)T * k;
   if (rows == 0) return hipSuccess;
   const bool two = copy != compute;
+  // the events a combine on a stream of its own uses (null when none is needed)
+  const auto ev = [&](int i) { return events ? events[i] : nullptr; };
   hipError_t e = hipSuccess;
   if (two) {
     if ((e = hipEventRecord(events[0], compute)) != hipSuccess) return e;
@@ -97,16 +158,20 @@ hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, in
     e = launch_expert_scale_wave(send, dtype, rows, H, E, R, W, offs, cnts, wave_offsets, w, out,
                                  compute);
     if (e != hipSuccess) return e;
+    e = after_experts(wc, out, dtype, T, k, H, w, ev(1 + W + w), ev(W + w), compute, copy);
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return finish_combine(wc, out, dtype, T, k, H, W, ev(2 * W), ev(1 + 2 * W), compute, copy);
 }
 
+// events: [0] copy start, [1..W] gathers, [1+W+2w] / [2+W+2w] wave w's fork
+// and join, [1+3W+w] wave w's experts done, [1+4W] the final join.
 hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
                                const void* w_down, void* send, void* hbuf, void* out,
-                               hipStream_t compute, hipStream_t copy, hipStream_t side,
-                               const hipEvent_t* events) {
+                               const WaveCombine& wc, hipStream_t compute, hipStream_t copy,
+                               hipStream_t side, const hipEvent_t* events) {
   const int64_t rows = (int64_t)T * k;
   if (rows == 0) return hipSuccess;
   const int L = E / R, LW = L / W;
@@ -120,8 +185,8 @@ hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E,
   // 1632 (the fork and join cost more than the overlap gives). Otherwise one
   // chain.
   const bool chains = side != nullptr && R * LW >= 8 && (R == 1 || W == 1);
+  const auto ev = [&](int i) { return events ? events[i] : nullptr; };
   hipError_t e = hipSuccess;
-  // events: [0] copy start, [1..W] gathers, then a fork and a join per wave
   if (two) {
     // the copy stream starts after everything already queued on the compute
     // stream (the index stage that wrote row_token and wave_offsets)
@@ -140,23 +205,25 @@ hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E,
       e = launch_expert_swiglu_subset(send, rows, H, I, R * LW, LW, L, w * LW, offs, cnts,
                                       w_gate_up, w_down, hbuf, out, compute);
       if (e != hipSuccess) return e;
-      continue;
+    } else {
+      // the wave's experts w*LW + 2i + c (R == 1), or 2i + c (W == 1), as two
+      // chains: c = 0 on the compute stream, c = 1 on the side stream
+      hipEvent_t fork = events[1 + W + 2 * w], join = events[2 + W + 2 * w];
+      if ((e = hipEventRecord(fork, compute)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
+      const int n = R * LW;
+      for (int c = 0; c < 2; ++c) {
+        e = launch_expert_swiglu_subset(send, rows, H, I, (n - c + 1) / 2, 1, 2, w * LW + c, offs,
+                                        cnts, w_gate_up, w_down, hbuf, out, c ? side : compute);
+        if (e != hipSuccess) return e;
+      }
+      if ((e = hipEventRecord(join, side)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(compute, join, 0)) != hipSuccess) return e;
     }
-    // the wave's experts w*LW + 2i + c (R == 1), or 2i + c (W == 1), as two
-    // chains: c = 0 on the compute stream, c = 1 on the side stream
-    hipEvent_t fork = events[1 + W + 2 * w], join = events[2 + W + 2 * w];
-    if ((e = hipEventRecord(fork, compute)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
-    const int n = R * LW;
-    for (int c = 0; c < 2; ++c) {
-      e = launch_expert_swiglu_subset(send, rows, H, I, (n - c + 1) / 2, 1, 2, w * LW + c, offs,
-                                      cnts, w_gate_up, w_down, hbuf, out, c ? side : compute);
-      if (e != hipSuccess) return e;
-    }
-    if ((e = hipEventRecord(join, side)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(compute, join, 0)) != hipSuccess) return e;
+    e = after_experts(wc, out, 1, T, k, H, w, ev(1 + 3 * W + w), ev(3 * W + w), compute, copy);
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return finish_combine(wc, out, 1, T, k, H, W, ev(4 * W), ev(1 + 4 * W), compute, copy);
 }
 
 }  // namespace moe

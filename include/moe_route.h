@@ -352,61 +352,122 @@ int moe_stats(const int32_t* expert_counts, int32_t E, int32_t R,
 int moe_dirichlet_alpha(const int32_t* expert_counts, int32_t E, double* alpha_out,
                         moe_stream_t stream);
 
+/* Completion-wave order of the tokens, for the combine of the wave schedule
+ * (irregular AllToAll page, "Wave-Scheduled" pipelining: each wave runs
+ * dispatch -> compute -> combine). A token's weighted sum needs all its kept
+ * picks' expert outputs, so it is complete after the last wave holding one of
+ * its rows: the wave of its largest position, where row r is in the largest
+ * wave w with wave_offsets[w] <= r (picks with pos outside [0, T*k) do not
+ * count; a token with none is complete before any wave, wave 0).
+ * pos [T][k], wave_offsets [W+1]: as written by a dispatch-index call with the
+ *   same shape (DEVICE, in).
+ * token_wave_offsets [W+1] out: first entry of each wave's tokens (last = T).
+ * token_order [T] out: the tokens wave by wave, ascending id within a wave.
+ * workspace: device scratch of moe_combine_order_workspace_bytes(shape) bytes
+ *   (contents need not be initialised; clobbered by the call).
+ * Two launches (a count and a place pass over blocks of tokens).
+ * Errors: MOE_ERR_ARG (null pointers, shape), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE,
+ *         MOE_ERR_DEVICE. */
+int moe_combine_order(const moe_shape* shape, const int32_t* pos, const int32_t* wave_offsets,
+                      int32_t* token_wave_offsets, int32_t* token_order, void* workspace,
+                      size_t workspace_bytes, moe_stream_t stream);
+
+/* Bytes of device workspace moe_combine_order needs for this shape (host-only,
+ * pure; 0 for an invalid shape; at most 2 MiB). */
+size_t moe_combine_order_workspace_bytes(const moe_shape* shape);
+
+/* The combine of the tokens whose completion wave lies in [w0, w1) (entries
+ * token_wave_offsets[w0] .. token_wave_offsets[w1] of token_order, from
+ * moe_combine_order): y[t] for those tokens, with moe_combine's arithmetic,
+ * so each token's bits equal moe_combine's; other rows of y are untouched.
+ * Over w0..w1 = 0..W, in one call or any split, it writes all of y.
+ * expert_out [T*k][H] (the plain layout), topk_w [T][k], pos [T][k], y [T][H].
+ * Errors: MOE_ERR_ARG (null pointers, 0 <= w0 <= w1 <= W violated),
+ *         MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
+int moe_combine_waves(const moe_shape* shape, const void* expert_out, const float* topk_w,
+                      const int32_t* pos, const int32_t* token_order,
+                      const int32_t* token_wave_offsets, int32_t w0, int32_t w1, void* y,
+                      moe_stream_t stream);
+
 /* Wave-pipelined local layer (irregular AllToAll page, "Wave-Scheduled"
- * pipelining: the experts in W waves, each wave's dispatch -> compute, the
- * next wave's dispatch overlapping this wave's compute). Wave w owns local
- * slots [w*L/W, (w+1)*L/W) of every rank, i.e. the send rows
+ * pipelining: the experts in W waves, each wave's dispatch -> compute ->
+ * combine, the next wave's dispatch overlapping this wave's compute). Wave w
+ * owns local slots [w*L/W, (w+1)*L/W) of every rank, i.e. the send rows
  * [wave_offsets[w], wave_offsets[w+1]) written by a dispatch-index call with
  * the same shape. For each wave, in order: on copy_stream the gather dispatch
  * send_buf[r] = x[row_token[r]] of the wave's rows, an event, and on
  * compute_stream (after that event) the moe_expert_swiglu arithmetic on the
- * wave's R*L/W experts. Results are bit-identical to moe_dispatch_copy +
- * moe_expert_swiglu. copy_stream first waits for the work already queued on
+ * wave's R*L/W experts; with y non-NULL, then the combine of the tokens
+ * completed by this wave, after an event on compute_stream: on
+ * combine_stream when it is non-NULL (at once), else on copy_stream behind
+ * the next wave's gather (the page asks that a wave's dispatch never wait
+ * behind a combine; a stream of its own keeps the two apart).
+ * Results are bit-identical to moe_dispatch_copy + moe_expert_swiglu (+
+ * moe_combine). copy_stream first waits for the work already queued on
  * compute_stream; when this call returns, compute_stream carries every wave's
- * FFN (follow with moe_combine there). copy_stream == compute_stream runs the
- * same launches serialised. With side_stream non-NULL, a wave whose experts
- * split into even and odd slots as one stride-2 run of ids each (R == 1, or
- * W == 1) and that holds at least eight experts runs the odd ones on
- * side_stream, forked from compute_stream after the wave's event and joined
- * back into it (as in moe_expert_swiglu).
+ * FFN and, with y, joins the last combine (without y, follow with moe_combine
+ * there). copy_stream == compute_stream runs the same
+ * launches serialised. With side_stream non-NULL, a wave whose experts split
+ * into even and odd slots as one stride-2 run of ids each (R == 1, or W == 1)
+ * and that holds at least eight experts runs the odd ones on side_stream,
+ * forked from compute_stream after the wave's event and joined back into it
+ * (as in moe_expert_swiglu).
+ * y, topk_w, pos, token_order, token_wave_offsets: the per-wave combine
+ * (as moe_combine_waves; token tables from moe_combine_order); y NULL: no
+ * combine (the others may be NULL then).
  * events: n_events caller-owned hipEvent_t handles, at least
- * moe_swiglu_waves_events(W) = 1 + 3W of them whenever copy_stream !=
- * compute_stream or side_stream is non-NULL (one to start the copy stream, one
- * per gather, a fork and a join per wave); unused otherwise. Streams and
- * events are the caller's, on one device. Arguments otherwise as
- * moe_expert_swiglu, plus x [T][H], row_token [T*k], wave_offsets [W+1]
- * (DEVICE). W gathers and 2W FFN kernels, or 4W with the two chains.
+ * moe_swiglu_waves_events(W) = 2 + 4W of them whenever copy_stream !=
+ * compute_stream, side_stream is non-NULL, or y and a combine_stream other
+ * than compute_stream are given (one to start the copy stream, one per
+ * gather, a fork and a join per wave, one per wave's experts and a final
+ * join); unused otherwise. Streams and events are the caller's, on one device.
+ * Arguments otherwise as moe_expert_swiglu, plus x [T][H], row_token [T*k],
+ * wave_offsets [W+1] (DEVICE). W gathers, 2W FFN kernels (4W with the two
+ * chains) and W combines with y.
  * Errors: as moe_expert_swiglu; MOE_ERR_ARG also for null x / row_token /
- *         wave_offsets, and for too few (or null) events when they are used. */
+ *         wave_offsets / combine tables with y, and for too few (or null)
+ *         events when they are used. */
 int moe_swiglu_waves(const moe_shape* shape, int32_t I, const void* x, const int32_t* row_token,
                      const int32_t* wave_offsets, const int32_t* expert_offsets,
                      const int32_t* expert_counts, const void* w_gate_up, const void* w_down,
                      void* send_buf, void* expert_out, void* workspace, size_t workspace_bytes,
-                     moe_stream_t compute_stream, moe_stream_t copy_stream,
-                     moe_stream_t side_stream, void* const* events, int32_t n_events);
+                     const float* topk_w, const int32_t* pos, const int32_t* token_order,
+                     const int32_t* token_wave_offsets, void* y, moe_stream_t compute_stream,
+                     moe_stream_t copy_stream, moe_stream_t side_stream,
+                     moe_stream_t combine_stream, void* const* events, int32_t n_events);
 
 /* The same wave schedule with the identity-scaled experts of moe_expert_scale
  * (the experts of the synthetic workloads): for each wave w, on copy_stream
  * the gather dispatch send_buf[r] = x[row_token[r]] of rows [wave_offsets[w],
  * wave_offsets[w+1]), an event, and on compute_stream the (e+1) scaling of
- * those rows into expert_out. Results are bit-identical to moe_dispatch_copy +
- * moe_expert_scale (follow with moe_combine on compute_stream). copy_stream
- * first waits for the work already queued on compute_stream; copy_stream ==
- * compute_stream runs the same launches serialised. events: at least 1 + W
- * caller-owned hipEvent_t handles when the streams differ (unused otherwise).
- * 2W launches. row_token, wave_offsets, expert_offsets, expert_counts as
+ * those rows into expert_out; with y non-NULL the per-wave combine as in
+ * moe_swiglu_waves (on combine_stream, or behind the next gather on
+ * copy_stream when it is NULL). Results are bit-identical to moe_dispatch_copy +
+ * moe_expert_scale (+ moe_combine; without y follow with moe_combine on
+ * compute_stream). copy_stream first waits for the work already queued on
+ * compute_stream; copy_stream == compute_stream runs the same launches
+ * serialised. events: at least moe_scale_waves_events(W) = 2 + 2W caller-owned
+ * hipEvent_t handles when copy_stream != compute_stream, or y and a
+ * combine_stream other than compute_stream are given (unused otherwise). 2W launches,
+ * 3W with y. row_token, wave_offsets, expert_offsets, expert_counts as
  * written by a dispatch-index call with the same shape (DEVICE).
  * Errors: MOE_ERR_ARG (null pointers, too few or null events), MOE_ERR_ALIGN,
  *         MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 int moe_scale_waves(const moe_shape* shape, const void* x, const int32_t* row_token,
                     const int32_t* wave_offsets, const int32_t* expert_offsets,
                     const int32_t* expert_counts, void* send_buf, void* expert_out,
-                    moe_stream_t compute_stream, moe_stream_t copy_stream, void* const* events,
+                    const float* topk_w, const int32_t* pos, const int32_t* token_order,
+                    const int32_t* token_wave_offsets, void* y, moe_stream_t compute_stream,
+                    moe_stream_t copy_stream, moe_stream_t combine_stream, void* const* events,
                     int32_t n_events);
 
-/* Events moe_swiglu_waves needs for W waves: 1 + 3W (-1 for W outside
+/* Events moe_swiglu_waves needs for W waves: 2 + 4W (-1 for W outside
  * [1, 2^20]). Host-only, pure. */
 int32_t moe_swiglu_waves_events(int32_t W);
+
+/* Events moe_scale_waves needs for W waves: 2 + 2W (-1 for W outside
+ * [1, 2^20]). Host-only, pure. */
+int32_t moe_scale_waves_events(int32_t W);
 
 /* ---------------------------------------------------------------------------
  * Virtual-source exchange: the expert-parallel exchange of R ranks emulated on

@@ -240,6 +240,9 @@ def test_vsrc_validation_and_workspace():
     assert 3 * 256 * 32 * 4 <= L.moe_vsrc_workspace_bytes(ctypes.byref(big)) < 1 << 20
 
 
+NO_COMBINE = [None] * 5  # topk_w, pos, token_order, token_wave_offsets, y
+
+
 def test_swiglu_waves_validation():
     L = moe.lib()
     sh = _shape(T=64, H=256, E=8, k=2, R=1, W=2)
@@ -247,23 +250,32 @@ def test_swiglu_waves_validation():
     # x, row_token, wave_offsets, offsets, counts, w_gate_up, w_down, send, out, workspace
     a = [FAKE] * 10
     ok = lambda *v: L.moe_swiglu_waves(ctypes.byref(v[0]), v[1], *v[2], ws if len(v) < 4 else v[3],  # noqa: E731
-                                       None, None, None, None, 0)
+                                       *NO_COMBINE, None, None, None, None, None, 0)
     assert ok(sh, 100, a) == ARG                              # I % 64 != 0
     assert ok(_shape(T=64, H=256, E=8, k=2, R=1, W=2, dtype=moe.MOE_F32), 128, a) == UNSUPPORTED
     assert ok(sh, 128, [FAKE, FAKE, None] + a[3:]) == ARG     # no wave_offsets
     assert ok(sh, 128, [None] + a[1:]) == ARG                 # no x
     assert ok(sh, 128, [ctypes.c_void_p((1 << 20) + 4)] + a[1:]) == ALIGN
     assert ok(sh, 128, a, ws - 1) == WORKSPACE
-    # a copy or side stream needs 1 + 3W caller events, none of them null
-    assert L.moe_swiglu_waves_events(2) == 7
+    # a copy or side stream needs 2 + 4W caller events, none of them null
+    assert L.moe_swiglu_waves_events(2) == 10
     assert L.moe_swiglu_waves_events(0) == -1
-    evs = (ctypes.c_void_p * 7)(*[FAKE] * 7)
-    waves = lambda copy, side, ev, n: L.moe_swiglu_waves(  # noqa: E731
-        ctypes.byref(sh), 128, *a, ws, None, copy, side, ev, n)
+    evs = (ctypes.c_void_p * 10)(*[FAKE] * 10)
+    waves = lambda copy, side, ev, n, c=NO_COMBINE, cs=None: L.moe_swiglu_waves(  # noqa: E731
+        ctypes.byref(sh), 128, *a, ws, *c, None, copy, side, cs, ev, n)
     assert waves(FAKE, None, None, 0) == ARG
-    assert waves(None, FAKE, evs, 6) == ARG
-    holes = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
-    assert waves(FAKE, None, holes, 7) == ARG
+    assert waves(None, FAKE, evs, 9) == ARG
+    holes = (ctypes.c_void_p * 10)(*([FAKE] * 9 + [None]))
+    assert waves(FAKE, None, holes, 10) == ARG
+    # with y, the combine's tables and inputs must be there
+    for i in range(4):
+        c = [FAKE] * 5
+        c[i] = None
+        assert waves(None, None, None, 0, c) == ARG, i
+    c = [FAKE] * 4 + [ctypes.c_void_p((1 << 20) + 8)]  # y not 16-byte aligned
+    assert waves(None, None, None, 0, c) == ALIGN
+    # a combine stream of its own needs the events too (without y it is ignored)
+    assert waves(None, None, None, 0, [FAKE] * 5, FAKE) == ARG
 
 
 def test_noalloc_dispatch_validation():
@@ -308,16 +320,60 @@ def test_scale_waves_validation():
     L = moe.lib()
     sh = _shape(T=64, H=256, E=8, k=2, R=1, W=2)
     a = [FAKE] * 7  # x, row_token, wave_offsets, expert_offsets, expert_counts, send, out
-    evs = (ctypes.c_void_p * 3)(*[FAKE] * 3)
-    go = lambda a, copy, ev, n: L.moe_scale_waves(ctypes.byref(sh), *a, None, copy, ev, n)  # noqa: E731
+    assert L.moe_scale_waves_events(2) == 6
+    assert L.moe_scale_waves_events(0) == -1
+    evs = (ctypes.c_void_p * 6)(*[FAKE] * 6)
+    go = lambda a, copy, ev, n, c=NO_COMBINE, cs=None: L.moe_scale_waves(  # noqa: E731
+        ctypes.byref(sh), *a, *c, None, copy, cs, ev, n)
     for i in range(7):
         b = list(a)
         b[i] = None
         assert go(b, None, None, 0) == ARG, i
-    assert go(a, FAKE, None, 0) == ARG          # a copy stream needs 1 + W events
-    assert go(a, FAKE, evs, 2) == ARG
-    holes = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
-    assert go(a, FAKE, holes, 3) == ARG
+    assert go(a, FAKE, None, 0) == ARG          # a copy stream needs 2 + 2W events
+    assert go(a, FAKE, evs, 5) == ARG
+    holes = (ctypes.c_void_p * 6)(FAKE, None, FAKE, FAKE, FAKE, FAKE)
+    assert go(a, FAKE, holes, 6) == ARG
     b = list(a)
     b[0] = ctypes.c_void_p((1 << 20) + 4)
     assert go(b, None, None, 0) == ALIGN
+    for i in range(4):
+        c = [FAKE] * 5
+        c[i] = None
+        assert go(a, None, None, 0, c) == ARG, i
+    assert go(a, None, None, 0, [FAKE] * 5, FAKE) == ARG   # own combine stream: events
+
+
+def test_combine_order_and_waves_validation():
+    L = moe.lib()
+    sh = _shape(T=64, H=256, E=8, k=2, R=1, W=2)
+    ws = L.moe_combine_order_workspace_bytes(ctypes.byref(sh))
+    assert 0 < ws <= 2 << 20
+    # the largest shapes stay within 2 MiB: at most min(512, 65536 / W) blocks
+    for big in (_shape(T=1 << 20, H=16, E=1024, k=1, R=1, W=1024),
+                _shape(T=1 << 20, H=16, E=64, k=1, R=1, W=1)):
+        assert 0 < L.moe_combine_order_workspace_bytes(ctypes.byref(big)) <= 2 << 20
+    # pos, wave_offsets, token_wave_offsets, token_order, workspace
+    a = [FAKE] * 5
+    order = lambda a, n=ws: L.moe_combine_order(ctypes.byref(sh), *a, n, None)  # noqa: E731
+    for i in range(5):
+        b = list(a)
+        b[i] = None
+        assert order(b) == ARG, i
+    b = list(a)
+    b[0] = ctypes.c_void_p((1 << 20) + 2)
+    assert order(b) == ALIGN
+    assert order(a, ws - 1) == WORKSPACE
+    assert L.moe_combine_order(None, *a, ws, None) == ARG
+    # expert_out, topk_w, pos, token_order, token_wave_offsets | w0, w1 | y
+    c = [FAKE] * 5
+    cw = lambda c, w0, w1, y=FAKE: L.moe_combine_waves(ctypes.byref(sh), *c, w0, w1, y, None)  # noqa: E731
+    for w0, w1 in ((-1, 1), (1, 0), (0, 3), (2, 3)):
+        assert cw(c, w0, w1) == ARG, (w0, w1)
+    for i in range(5):
+        d = list(c)
+        d[i] = None
+        assert cw(d, 0, 2) == ARG, i
+    assert cw(c, 0, 2, None) == ARG
+    assert cw(c, 0, 2, ctypes.c_void_p((1 << 20) + 8)) == ALIGN
+    d = [ctypes.c_void_p((1 << 20) + 8)] + c[1:]
+    assert cw(d, 0, 2) == ALIGN

@@ -77,8 +77,8 @@ def test_graph_replay_default_step():
 def test_graph_replay_decode_step():
     """The decode step as the benchmark's --fused path runs it: routing, the
     one-launch dispatch with its statistics block, experts, combine; and the
-    wave-pipelined identity-scaled experts on two streams (dirichlet_waves
-    layout, W = 8) in the same graph."""
+    wave-pipelined identity-scaled experts on two streams with the per-wave
+    combine on a third (dirichlet_waves layout, W = 8) in the same graph."""
     wl = synth.WORKLOADS["decode_hot"]
     print(f"[graph] decode step: T={wl.T} H={wl.H} E={wl.E} k={wl.k}", flush=True)
     shape = shape_of(wl)
@@ -97,8 +97,10 @@ def test_graph_replay_decode_step():
     w_w = torch.empty((wv.T, wv.k), dtype=torch.float32, device=DEV)
     eo_w = torch.empty_like(out_w["send_buf"])
     y_w = torch.empty((wv.T, wv.H), dtype=torch.bfloat16, device=DEV)
-    copy = torch.cuda.Stream()
-    chains = moe.Chains(n_events=1 + wv.W, side=False)
+    two_w = torch.empty((wv.W + 1,), dtype=torch.int32, device=DEV)
+    order_w = torch.empty((wv.T,), dtype=torch.int32, device=DEV)
+    copy, cstream = torch.cuda.Stream(), torch.cuda.Stream()
+    chains = moe.Chains(n_events=moe.scale_waves_events(wv.W), side=False)
     out2 = moe.alloc_dispatch(shape, DEV)
     idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
 
@@ -108,8 +110,10 @@ def test_graph_replay_decode_step():
                          expert_out=eo)
         moe.combine(eo, w, out["pos"], shape, y=y)
         moe.route_index(logits_w, shape_w, out_w, idx_w, w_w)
-        moe.scale_waves(x_w, out_w, shape_w, expert_out=eo_w, copy_stream=copy, chains=chains)
-        moe.combine(eo_w, w_w, out_w["pos"], shape_w, y=y_w)
+        moe.combine_order(out_w["pos"], out_w["wave_offsets"], shape_w, two_w, order_w)
+        moe.scale_waves(x_w, out_w, shape_w, expert_out=eo_w, copy_stream=copy, chains=chains,
+                        combine=dict(topk_w=w_w, pos=out_w["pos"], token_order=order_w,
+                                     token_wave_offsets=two_w, y=y_w, stream=cstream))
 
     def noise():
         moe.route_dispatch(logits, x, shape, out2, idx2, w2)
@@ -117,7 +121,7 @@ def test_graph_replay_decode_step():
     n, nw = wl.T * wl.k, wv.T * wv.k
     outputs = [idx, w, raw, out["expert_counts"], out["expert_offsets"], out["rank_counts"],
                out["rank_offsets"], out["wave_offsets"], out["pos"], out["row_token"][:n],
-               out["send_buf"], eo, y, out_w["send_buf"][:nw], eo_w[:nw], y_w]
+               out["send_buf"], eo, y, out_w["send_buf"][:nw], eo_w[:nw], y_w, two_w, order_w]
     _replays_match(step, outputs, noise)
 
 

@@ -6,7 +6,8 @@ Bars: the gathered send rows bit-exact against the oracle's dispatch; the
 expert rows bit-identical to the unpipelined moe_expert_swiglu on the same send
 buffer (same per-element MFMA arithmetic) and within the FFN tolerance of the
 oracle's fp64 SwiGLU (its rounding bound); the combined tokens bit-identical to
-the unpipelined path."""
+the unpipelined path, also when each wave's completed tokens are combined in
+the pipeline."""
 import numpy as np
 import pytest
 import torch
@@ -36,19 +37,31 @@ def _plain(wl, x, gu, dn, idx, w):
     return shape, out, eo, y
 
 
-def _waves(wl, x, gu, dn, idx, w, two_streams, side=True):
-    """two_streams: gathers on a copy stream; side: the caller's side stream for
-    the second chain of a wave's experts (with neither, no events at all)."""
+def _waves(wl, x, gu, dn, idx, w, two_streams, side=True, in_pipe=None):
+    """two_streams: gathers on a copy stream; side: the caller's side stream
+    for the second chain of a wave's experts (with neither, no events at all);
+    in_pipe: each wave's completed tokens combined in the pipeline instead of
+    one combine afterwards, on the copy stream ("copy") or on a stream of their
+    own ("own")."""
     shape = moe.Shape(wl.T, wl.H, wl.E, wl.k, wl.R, wl.W, torch.bfloat16)
     out = moe.alloc_dispatch(shape, DEV)
     out["send_buf"].fill_(0)
     moe.dispatch_index(dev(idx), shape, out)
     copy = torch.cuda.Stream() if two_streams else None
     chains = (moe.Chains(n_events=moe.swiglu_waves_events(wl.W), side=side)
-              if two_streams or side else None)
-    xd = dev(x)
-    eo = moe.swiglu_waves(xd, out, shape, dev(gu), dev(dn), copy_stream=copy, chains=chains)
-    y = moe.combine(eo, dev(w.astype(np.float32)), out["pos"], shape)
+              if two_streams or side or in_pipe == "own" else None)
+    xd, wd = dev(x), dev(w.astype(np.float32))
+    if in_pipe:
+        two, order = moe.combine_order(out["pos"], out["wave_offsets"], shape)
+        y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device=DEV)
+        comb = dict(topk_w=wd, pos=out["pos"], token_order=order, token_wave_offsets=two, y=y)
+        if in_pipe == "own":
+            comb["stream"] = torch.cuda.Stream()
+        eo, y = moe.swiglu_waves(xd, out, shape, dev(gu), dev(dn), copy_stream=copy,
+                                 chains=chains, combine=comb)
+    else:
+        eo = moe.swiglu_waves(xd, out, shape, dev(gu), dev(dn), copy_stream=copy, chains=chains)
+        y = moe.combine(eo, wd, out["pos"], shape)
     torch.cuda.synchronize()
     return out, eo, y
 
@@ -61,14 +74,16 @@ CASES = [("R1_W1", 1, 1), ("R1_W2", 1, 2), ("R1_W4", 1, 4), ("R1_W16", 1, 16), (
 
 
 @pytest.mark.parametrize("name,R,W", CASES)
-@pytest.mark.parametrize("two_streams,side", [(True, True), (False, True), (False, False)])
-def test_wave_pipeline_matches_plain_and_oracle(name, R, W, two_streams, side):
+@pytest.mark.parametrize("two_streams,side,in_pipe", [
+    (True, True, None), (False, True, None), (False, False, None), (True, True, "copy"),
+    (False, False, "copy"), (True, True, "own"), (False, False, "own")])
+def test_wave_pipeline_matches_plain_and_oracle(name, R, W, two_streams, side, in_pipe):
     wl = synth.WORKLOADS["local_layer"].with_(T=1024, H=256, I=128, R=R, W=W, seed=11)
-    print(f"[waves] {name} two_streams={two_streams} side={side}: T={wl.T} H={wl.H} E={wl.E} "
-          f"I={wl.I}", flush=True)
+    print(f"[waves] {name} two_streams={two_streams} side={side} in_pipe={in_pipe}: T={wl.T} "
+          f"H={wl.H} E={wl.E} I={wl.I}", flush=True)
     x, gu, dn, idx, w = _setup(wl)
     shape, plain, eo_p, y_p = _plain(wl, x, gu, dn, idx, w)
-    out, eo, y = _waves(wl, x, gu, dn, idx, w, two_streams, side)
+    out, eo, y = _waves(wl, x, gu, dn, idx, w, two_streams, side, in_pipe)
     ref = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
     n = ref["nrows"]
     np.testing.assert_array_equal(host(out["send_buf"])[:n], ref["send_buf"])
@@ -113,18 +128,20 @@ SCALE_CASES = [("dirichlet_shape_W8", 32, 8, 1024, 256), ("dirichlet_shape_W1", 
 
 
 @pytest.mark.parametrize("name,R,W,T,H", SCALE_CASES)
-@pytest.mark.parametrize("two_streams", [True, False])
-def test_scale_waves_match_plain(name, R, W, T, H, two_streams):
+@pytest.mark.parametrize("two_streams,in_pipe", [(True, None), (False, None), (True, "copy"),
+                                                 (False, "copy"), (True, "own"), (False, "own")])
+def test_scale_waves_match_plain(name, R, W, T, H, two_streams, in_pipe):
     """moe_scale_waves (per wave: gather dispatch on a copy stream, the wave's
-    identity-scaled experts on the compute stream) against moe_dispatch_copy +
-    moe_expert_scale and the oracle: send rows, expert rows and the combine
-    after it, bit for bit."""
+    identity-scaled experts on the compute stream, with in_pipe the combine of
+    the wave's completed tokens) against moe_dispatch_copy + moe_expert_scale
+    + moe_combine and the oracle: send rows, expert rows and the combined
+    tokens, bit for bit."""
     base = synth.WORKLOADS["dirichlet_waves"] if R == 32 else synth.WORKLOADS["zipf"]
     dt = "f32" if name.endswith("f32") else "bf16"
     E = 256 if R == 32 else 64
     wl = base.with_(T=T, H=H, E=E, R=R, W=W, dtype=dt, seed=7)
-    print(f"[scale waves] {name} two_streams={two_streams}: T={T} H={H} E={E} k={wl.k} R={R} "
-          f"W={W} {dt}", flush=True)
+    print(f"[scale waves] {name} two_streams={two_streams} in_pipe={in_pipe}: T={T} H={H} E={E} "
+          f"k={wl.k} R={R} W={W} {dt}", flush=True)
     logits, x = synth.logits(wl), synth.hidden(wl)
     idx, w = oracle.route(logits, wl.k)
     ref = oracle.dispatch(x, idx, wl.E, wl.R, wl.W)
@@ -142,9 +159,20 @@ def test_scale_waves_match_plain(name, R, W, T, H, two_streams):
     eo = torch.empty_like(out["send_buf"])
     eo.view(torch.uint8).fill_(0x5A)
     copy = torch.cuda.Stream() if two_streams else None
-    chains = moe.Chains(n_events=1 + W, side=False) if two_streams else None
-    moe.scale_waves(xd, out, shape, expert_out=eo, copy_stream=copy, chains=chains)
-    y = moe.combine(eo, wd, out["pos"], shape)
+    chains = (moe.Chains(n_events=moe.scale_waves_events(W), side=False)
+              if two_streams or in_pipe == "own" else None)
+    if in_pipe:
+        two, order = moe.combine_order(out["pos"], out["wave_offsets"], shape)
+        y = torch.empty((T, H), dtype=tdt, device=DEV)
+        y.view(torch.uint8).fill_(0xA5)
+        comb = dict(topk_w=wd, pos=out["pos"], token_order=order, token_wave_offsets=two, y=y)
+        if in_pipe == "own":
+            comb["stream"] = torch.cuda.Stream()
+        moe.scale_waves(xd, out, shape, expert_out=eo, copy_stream=copy, chains=chains,
+                        combine=comb)
+    else:
+        moe.scale_waves(xd, out, shape, expert_out=eo, copy_stream=copy, chains=chains)
+        y = moe.combine(eo, wd, out["pos"], shape)
     torch.cuda.synchronize()
     n = ref["nrows"]
     np.testing.assert_array_equal(host(out["send_buf"])[:n], ref["send_buf"])
