@@ -129,15 +129,17 @@ template <int KMAX, bool kBF16, bool kCacheIn, bool kUniform>
 __global__ __launch_bounds__(kBlock) void combine_wave_kernel(
     const v4u* __restrict__ eo, const float* __restrict__ w, const int32_t* __restrict__ pos,
     int k, uint32_t nvec, uint32_t nrows, const int32_t* __restrict__ order,
-    const int32_t* __restrict__ twoff, int w0, int w1, v4u* __restrict__ y) {
-  const uint32_t a = (uint32_t)twoff[w0];
-  const uint32_t n = ((uint32_t)twoff[w1] - a) * nvec;  // T * nvec < 2^31
+    const int32_t* __restrict__ twoff, int w0, int w1, int T, v4u* __restrict__ y) {
+  // entries [a, b) of the order, clamped to [0, T] (T * nvec < 2^31)
+  const int a = min(max(twoff[w0], 0), T), b = min(max(twoff[w1], a), T);
+  const uint32_t n = (uint32_t)(b - a) * nvec;
   const uint32_t q = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
   if (q >= n) return;
   uint32_t j = q / nvec;
   if constexpr (kUniform) j = __builtin_amdgcn_readfirstlane(j);  // nvec % 64 == 0
   const uint32_t col = q - j * nvec;
   const int32_t t = order[a + j];
+  if ((uint32_t)t >= (uint32_t)T) return;  // not a token: nothing to write
   store_stream(y + (size_t)t * nvec + col,
                combine_column<KMAX, kBF16, kCacheIn>(eo, w + (size_t)t * k, pos + (size_t)t * k, k,
                                                      nvec, col, nrows));
@@ -145,8 +147,9 @@ __global__ __launch_bounds__(kBlock) void combine_wave_kernel(
 
 template <int KMAX>
 hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int k, uint32_t nvec,
-              uint32_t total, uint32_t nrows, const int32_t* order, const int32_t* twoff, int w0,
-              int w1, void* y, hipStream_t s) {
+              int T, uint32_t nrows, const int32_t* order, const int32_t* twoff, int w0, int w1,
+              void* y, hipStream_t s) {
+  const uint32_t total = (uint32_t)T * nvec;
   const unsigned grid = (total + kBlock - 1) / kBlock;  // total = T * nvec > 0
   const v4u* in = static_cast<const v4u*>(eo);
   v4u* out = static_cast<v4u*>(y);
@@ -155,7 +158,7 @@ hipError_t go(const void* eo, bool bf16, const float* w, const int32_t* pos, int
   const bool uniform = kCombineUniform && nvec % kWave == 0 && (cache || kStreamUniform);
   auto run = [&](auto kernel) {
     return launch(kernel, dim3(grid), dim3(kBlock), 0, s, in, w, pos, k, nvec, nrows, order,
-                  twoff, w0, w1, out);
+                  twoff, w0, w1, T, out);
   };
   auto pick = [&](auto bf, auto ca) {
     constexpr bool B = decltype(bf)::value, C = decltype(ca)::value;
@@ -202,15 +205,14 @@ hipError_t launch_combine_waves(const void* expert_out, int dtype, const float* 
   if (T == 0 || w0 >= w1) return hipSuccess;
   const bool bf16 = dtype == 1;
   const uint32_t nvec = (uint32_t)(H * (bf16 ? 2 : 4) / 16);
-  const uint32_t total = (uint32_t)T * nvec;
   const uint32_t nrows = (uint32_t)T * (uint32_t)k;
   const int32_t* o = token_order;
   const int32_t* tw = token_wave_offsets;
-  if (k <= 2) return go<2>(expert_out, bf16, w, pos, k, nvec, total, nrows, o, tw, w0, w1, y, s);
-  if (k <= 4) return go<4>(expert_out, bf16, w, pos, k, nvec, total, nrows, o, tw, w0, w1, y, s);
-  if (k <= 8) return go<8>(expert_out, bf16, w, pos, k, nvec, total, nrows, o, tw, w0, w1, y, s);
-  if (k <= 16) return go<16>(expert_out, bf16, w, pos, k, nvec, total, nrows, o, tw, w0, w1, y, s);
-  return go<32>(expert_out, bf16, w, pos, k, nvec, total, nrows, o, tw, w0, w1, y, s);
+  if (k <= 2) return go<2>(expert_out, bf16, w, pos, k, nvec, T, nrows, o, tw, w0, w1, y, s);
+  if (k <= 4) return go<4>(expert_out, bf16, w, pos, k, nvec, T, nrows, o, tw, w0, w1, y, s);
+  if (k <= 8) return go<8>(expert_out, bf16, w, pos, k, nvec, T, nrows, o, tw, w0, w1, y, s);
+  if (k <= 16) return go<16>(expert_out, bf16, w, pos, k, nvec, T, nrows, o, tw, w0, w1, y, s);
+  return go<32>(expert_out, bf16, w, pos, k, nvec, T, nrows, o, tw, w0, w1, y, s);
 }
 
 }  // namespace moe

@@ -156,3 +156,27 @@ def test_full_size_dirichlet_waves():
         moe.combine_waves(eo, wd, out["pos"], order, two, shape, w0, w0 + 1, y=y)
     torch.cuda.synchronize()
     assert torch.equal(_bits(y), _bits(y_ref))
+
+
+def test_tables_out_of_range_are_clamped():
+    """Offsets outside [0, T] and order entries that are not tokens: the wave
+    combine clamps the range to [0, T] and skips the entries, writing only the
+    listed tokens' rows (as moe_combine computes them)."""
+    wl = CASES["k1"]
+    x, idx, w = _inputs(wl)
+    shape, out, eo, wd, y_ref = _run(wl, x, idx, w)
+    T = wl.T
+    order = torch.arange(T, dtype=torch.int32, device=DEV)
+    order[::5] = -1
+    order[1::7] = T + 3
+    two = torch.tensor([-40] + [T // 2] * (wl.W - 1) + [T + 100], dtype=torch.int32, device=DEV)
+    y = torch.empty_like(y_ref)
+    y.view(torch.uint8).fill_(0x77)
+    moe.combine_waves(eo, wd, out["pos"], order, two, shape, 0, wl.W, y=y)
+    torch.cuda.synchronize()
+    listed = torch.zeros(T, dtype=torch.bool, device=DEV)
+    o = order.long()
+    listed[o[(o >= 0) & (o < T)]] = True
+    assert torch.equal(_bits(y[listed]), _bits(y_ref[listed]))
+    assert bool((y.view(torch.uint8)[~listed] == 0x77).all())
+    assert int(listed.sum()) < T
