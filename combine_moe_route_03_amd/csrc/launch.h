@@ -219,11 +219,8 @@ hipError_t launch_expert_swiglu_subset(const void* send, int64_t rows, int H, in
                                        const int32_t* cnts, const void* w_gate_up,
                                        const void* w_down, void* hbuf, void* out, hipStream_t s);
 
-// Wave-pipelined local layer: per wave, gather dispatch of its rows on `copy`,
-// then the FFN of its experts on `compute` after an event (copy == compute:
-// the same work, serialised). `events` holds at least 1 + 3W caller-owned
-// events when copy != compute or side is non-null; `side` (may be null)
-// carries the second chain of a wave's experts.
+// The gather dispatch of wave w's rows: send[r] = x[row_token[r]] for r in
+// [wave_offsets[w], wave_offsets[w+1]) (read on the device).
 hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int32_t* wave_offsets,
                               int w, int T, int64_t rows_max, int64_t row_bytes, void* send,
                               hipStream_t s);
@@ -237,7 +234,10 @@ hipError_t launch_scale_waves(const void* x, int T, int k, int64_t row_bytes, in
                               const int32_t* wave_offsets, const int32_t* offs,
                               const int32_t* cnts, void* send, void* out, const WaveCombine& wc,
                               hipStream_t compute, hipStream_t copy, const hipEvent_t* events);
-// The same with the SwiGLU experts (2 + 4W events when used).
+// The same with the SwiGLU experts (copy == compute: the same work,
+// serialised); `side` (may be null) carries the second chain of a wave's
+// experts; events holds at least 2 + 4W caller-owned events when copy !=
+// compute, side is non-null or wc.stream is a stream of its own.
 hipError_t launch_swiglu_waves(const void* x, int T, int k, int H, int I, int E, int R, int W,
                                const int32_t* row_token, const int32_t* wave_offsets,
                                const int32_t* offs, const int32_t* cnts, const void* w_gate_up,
