@@ -141,11 +141,20 @@ def algorithmic_bytes(wl) -> dict:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
 
+def source_code_hash(text: str) -> str:
+    """First 16 hex digits of the SHA-256 of C/C++ source text with its comments
+    and whitespace taken out, so that edits to comments alone keep a record."""
+    import hashlib
+    import re
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()[:16]
+
+
 def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (scaled by the counters' reading of a plain 1 GiB copy),
-    or None when there is no record or the kernel's sources changed since."""
-    import hashlib
+    or None when there is no record or the code of the kernel's sources (their
+    text without comments) changed since."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
     except OSError:
@@ -158,11 +167,11 @@ def stored_traffic(workload: str, kernel: str):
         f = fields(ln)
         if f.get("workload") != workload or f.get("kernel") != kernel or scale is None:
             continue
-        h = hashlib.sha256()
+        text = ""
         for src in f["sources"].split(","):
-            with open(os.path.join(ROOT, "combine_moe_route_03_amd", "csrc", src), "rb") as fh:
-                h.update(fh.read())
-        if h.hexdigest()[:16] != f["sha256"]:
+            with open(os.path.join(ROOT, "combine_moe_route_03_amd", "csrc", src)) as fh:
+                text += fh.read() + "\n"
+        if source_code_hash(text) != f["code_sha256"]:
             return None
         kib = float(f["fetch_kib"]) * float(scale["fetch"]) + float(f["write_kib"]) * float(scale["write"])
         return int(round(kib * 1024))

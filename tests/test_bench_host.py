@@ -36,11 +36,18 @@ def test_stored_traffic_record_and_guard(tmp_path, monkeypatch):
     fake = tmp_path / "t.md"
     fake.write_text("scale fetch=2.0 write=1.0\n"
                     "traffic workload=zipf kernel=expert_scale_kernel fetch_kib=10 write_kib=20 "
-                    "sources=expert.hip sha256=0000000000000000\n")
+                    "sources=expert.hip code_sha256=0000000000000000\n")
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(fake))
     assert bench.stored_traffic("zipf", "expert_scale_kernel") is None  # sources changed
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
     assert bench.stored_traffic("zipf", "expert_scale_kernel") is None
+
+
+def test_source_code_hash_ignores_comments_only():
+    a = "int f(int x) {  // add one\n  return x + 1; /* done */ }\n"
+    b = "// a header comment\nint f(int x) {\n  return x + 1;\n}\n"
+    assert bench.source_code_hash(a) == bench.source_code_hash(b)
+    assert bench.source_code_hash(a) != bench.source_code_hash(a.replace("x + 1", "x + 2"))
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
