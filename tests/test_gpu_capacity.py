@@ -12,7 +12,7 @@ import torch
 import combine_moe_route_03_amd as moe
 import oracle
 import synth
-from test_gpu_parity import DEV, PARITY, dev, host, shape_of
+from test_gpu_parity import PARITY, dev, host, shape_of
 
 pytestmark = pytest.mark.gpu
 

@@ -5,7 +5,6 @@ rows, scipy's expit for the one-hot/identity special case, the zero
 up-projection, exact power-of-two scalings, and expert selection.
 """
 import numpy as np
-import pytest
 import scipy.special
 import torch
 
