@@ -94,11 +94,14 @@ def test_wave_pipeline_matches_plain_and_oracle(name, R, W, two_streams, side, i
         ref["expert_counts"], ref["expert_offsets"], rows), gu, dn)
 
 
-def test_wave_pipeline_full_size_repeat():
-    """The local layer at full size, W = 4 on two streams, twice in a row into
-    the same buffers: identical to the unpipelined path both times."""
+@pytest.mark.parametrize("in_pipe", [False, True])
+def test_wave_pipeline_full_size_repeat(in_pipe):
+    """The local layer at full size, W = 4 on two streams (with in_pipe each
+    wave's completed tokens combined on a third), twice in a row into the same
+    buffers: identical to the unpipelined path both times."""
     wl = synth.WORKLOADS["local_layer"].with_(W=4)
-    print(f"[waves full] T={wl.T} H={wl.H} E={wl.E} I={wl.I} W={wl.W}", flush=True)
+    print(f"[waves full] T={wl.T} H={wl.H} E={wl.E} I={wl.I} W={wl.W} in_pipe={in_pipe}",
+          flush=True)
     x, gu, dn, idx, w = _setup(wl, std=0.02)
     shape, plain, eo_p, y_p = _plain(wl, x, gu, dn, idx, w)
     out = moe.alloc_dispatch(shape, DEV)
@@ -110,11 +113,21 @@ def test_wave_pipeline_full_size_repeat():
     ws = torch.empty((moe.expert_swiglu_workspace_bytes(shape, wl.I),), dtype=torch.uint8,
                      device=DEV)
     n = int(host(out["expert_counts"]).sum())
+    wd = dev(w.astype(np.float32))
+    two, order = moe.combine_order(out["pos"], out["wave_offsets"], shape)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    comb = dict(topk_w=wd, pos=out["pos"], token_order=order, token_wave_offsets=two, y=y,
+                stream=torch.cuda.Stream())
     for rep in range(2):
         eo.fill_(0)
-        moe.swiglu_waves(xd, out, shape, gud, dnd, expert_out=eo, workspace=ws, copy_stream=side,
-                         chains=chains)
-        y = moe.combine(eo, dev(w.astype(np.float32)), out["pos"], shape)
+        y.fill_(float("nan"))
+        if in_pipe:
+            moe.swiglu_waves(xd, out, shape, gud, dnd, expert_out=eo, workspace=ws,
+                             copy_stream=side, chains=chains, combine=comb)
+        else:
+            moe.swiglu_waves(xd, out, shape, gud, dnd, expert_out=eo, workspace=ws,
+                             copy_stream=side, chains=chains)
+            moe.combine(eo, wd, out["pos"], shape, y=y)
         torch.cuda.synchronize()
         assert torch.equal(out["send_buf"][:n], plain["send_buf"][:n]), rep
         assert torch.equal(eo[:n], eo_p[:n]), rep
@@ -180,3 +193,34 @@ def test_scale_waves_match_plain(name, R, W, T, H, two_streams, in_pipe):
     bits = torch.int16 if dt == "bf16" else torch.int32
     assert torch.equal(eo[:n].view(bits), eo_p[:n].view(bits))
     assert torch.equal(y.view(bits), y_p.view(bits))
+
+
+def test_scale_waves_full_size_dirichlet_waves():
+    """dirichlet_waves at full size (T=16384, H=7168, E=256, k=8, R=32, W=8): the
+    wave pipeline on two streams with each wave's completed tokens combined on
+    a third, bit for bit against moe_dispatch_copy + moe_expert_scale +
+    moe_combine on every send row, expert row and token."""
+    wl = synth.WORKLOADS["dirichlet_waves"]
+    print(f"[scale waves full] T={wl.T} H={wl.H} E={wl.E} k={wl.k} R={wl.R} W={wl.W}",
+          flush=True)
+    shape = moe.Shape(wl.T, wl.H, wl.E, wl.k, wl.R, wl.W, torch.bfloat16)
+    logits, xd = dev(synth.logits(wl)), dev(synth.hidden(wl))
+    idx, wd = moe.route(logits, wl.k)
+    plain = moe.dispatch(xd, idx, wl.E, wl.R, wl.W)
+    eo_p = moe.expert_scale(plain["send_buf"], plain["expert_offsets"], plain["expert_counts"],
+                            shape)
+    y_p = moe.combine(eo_p, wd, plain["pos"], shape)
+    out = moe.alloc_dispatch(shape, DEV)
+    moe.dispatch_index(idx, shape, out)
+    two, order = moe.combine_order(out["pos"], out["wave_offsets"], shape)
+    eo = torch.empty_like(out["send_buf"])
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    chains = moe.Chains(n_events=moe.scale_waves_events(wl.W), side=False)
+    moe.scale_waves(xd, out, shape, expert_out=eo, copy_stream=torch.cuda.Stream(), chains=chains,
+                    combine=dict(topk_w=wd, pos=out["pos"], token_order=order,
+                                 token_wave_offsets=two, y=y, stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    n = wl.T * wl.k
+    assert torch.equal(out["send_buf"][:n].view(torch.int16), plain["send_buf"][:n].view(torch.int16))
+    assert torch.equal(eo[:n].view(torch.int16), eo_p[:n].view(torch.int16))
+    assert torch.equal(y.view(torch.int16), y_p.view(torch.int16))
