@@ -126,7 +126,12 @@ __global__ __launch_bounds__(kWave * WM * WN, OCC) void ffn_gemm_kernel(
     else return lds4;
   };
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // Wave-uniform values are read into scalar registers (readfirstlane): then
+  // the buffer descriptors and LDS addresses built from them are scalar and
+  // each global->LDS load is one instruction, not a loop over lanes (local
+  // layer FFN 632-637 -> 625-628 us).
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid / WN, wn = wid % WN;
 
   // ---- which tile. The m-tiles (every expert's rows in BM-row tiles, in
@@ -186,16 +191,17 @@ __global__ __launch_bounds__(kWave * WM * WN, OCC) void ffn_gemm_kernel(
     }
   }
   __syncthreads();
-  const int e = info[0];
+  const int e = __builtin_amdgcn_readfirstlane(info[0]);
   if (e < 0) return;  // uniform over the block
-  const int row0 = info[1], rows = info[2];
+  const int row0 = __builtin_amdgcn_readfirstlane(info[1]);
+  const int rows = __builtin_amdgcn_readfirstlane(info[2]);
   // Waves whose 32-row MFMA tiles all lie past the tile's last row (the
   // partial last m-tile of an expert) run a loop that only loads and meets the
   // barriers: no fragment reads, no MFMAs, so the SIMDs they share with live
   // waves give those the MFMA pipe (local layer FFN 674-676 -> 630-632 us;
   // zero rows computed: 11% -> 3.4% of the rows).
   const bool live = wm * (BM / WM) < rows;
-  ntile = info[3];
+  ntile = __builtin_amdgcn_readfirstlane(info[3]);
 
   // ---- global -> LDS without registers (global_load_lds_dwordx4): one wave
   // instruction fills 64 consecutive 16-byte LDS slots, lane l slot l, i.e.
