@@ -10,13 +10,14 @@ cd "$ROOT"
 OUT=$ROOT/_build/san
 mkdir -p "$OUT"
 SRC=combine_moe_route_03_amd/csrc
+# the library's own source list, so that this build never misses a file
+SOURCES=$(python3 -c "import sys; sys.path.insert(0, 'combine_moe_route_03_amd'); \
+import _build; print(' '.join('$SRC/' + s for s in _build.SOURCES))")
 /opt/rocm/bin/hipcc --offload-arch=gfx950 -O1 -g -std=c++17 -fPIC -shared \
   -Xclang -target-feature -Xclang -packed-fp32-ops \
   -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined \
-  -Xarch_host -fno-sanitize-recover=undefined -shared-libsan \
-  -I include -I $SRC \
-  $SRC/abi.hip $SRC/route.hip $SRC/dispatch.hip $SRC/combine.hip $SRC/expert.hip $SRC/ffn.hip \
-  $SRC/stats.hip $SRC/alpha.hip $SRC/exchange.hip $SRC/waves.hip $SRC/dispatch_small.hip \
+  -Xarch_host -fno-sanitize-recover=undefined -shared-libsan -Wl,-z,defs \
+  -I include -I $SRC $SOURCES \
   -o "$OUT/libmoe_route_san.so"
 export MOE_ROUTE_LIB=$OUT/libmoe_route_san.so
 export LD_PRELOAD=$(ls /opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so | head -1)
