@@ -36,8 +36,10 @@
  *     this is plain expert-id order. Counts and offsets are in ROWS; the byte
  *     displacement of a row is rows * H * element size.
  *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), E % R == 0, L % W == 0,
- *     T >= 0, T * k < 2^31, H * element size a multiple of 16 bytes, hidden-
- *     state pointers 16-byte aligned, index/weight pointers 4-byte aligned.
+ *     T >= 0, H >= 1, R >= 1, W >= 1, T * k < 2^31, H * element size a
+ *     multiple of 16 bytes and T * k * H * element size / 16 < 2^31 (the row
+ *     kernels index 16-byte vectors in 32 bits), hidden-state pointers 16-byte
+ *     aligned, index/weight pointers 4-byte aligned.
  *   - T == 0 is valid: counts and offsets are written as zeros, nothing else.
  */
 #ifndef MOE_ROUTE_H

@@ -377,3 +377,36 @@ def test_combine_order_and_waves_validation():
     assert cw(c, 0, 2, ctypes.c_void_p((1 << 20) + 8)) == ALIGN
     d = [ctypes.c_void_p((1 << 20) + 8)] + c[1:]
     assert cw(d, 0, 2) == ALIGN
+
+def _valid_shape(T, H, E, k, R, W, dtype):
+    """The shape rules the header states, written out (not the library's code)."""
+    if dtype not in (moe.MOE_F32, moe.MOE_BF16):
+        return False
+    if T < 0 or H < 1 or not 1 <= E <= 1024 or not 1 <= k <= min(32, E) or R < 1 or W < 1:
+        return False
+    if E % R or (E // R) % W:
+        return False
+    row = H * (4 if dtype == moe.MOE_F32 else 2)
+    if row % 16:
+        return False
+    return T * k < 2**31 and T * k * (row // 16) < 2**31
+
+
+def test_shape_rules_random():
+    """moe_dispatch_workspace_bytes is 0 exactly for the shapes the stated rules
+    reject, over random shapes around every limit (seeded)."""
+    import numpy as np
+    L = moe.lib()
+    g = np.random.default_rng(2024)
+    pick = lambda *vals: int(g.choice(vals))  # noqa: E731
+    for _ in range(3000):
+        T = pick(-1, 0, 1, 7, 4096, 2**20, 2**27, 2**28 + 1, 2**30)
+        H = pick(0, 1, 4, 8, 12, 64, 7168, 2**16, 2**20)
+        E = pick(0, 1, 2, 6, 8, 64, 256, 1023, 1024, 1025)
+        k = pick(0, 1, 2, 6, 8, 32, 33, E, E + 1)
+        R = pick(0, 1, 2, 3, 4, 8, 32, E, E + 1)
+        W = pick(0, 1, 2, 4, 8, 16, 3)
+        dtype = pick(moe.MOE_F32, moe.MOE_BF16, 2, -1)
+        sh = moe.MoeShape(T=T, H=H, E=E, k=k, R=R, W=W, dtype=dtype)
+        got = L.moe_dispatch_workspace_bytes(ctypes.byref(sh))
+        assert (got > 0) == _valid_shape(T, H, E, k, R, W, dtype), (T, H, E, k, R, W, dtype)
