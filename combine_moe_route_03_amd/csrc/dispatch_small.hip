@@ -27,7 +27,10 @@ namespace {
 
 constexpr int kNT = kIndexBlock;  // 1024 threads: one pick of the batch each
 constexpr int kNW = kNT / kWave;
-constexpr int kVecs = 2;          // x vectors a thread loads up front
+// x vectors a thread loads up front: one, so the copy spreads over twice the
+// blocks of two (decode: 64 compute units instead of 32; dispatch 10.0-10.1
+// -> 9.0-9.3 us; 255 blocks of a quarter vector a thread measured the same)
+constexpr int kVecs = 1;
 
 template <int KMAX>
 __global__ __launch_bounds__(kNT) void dispatch_small_kernel(
