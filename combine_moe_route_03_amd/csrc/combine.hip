@@ -21,7 +21,10 @@
 namespace moe {
 namespace {
 
-constexpr int kBlock = 256;
+// 128-thread blocks: dirichlet_waves (streamed rows) 350-353 -> 341-343 us
+// against 256 (512: 349-350, 1024: 346-347, 64: 348-350); the cached-row
+// workloads measured the same with either.
+constexpr int kBlock = 128;
 
 template <int KMAX, bool kBF16, bool kCacheIn, bool kUniform>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const v4u* __restrict__ eo,

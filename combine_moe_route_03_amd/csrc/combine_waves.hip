@@ -26,6 +26,9 @@ namespace moe {
 namespace {
 
 constexpr int kOrderBlock = 1024;
+// 256-thread blocks: the grid covers all T tokens whatever the range, and
+// with 128 the launches of empty early waves cost more (dirichlet_waves,
+// W = 8, the eight waves one call each: 525 against 445 us).
 constexpr int kBlock = 256;
 
 __device__ __forceinline__ int wave_of_row(const int32_t* s_wo, int W, int32_t r) {
