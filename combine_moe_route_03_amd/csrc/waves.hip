@@ -28,7 +28,10 @@ constexpr int kU = 4;  // vectors per thread in flight
 
 // Rows [wave_offsets[w], wave_offsets[w+1]) of send <- x[row_token[r]], read
 // on the device; a grid-stride loop over the wave's (row, 16-byte column)
-// pairs. Rows whose token is outside [0, T) are skipped.
+// pairs. Rows whose token is outside [0, T) are skipped. kCache: the stores
+// go through the caches (the wave's experts read the rows next); otherwise
+// they stream (the whole send buffer past the cache budget).
+template <bool kCache>
 __global__ __launch_bounds__(kBlock) void gather_wave_kernel(
     const v4u* __restrict__ x, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ wave_offsets, int w, int T, int64_t rows_max, uint32_t nvec,
@@ -57,7 +60,10 @@ __global__ __launch_bounds__(kBlock) void gather_wave_kernel(
       if (src[u] >= 0) v[u] = x[src[u]];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (dst[u] >= 0) send[dst[u]] = v[u];  // through the caches: the FFN reads it next
+      if (dst[u] >= 0) {
+        if constexpr (kCache) send[dst[u]] = v[u];
+        else store_stream(send + dst[u], v[u]);
+      }
   }
 }
 
@@ -69,8 +75,16 @@ hipError_t launch_gather_wave(const void* x, const int32_t* row_token, const int
   const uint32_t nvec = (uint32_t)(row_bytes / 16);
   const int64_t want = (rows_max * nvec + kBlock * kU - 1) / (kBlock * kU);
   const unsigned grid = (unsigned)(want < 2048 ? (want < 1 ? 1 : want) : 2048);
-  return launch(gather_wave_kernel, dim3(grid), dim3(kBlock), 0, s, static_cast<const v4u*>(x),
-                row_token, wave_offsets, w, T, rows_max, nvec, static_cast<v4u*>(send));
+  // the expert stage's policy for the same buffer: streaming stores past the
+  // budget (dirichlet_waves, 1.9 GB: gather 590 -> 540 us at W = 1, step at
+  // W = 8 1.638 -> 1.567 ms with two streams; the x rows re-read for each
+  // copy come from HBM either way)
+  auto go = [&](auto kernel) {
+    return launch(kernel, dim3(grid), dim3(kBlock), 0, s, static_cast<const v4u*>(x), row_token,
+                  wave_offsets, w, T, rows_max, nvec, static_cast<v4u*>(send));
+  };
+  return rows_max * row_bytes <= kCacheReuseBytes ? go(gather_wave_kernel<true>)
+                                                  : go(gather_wave_kernel<false>);
 }
 
 namespace {
