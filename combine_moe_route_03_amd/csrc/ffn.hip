@@ -52,7 +52,42 @@ constexpr int kXCD = 8;
 // L2, 4 and 8 are faster than 1 (step 723-726 against 733 us, same box).
 constexpr int kGroupM = 4;
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a pair of bf16 (low half = a), round to nearest even: on
+// gfx950 one v_cvt_pk_bf16_f32, which rounds every non-NaN float exactly as
+// the bit-twiddling f32_to_bf16_rne does (checked on the device over 16M bit
+// patterns: denormals, ties of both parities, overflow to infinity); a NaN
+// keeps its payload instead of becoming the canonical one.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// SiLU(g) = g / (1 + e^-g), evaluated as num / (1 + e^-|g|) with num = g for
+// g >= 0 and g e^-|g| below, so the denominator stays in (1, 2]: e^-|g| is
+// the hardware base-2 exponential of -|g| log2(e), the product split into a
+// rounded part and its error (log2(e) as a float plus its remainder, the
+// error carried to first order after the exponential), and the reciprocal is
+// the hardware one refined by one Newton step. Relative error at most
+// 4.6 x 2^-24 against the exact SiLU over 16M arguments in [-100, 100]
+// (3.1 x 2^-24 for expf and an IEEE division), in ~13 instructions instead of
+// ~25: the gate/up epilogue is bound by its instruction count.
+__device__ __forceinline__ float silu(float g) {
+  constexpr float kL1 = 1.44269504f;            // log2(e) rounded to float
+  constexpr float kL2 = 1.925963033500011e-08f;  // log2(e) - kL1
+  constexpr float kLn2 = 0.693147181f;
+  const float a = -__builtin_fabsf(g);
+  const float t = a * kL1;
+  const float tl = __builtin_fmaf(a, kL1, -t) + a * kL2;  // a log2(e) - t
+  const float e0 = __builtin_amdgcn_exp2f(t);
+  const float e = __builtin_fmaf(e0, tl * kLn2, e0);      // e^-|g|
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+  return (g >= 0.0f ? g : g * e) * r;
+}
 
 // XOR key of tile row r for a K step of BK bf16 (BK/8 16-byte chunks a row).
 // The 64 four-byte banks span 256 bytes; a fragment read (ds_read_b128)
@@ -383,25 +418,40 @@ __global__ __launch_bounds__(kWave * WM * WN, OCC) void ffn_gemm_kernel(
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- epilogue: result (row, col) of register r of a 32x32 tile is
-  // row 8*(r/4) + 4*(lane/32) + r%4, col lane%32.
+  // row 8*(r/4) + 4*(lane/32) + r%4, col lane%32, so registers r and r+1 (r
+  // even) are two consecutive rows of one column: one hardware conversion
+  // makes both bf16 values, each stored as 2 bytes (a wave's store covers two
+  // rows, 64 contiguous bytes each). The stores go through a buffer
+  // descriptor over the tile's rows of C, whose range check drops the rows
+  // past the tile's last one (no per-row branch); a fragment's column offset
+  // is an immediate. Local layer FFN: the epilogue took 12.6 us a gate/up
+  // tile and 7.8 us a down tile with per-row branches, 64-bit addresses and
+  // the bit-twiddling rounding, ~900 and ~940 instructions a wave.
+  const __amdgpu_buffer_rsrc_t crsrc =
+      make_rsrc(C + (int64_t)row0 * ldc, (int64_t)rows * ldc * 2);
+  const int ccol = kGateUp ? ntile * (BN / 2) + wn * (BN / 2 / WN) : ntile * BN + wn * (BN / WN);
+  const uint32_t vbase =
+      (uint32_t)(((wm * (BM / WM) + 4 * (lane >> 5)) * ldc + ccol + (lane & 31)) * 2);
+  constexpr int NO = kGateUp ? NI / 2 : NI;  // output fragments of a fragment row
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = wm * (BM / WM) + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (tr >= rows) continue;
-      uint16_t* crow = C + (int64_t)(row0 + tr) * ldc;
-      if constexpr (kGateUp) {
+    for (int r = 0; r < 16; r += 2) {
+      const uint32_t v0 = vbase + (uint32_t)((mi * 32 + 8 * (r >> 2) + (r & 3)) * ldc * 2);
+      const uint32_t v1 = v0 + (uint32_t)(ldc * 2);
 #pragma unroll
-        for (int ni = 0; ni < NI / 2; ++ni) {
-          const float g = acc[mi][ni][r], u = acc[mi][ni + NI / 2][r];
-          const float h = (g / (1.0f + expf(-g))) * u;
-          crow[ntile * (BN / 2) + wn * (BN / 2 / WN) + ni * 32 + (lane & 31)] = bf16_bits(h);
+      for (int ni = 0; ni < NO; ++ni) {
+        float a, b;
+        if constexpr (kGateUp) {
+          a = silu(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r];
+          b = silu(acc[mi][ni][r + 1]) * acc[mi][ni + NI / 2][r + 1];
+        } else {
+          a = acc[mi][ni][r];
+          b = acc[mi][ni][r + 1];
         }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          crow[ntile * BN + wn * (BN / WN) + ni * 32 + (lane & 31)] = bf16_bits(acc[mi][ni][r]);
+        const uint32_t p = bf16x2_rne(a, b);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)p, crsrc, v0 + ni * 64, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(p >> 16), crsrc, v1 + ni * 64, 0, 0);
       }
     }
   }

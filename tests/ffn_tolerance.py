@@ -12,7 +12,8 @@ oracle reports (g, u, out) and absolute-value sums of the operands:
     dg_j  = gamma_H * sum_h |Wg[j][h] s_h|          fp32 sum of H exact products
     du_j  = gamma_H * sum_h |Wu[j][h] s_h|
     dh_j  = |SiLU'(g_j) u_j| dg_j + |SiLU(g_j)| du_j + 8 u_32 |SiLU(g_j) u_j|
-            (the last term: expf, the add, the division and the product)
+            (the last term: the kernel's SiLU, at most 4.6 u_32 from the exact
+            one over 16M arguments in [-100, 100], and the product with u)
     flip_j = max |r(h_j +- dh_j) - r(h_j)|            r = round to bf16
     E_c   = sum_j |Wd[c][j]| flip_j + gamma_I sum_j |Wd[c][j]| (|h_j| + flip_j)
     |got_c - out_c| <= E_c (1 + 2^-8) + 2^-8 |out_c|   final bf16 rounding
