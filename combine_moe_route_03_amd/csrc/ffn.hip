@@ -70,10 +70,11 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // the hardware base-2 exponential of -|g| log2(e), the product split into a
 // rounded part and its error (log2(e) as a float plus its remainder, the
 // error carried to first order after the exponential), and the reciprocal is
-// the hardware one refined by one Newton step. Relative error at most
-// 4.6 x 2^-24 against the exact SiLU over 16M arguments in [-100, 100]
-// (3.1 x 2^-24 for expf and an IEEE division), in ~13 instructions instead of
-// ~25: the gate/up epilogue is bound by its instruction count.
+// the hardware one refined by one Newton step. For finite g (an infinite one
+// gives NaN) the relative error is at most 4.6 x 2^-24 against the exact
+// SiLU over 16M arguments in [-100, 100] (3.1 x 2^-24 for expf and an IEEE
+// division), in ~13 instructions instead of ~25: the gate/up epilogue is
+// bound by its instruction count.
 __device__ __forceinline__ float silu(float g) {
   constexpr float kL1 = 1.44269504f;            // log2(e) rounded to float
   constexpr float kL2 = 1.925963033500011e-08f;  // log2(e) - kL1
