@@ -92,6 +92,44 @@ def test_swiglu_empty_and_ragged_experts(H, I):
     _check_rows(host(eo_gpu), x[rt], _row_expert(ec, eo, rows), gu, dn)
 
 
+@pytest.mark.parametrize("two_chains", [True, False])
+@pytest.mark.parametrize("H,I", [(128, 64), (256, 128)])  # 128- and 256-row tile paths
+def test_swiglu_stores_stay_in_their_rows(H, I, two_chains):
+    """The epilogue stores through buffer descriptors whose range check drops
+    the rows past a tile's last one: with the last expert's tile mostly past
+    the end of expert_out and of the h workspace, guard bytes right after both
+    stay untouched, and every row is right."""
+    E, k = 4, 1
+    sizes = {0: 3, 1: 300, 3: 5}  # expert 2 has no rows; expert 3 (last) a 5-row tile
+    T = sum(sizes.values())
+    idx = np.concatenate([np.full(n, e, np.int32) for e, n in sizes.items()]).reshape(T, k)
+    wl = synth.Workload("ffn", T=T, H=H, dtype="bf16", E=E, k=k, R=1, W=1, routing="iid",
+                        expert="swiglu", I=I, seed=6)
+    print(f"[ffn guard] H={H} I={I} two_chains={two_chains}", flush=True)
+    x = synth.hidden(wl)
+    gu, dn = synth.swiglu_weights(wl, std=0.1)
+    ec, _ = oracle.counts(idx, E, 1, 1)
+    eo, _, _ = oracle.offsets(ec, 1, 1)
+    pos, rt = oracle.positions(idx, E, eo, T)
+    shape = moe.Shape(T, H, E, k, 1, 1, torch.bfloat16)
+    out = moe.dispatch(dev(x), dev(idx), E, 1, 1)
+    guard = 256  # rows past the end (a whole tile's worth)
+    big_out = torch.empty((T * k + guard, H), dtype=torch.bfloat16, device=DEV)
+    big_out.view(torch.uint8).fill_(0xA7)
+    ws_bytes = moe.expert_swiglu_workspace_bytes(shape, I)
+    big_ws = torch.empty((ws_bytes + guard * I * 2,), dtype=torch.uint8, device=DEV)
+    big_ws.fill_(0x5C)
+    eo_gpu = moe.expert_swiglu(out["send_buf"], out["expert_offsets"], out["expert_counts"], shape,
+                               dev(gu), dev(dn), expert_out=big_out[:T * k],
+                               workspace=big_ws[:ws_bytes],
+                               chains=moe.Chains() if two_chains else None)
+    torch.cuda.synchronize()
+    assert bool((big_out[T * k:].view(torch.uint8) == 0xA7).all())
+    assert bool((big_ws[ws_bytes:] == 0x5C).all())
+    rows = np.arange(T)
+    _check_rows(host(eo_gpu), x[rt], _row_expert(ec, eo, rows), gu, dn)
+
+
 def test_swiglu_validation():
     wl = synth.WORKLOADS["local_layer"]
     sh = moe.Shape(8, 4096, 16, 2, 1, 1, torch.bfloat16)
