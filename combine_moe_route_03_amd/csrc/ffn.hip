@@ -9,11 +9,13 @@
 //
 // Both are A[M_e x K] * B[N x K]^T with K contiguous in both operands, on
 // v_mfma_f32_32x32x16_bf16. Two tile shapes, one kernel template:
-//   large: 256 x 256 x 64 per 1024-thread block, 16 waves as 4 x 4, each wave
-//          64 x 64 (2 x 2 MFMA tiles, 64 fp32 accumulators per lane), four
-//          waves per SIMD so some issue MFMAs while others wait on LDS or the
-//          barrier (one wave of 128 x 128 per SIMD measured 13% slower, two of
-//          128 x 64 2% slower). Needs I % 128 == 0 and H % 256 == 0.
+//   large: 256 x 256 x 64 per 512-thread block, 8 waves as 4 x 2, each wave
+//          64 x 128 (2 x 4 MFMA tiles, 128 fp32 accumulators per lane), two
+//          waves per SIMD so one issues MFMAs while the other waits on LDS or
+//          the barrier; no spill at 226 VGPRs (16 waves of 64 x 64, four a
+//          SIMD, spilled 20 bytes a lane and measured 1.6% slower; one wave
+//          of 128 x 128 per SIMD 13% slower). Needs I % 128 == 0 and
+//          H % 256 == 0.
 //   small: 128 x 128 x 64, 4 waves of 64 x 64 (2 x 2 tiles), two blocks per
 //          compute unit; any I % 64 == 0 and H % 128 == 0.
 // Global -> LDS moves go through buffer loads with the LDS bit (16 bytes a
@@ -463,7 +465,11 @@ __global__ __launch_bounds__(kWave * WM * WN, OCC) void ffn_gemm_kernel(
 // not uncovered load latency, bounds this kernel.
 constexpr int kLargeBK = 64;
 constexpr int kLargeNS = 2;
-constexpr int kLargeWM = 4, kLargeWN = 4;  // 4 x 4 waves, four per SIMD (2 x 4: 698 us, 4 x 2: 692, 4 x 4: 683)
+// 4 x 2 waves, two per SIMD: local layer FFN 581.5-581.9 against 590.8-591.8
+// us for 4 x 4 (16 waves) with the current epilogue, same box, interleaved
+// (with the earlier, instruction-heavy epilogue 4 x 4 was the faster: 683
+// against 692 us, 2 x 4 698).
+constexpr int kLargeWM = 4, kLargeWN = 2;
 
 template <int BM, int BN, int OCC, int BK, int NS, int WM, int WN>
 hipError_t run_ffn(const void* send, int64_t rows, int H, int I, int E, int sg, int sstride,
