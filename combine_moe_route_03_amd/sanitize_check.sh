@@ -10,7 +10,7 @@ cd "$ROOT"
 OUT=$ROOT/_build/san
 mkdir -p "$OUT"
 SRC=combine_moe_route_03_amd/csrc
-# the library's own source list, so that this build never misses a file
+# the library's own source list, so that the sanitized library never misses a file
 SOURCES=$(python3 -c "import sys; sys.path.insert(0, 'combine_moe_route_03_amd'); \
 import _build; print(' '.join('$SRC/' + s for s in _build.SOURCES))")
 /opt/rocm/bin/hipcc --offload-arch=gfx950 -O1 -g -std=c++17 -fPIC -shared \
