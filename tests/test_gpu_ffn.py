@@ -56,7 +56,9 @@ def _run_gpu(wl, x, gu, dn, idx_o, two_chains=True):
 
 
 @pytest.mark.parametrize("T,E,H,I,k,seed", [(300, 4, 256, 128, 2, 1), (77, 5, 128, 64, 3, 2),
-                                            (1000, 16, 256, 192, 2, 3)])
+                                            (1000, 16, 256, 192, 2, 3),
+                                            (200, 3, 7168, 256, 2, 7),  # wide rows (H = 7168)
+                                            (300, 1, 256, 128, 1, 8)])  # one expert
 @pytest.mark.parametrize("two_chains", [True, False])
 def test_swiglu_small_full(T, E, H, I, k, seed, two_chains):
     wl = synth.Workload("ffn", T=T, H=H, dtype="bf16", E=E, k=k, R=1, W=1, routing="zipf0.5",
